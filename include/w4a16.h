@@ -1,0 +1,200 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so, INT4 weight-only quantization and the
+ * W4A16 matrix multiply on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (cited by page title and section):
+ *  [QB]  "Quantization basics: from FP32 to INT4" (量化基础：从 FP32 到 INT4
+ *        的压缩艺术, wsisp.com tutorial): §1.3 INT4 grid [-8, 7]; §2.1 affine
+ *        map and its inverse; §2.2 symmetric scale s = max|x| / q_max;
+ *        §2.4 error bound; §3 per-group granularity; §5 round must be a real
+ *        round (half-to-even), not a truncating cast.
+ *  [RL]  "INT4 QAT end-to-end for RL" (SGLang RL / slime / Miles write-up):
+ *        §2.1 fake quantization in the training forward pass; §3.2 real
+ *        quantization at weight update, 8 INT4 packed per INT32 (Fig. 4);
+ *        §4 W4A16 inference, moe_align_block_size, fused MoE and gating.
+ *  [TAG] "Quantization-aware training" tag summary (量化感知训练, reportify):
+ *        [11] one scale per 1 x 32 group; [32] two 4-bit weights per byte;
+ *        [35] block size picked from the token count and expert spread.
+ *
+ * Conventions for every entry point
+ *  - All tensors are row-major and contiguous, in device memory (pointers
+ *    from hipMalloc or a framework allocator on the current device).
+ *  - bfloat16 values are passed as their 16-bit patterns (uint16_t).
+ *  - The caller owns all memory; the library allocates and frees nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; no call synchronizes or reads back.
+ *  - Arguments are validated before anything is enqueued; on any error the
+ *    outputs are left untouched and a nonzero status is returned.
+ *  - Pointers marked "16-byte aligned" must be; others need their natural
+ *    alignment.  Inputs and outputs must not overlap unless stated.
+ *  - Sizes are int64_t; a size of 0 is a valid no-op where stated.
+ *  - Calls are deterministic: the same inputs give bitwise-identical outputs
+ *    (no floating-point atomics; reductions in a fixed order).
+ *  - Weight layout: Wq int32 [N, K/8]: nibble j (bits 4j..4j+3) of word w of
+ *    row n holds the two's-complement INT4 code of element k = 8w + j.
+ *    Scales S bf16 [N, K/32]: one per 32 consecutive k of a row.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define W4_OK               0
+#define W4_ERR_NULL         1  /* a required pointer is NULL */
+#define W4_ERR_SHAPE        2  /* a size is negative or K % 32 != 0, etc. */
+#define W4_ERR_MISALIGNED   3  /* a pointer lacks the required alignment */
+#define W4_ERR_UNSUPPORTED  4  /* valid but outside what the kernels cover */
+#define W4_ERR_HIP          5  /* a HIP launch failed; see w4_last_hip_error */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4_status_string(int status);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if
+ * none).  Thread-local; reset by no call except a later failure. */
+int w4_last_hip_error(void);
+
+/* Library version string. */
+const char* w4_version(void);
+
+/*
+ * w4_quantize_pack -- symmetric group-wise INT4 quantization + packing.
+ * [QB] §2.2 (z = 0, s = max|w| / 7), [TAG] [11] (1 x 32 groups), [RL] §3.2
+ * (eight codes per INT32).
+ *
+ *   for each row n and group g of 32 consecutive k:
+ *     amax = max |W[n, 32g .. 32g+31]|                       (exact)
+ *     S[n, g] = bf16_rne( fp32(amax) / 7 )                   (IEEE fp32 div)
+ *     q = S == 0 ? 0 : clamp( rint_half_even( fp32(w) / fp32(S) ), -8, 7 )
+ *     Wq packs q along k as described in the header comment.
+ *
+ * W   bf16 [N, K], 16-byte aligned, finite values (NaN/Inf: undefined codes).
+ * Wq  int32 [N, K/8] output, 16-byte aligned.
+ * S   bf16 [N, K/32] output, 2-byte aligned.
+ * K % 32 == 0, N >= 0, K >= 0 (N*K == 0 is a no-op).
+ * Outputs are bit-exact with the plain definition above.
+ */
+int w4_quantize_pack(const uint16_t* W, int64_t N, int64_t K,
+                     int32_t* Wq, uint16_t* S, void* stream);
+
+/*
+ * w4_fake_quant -- QAT forward quantize-dequantize ([RL] §2.1).
+ *   W_fq[n, k] = bf16_rne( q[n, k] * S[n, k/32] )
+ * with q and S exactly as w4_quantize_pack computes them; the fp32 product
+ * is exact, so W_fq equals the dequantized packed weights bit for bit.
+ * W, W_fq bf16 [N, K], 16-byte aligned.  W_fq == W (in place) is allowed;
+ * any other overlap is not.  K % 32 == 0.
+ */
+int w4_fake_quant(const uint16_t* W, int64_t N, int64_t K,
+                  uint16_t* W_fq, void* stream);
+
+/*
+ * w4a16_gemm -- Y = X * dequant(Wq, S)^T ([RL] §4: INT4 weights, BF16
+ * activations, dequantized in registers, BF16 matrix cores, fp32
+ * accumulation).
+ *   Y[m, n] = bf16_rne( sum_k X[m, k] * bf16_rne(q[n, k] * S[n, k/32]) )
+ * accumulated in fp32 (order unspecified but fixed).
+ * X  bf16 [M, K], 16-byte aligned.   Wq int32 [N, K/8], 16-byte aligned.
+ * S  bf16 [N, K/32].                 Y  bf16 [M, N] output, 4-byte aligned.
+ * K % 32 == 0; M, N >= 0 (M*N == 0 is a no-op); K == 0 writes zeros.
+ * Small M (<= 32) runs the decode kernel, larger M the tiled MFMA kernel.
+ */
+int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+               uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * w4_pick_block_size -- alignment block size from the token count and the
+ * expert count ([TAG] [35]):  B = min(64, max(16, next_pow2(ceil(T*k/E)))).
+ * Returns 0 if T < 0, k < 1 or E < 1.
+ */
+int32_t w4_pick_block_size(int64_t T, int32_t k, int32_t E);
+
+/*
+ * w4_moe_align_capacity -- length of sorted_token_ids that
+ * moe_align_block_size fills: round_up(T*k + E*(B-1), B).  Returns -1 on
+ * invalid arguments.  expert_ids holds capacity / B entries.
+ */
+int64_t w4_moe_align_capacity(int64_t T, int32_t k, int32_t E, int32_t B);
+
+/*
+ * moe_align_block_size -- merge and align each expert's token set
+ * ([RL] §4, [TAG] [35]).
+ * topk_ids int32 [T, k] (pair f = t*k + j routes to expert topk_ids[t, j];
+ * ids outside [0, E) are skipped).  Outputs, over their whole capacity:
+ *   sorted_token_ids int32 [cap]: experts in ascending order; inside an
+ *       expert its pairs f in ascending order, then the sentinel T*k up to
+ *       a multiple of B; after the last segment, the sentinel.
+ *   expert_ids int32 [cap/B]: the expert of each block, -1 past the end.
+ *   num_tokens_post_padded int32 [1]: total padded length (multiple of B).
+ * 1 <= k, 1 <= E <= 1024, 1 <= B <= 1024, T*k + E*B < 2^31.  T == 0 is
+ * valid (all sentinels, total 0).  Bit-exact; deterministic.
+ */
+int moe_align_block_size(const int32_t* topk_ids, int64_t T, int32_t k,
+                         int32_t E, int32_t B, int32_t* sorted_token_ids,
+                         int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                         void* stream);
+
+/*
+ * w4a16_moe_gemm -- grouped W4A16 GEMM over aligned expert blocks
+ * ([RL] §4 fused MoE).  For every block b < num_tokens_post_padded / B
+ * with e = expert_ids[b] in [0, E), and every slot holding a pair
+ * f = sorted_token_ids[b*B + i] < T*k:
+ *   Y[f, :] = bf16_rne( X[f / x_row_div, :] * dequant(Wq[e], S[e])^T
+ *                       (* topk_weights[f] if topk_weights != NULL) )
+ * Rows of Y not named by a valid slot are not written.
+ * X   bf16 [rows, K] with rows = (T*k) / x_row_div (x_row_div = k for the
+ *     gate_up projection of token rows, 1 for the down projection of pair
+ *     rows), 16-byte aligned.
+ * Wq  int32 [E, N, K/8], S bf16 [E, N, K/32] (experts stacked), Wq 16-byte
+ *     aligned.  Y bf16 [T*k, N], 4-byte aligned.
+ * sorted_token_ids / expert_ids / num_tokens_post_padded: as produced by
+ * moe_align_block_size with the same T, k, E, B (device memory; the count
+ * is read on the device, never by the host).
+ * topk_weights float32 [T*k] or NULL.  K % 32 == 0, N >= 1, B in [1, 1024],
+ * x_row_div in {1, k}.
+ */
+int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded,
+                   const float* topk_weights, uint16_t* Y, int64_t T,
+                   int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
+                   int32_t x_row_div, void* stream);
+
+/*
+ * w4_silu_mul -- SwiGLU between the expert projections (a reading: the
+ * pages name the gate_up / down pair but not the activation):
+ *   A[r, i] = bf16_rne( silu(H1[r, i]) * H1[r, I + i] ),  silu(v) = v/(1+e^-v)
+ * H1 bf16 [R, 2I], A bf16 [R, I], both 4-byte aligned; I even.
+ */
+int w4_silu_mul(const uint16_t* H1, uint16_t* A, int64_t R, int64_t I,
+                void* stream);
+
+/*
+ * w4_moe_sum -- top-k combine:
+ *   Out[t, :] = bf16_rne( sum_{j = 0..k-1, in order} w[t, j] * H2[t*k + j, :] )
+ * in fp32, with w = topk_weights, or w = 1 when topk_weights is NULL.
+ * H2 bf16 [T*k, H], Out bf16 [T, H], 4-byte aligned; H even.
+ */
+int w4_moe_sum(const uint16_t* H2, const float* topk_weights, uint16_t* Out,
+               int64_t T, int32_t k, int64_t H, void* stream);
+
+/*
+ * w4_moe_route -- softmax top-k routing (fused gating, [RL] §4 / [TAG] [35]):
+ *   p = softmax(logits[t, :]); pick the k largest logits (ties: lower
+ *   expert index first), ordered by descending logit; weights are the
+ *   picked p renormalised to sum to 1 (= softmax over the picked logits).
+ * logits float32 [T, E]; topk_ids int32 [T, k]; topk_weights float32 [T, k].
+ * 1 <= k <= min(E, 16), 1 <= E <= 1024.  fp32 arithmetic.
+ */
+int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
+                 int32_t* topk_ids, float* topk_weights, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,240 @@
+"""INT4 weight-only quantization and W4A16 GEMMs on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libw4a16.so`` (include/w4a16.h).
+Each function has the name of the C entry point it calls and does argument
+marshalling only: shape/dtype/device checks, output allocation through
+PyTorch, raw pointers and the current HIP stream.  Every step of the path
+runs in the library's HIP kernels; nothing here computes.
+
+Layouts (all row-major, contiguous, on one GPU):
+  W       bf16  [N, K]        source / master weights
+  Wq      int32 [N, K/8]      nibble j of word w holds the INT4 code of k = 8w + j
+  S       bf16  [N, K/32]     one scale per 32 consecutive k
+  X       bf16  [M, K]        activations;  Y bf16 [M, N]
+  experts stacked on a leading axis: Wq [E, N, K/8], S [E, N, K/32]
+"""
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "w4_quantize_pack", "w4_fake_quant", "w4a16_gemm", "w4_pick_block_size",
+    "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm",
+    "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
+]
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _stream(t):
+    return ctypes_void(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def ctypes_void(v):
+    return None if v is None else int(v)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def w4_quantize_pack(W, Wq=None, S=None):
+    """bf16 W [N, K] -> (int32 Wq [N, K/8], bf16 S [N, K/32])."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    if S is None:
+        S = torch.empty((N, K // 32), dtype=torch.bfloat16, device=W.device)
+    _need(Wq, "Wq", torch.int32)
+    _need(S, "S", torch.bfloat16)
+    if Wq.numel() != N * (K // 8) or S.numel() != N * (K // 32):
+        raise ValueError("Wq / S sizes do not match W")
+    lib = _lib.load()
+    _lib.check("w4_quantize_pack",
+               lib.w4_quantize_pack(_ptr(W), N, K, _ptr(Wq), _ptr(S), _stream(W)))
+    return Wq, S
+
+
+def w4_fake_quant(W, out=None):
+    """QAT forward: bf16 W [N, K] -> bf16 dequant(quantize(W)).  ``out`` may be W."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != W.numel():
+        raise ValueError("out size does not match W")
+    lib = _lib.load()
+    _lib.check("w4_fake_quant", lib.w4_fake_quant(_ptr(W), N, K, _ptr(out), _stream(W)))
+    return out
+
+
+def w4a16_gemm(X, Wq, S, out=None):
+    """Y [M, N] = X [M, K] * dequant(Wq, S)^T, bf16 out, fp32 accumulation."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wq, "Wq", torch.int32, 2)
+    _need(S, "S", torch.bfloat16, 2)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] * 8 != K or tuple(S.shape) != (N, K // 32):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} Wq {tuple(Wq.shape)} "
+                         f"S {tuple(S.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out size does not match [M, N]")
+    lib = _lib.load()
+    _lib.check("w4a16_gemm", lib.w4a16_gemm(_ptr(X), _ptr(Wq), _ptr(S), _ptr(out),
+                                            M, N, K, _stream(X)))
+    return out
+
+
+def w4_pick_block_size(T, k, E):
+    return int(_lib.load().w4_pick_block_size(T, k, E))
+
+
+def w4_moe_align_capacity(T, k, E, B):
+    return int(_lib.load().w4_moe_align_capacity(T, k, E, B))
+
+
+def moe_align_block_size(topk_ids, E, B, sorted_token_ids=None, expert_ids=None,
+                         num_tokens_post_padded=None):
+    """int32 topk_ids [T, k] -> (sorted_token_ids [cap], expert_ids [cap/B], ntpp [1])."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    cap = w4_moe_align_capacity(T, k, E, B)
+    if cap < 0:
+        raise ValueError("invalid T, k, E or B")
+    dev = topk_ids.device
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(cap // B, dtype=torch.int32, device=dev)
+    if num_tokens_post_padded is None:
+        num_tokens_post_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    for t, n, size in ((sorted_token_ids, "sorted_token_ids", cap),
+                       (expert_ids, "expert_ids", cap // B),
+                       (num_tokens_post_padded, "num_tokens_post_padded", 1)):
+        _need(t, n, torch.int32)
+        if t.numel() < size:
+            raise ValueError(f"{n} needs {size} entries")
+    lib = _lib.load()
+    _lib.check("moe_align_block_size", lib.moe_align_block_size(
+        _ptr(topk_ids), T, k, E, B, _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _stream(topk_ids)))
+    return sorted_token_ids, expert_ids, num_tokens_post_padded
+
+
+def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                   T, k, B, x_row_div, topk_weights=None, out=None):
+    """Grouped expert product over aligned blocks.
+
+    Row f of ``out`` [T*k, N] = X[f // x_row_div] * dequant(Wq[e], S[e])^T
+    (times topk_weights.flat[f] when given) for every valid slot f of every
+    block b < ntpp / B with e = expert_ids[b].  Other rows are not written.
+    """
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wq, "Wq", torch.int32, 3)
+    _need(S, "S", torch.bfloat16, 3)
+    E, N, kw = Wq.shape
+    K = kw * 8
+    if X.shape[1] != K or tuple(S.shape) != (E, N, K // 32):
+        raise ValueError("shape mismatch between X, Wq and S")
+    if X.shape[0] != (T * k) // x_row_div:
+        raise ValueError("X must have T*k / x_row_div rows")
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, n, torch.int32)
+    cap = w4_moe_align_capacity(T, k, E, B)
+    if sorted_token_ids.numel() < cap or expert_ids.numel() < cap // B:
+        raise ValueError("alignment buffers are smaller than the capacity")
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32)
+        if topk_weights.numel() != T * k:
+            raise ValueError("topk_weights must have T*k entries")
+    if out is None:
+        out = torch.empty((T * k, N), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * k * N:
+        raise ValueError("out must be [T*k, N]")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm", lib.w4a16_moe_gemm(
+        _ptr(X), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, k, E, N, K, B,
+        x_row_div, _stream(X)))
+    return out
+
+
+def w4_silu_mul(H1, out=None):
+    """bf16 H1 [R, 2I] -> bf16 A [R, I] = silu(H1[:, :I]) * H1[:, I:]."""
+    _need(H1, "H1", torch.bfloat16, 2)
+    R, I2 = H1.shape
+    I = I2 // 2
+    if I2 % 2:
+        raise ValueError("H1 must have an even number of columns")
+    if out is None:
+        out = torch.empty((R, I), dtype=torch.bfloat16, device=H1.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != R * I:
+        raise ValueError("out must be [R, I]")
+    lib = _lib.load()
+    _lib.check("w4_silu_mul", lib.w4_silu_mul(_ptr(H1), _ptr(out), R, I, _stream(H1)))
+    return out
+
+
+def w4_moe_sum(H2, topk_weights, T, k, out=None):
+    """bf16 H2 [T*k, H] -> bf16 Out [T, H] = sum_j w[t, j] * H2[t*k + j]."""
+    _need(H2, "H2", torch.bfloat16, 2)
+    H = H2.shape[1]
+    if H2.shape[0] != T * k:
+        raise ValueError("H2 must have T*k rows")
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32)
+        if topk_weights.numel() != T * k:
+            raise ValueError("topk_weights must have T*k entries")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=H2.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * H:
+        raise ValueError("out must be [T, H]")
+    lib = _lib.load()
+    _lib.check("w4_moe_sum", lib.w4_moe_sum(_ptr(H2), _ptr(topk_weights), _ptr(out), T, k, H,
+                                            _stream(H2)))
+    return out
+
+
+def w4_moe_route(logits, k, topk_ids=None, topk_weights=None):
+    """fp32 logits [T, E] -> (int32 ids [T, k], fp32 weights [T, k])."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32)
+    _need(topk_weights, "topk_weights", torch.float32)
+    if topk_ids.numel() != T * k or topk_weights.numel() != T * k:
+        raise ValueError("outputs must be [T, k]")
+    lib = _lib.load()
+    _lib.check("w4_moe_route", lib.w4_moe_route(_ptr(logits), T, E, k, _ptr(topk_ids),
+                                                _ptr(topk_weights), _stream(logits)))
+    return topk_ids, topk_weights

@@ -1,0 +1,172 @@
+// C ABI of libw4a16.so: argument validation and dispatch.
+//
+// Every entry point validates all of its arguments before enqueueing any
+// work, so a nonzero status leaves the outputs untouched.  Nothing here
+// allocates, synchronizes or reads device memory.
+#include "../../include/w4a16.h"
+
+#include "common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return W4_OK;
+  g_last_hip_error = (int)e;
+  return W4_ERR_HIP;
+}
+
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "ok";
+    case W4_ERR_NULL: return "null pointer";
+    case W4_ERR_SHAPE: return "bad shape";
+    case W4_ERR_MISALIGNED: return "misaligned pointer";
+    case W4_ERR_UNSUPPORTED: return "unsupported arguments";
+    case W4_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int w4_last_hip_error(void) { return g_last_hip_error; }
+
+const char* w4_version(void) { return "w4a16 gfx950 0.1"; }
+
+int w4_quantize_pack(const uint16_t* W, int64_t N, int64_t K, int32_t* Wq, uint16_t* S,
+                     void* stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (N == 0 || K == 0) return W4_OK;
+  if (!W || !Wq || !S) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
+  const int64_t words = N * (K / 8);
+  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_quantize(W, words, Wq, S, nullptr, false, as_stream(stream)));
+}
+
+int w4_fake_quant(const uint16_t* W, int64_t N, int64_t K, uint16_t* W_fq, void* stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (N == 0 || K == 0) return W4_OK;
+  if (!W || !W_fq) return W4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(W_fq, 16)) return W4_ERR_MISALIGNED;
+  const int64_t words = N * (K / 8);
+  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  // in place is fine; partial overlap is not
+  const uintptr_t a = (uintptr_t)W, b = (uintptr_t)W_fq, len = (uintptr_t)(words * 16);
+  if (a != b && a < b + len && b < a + len) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_quantize(W, words, nullptr, nullptr, W_fq, true, as_stream(stream)));
+}
+
+int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!Y) return W4_ERR_NULL;
+  if (!aligned(Y, 4)) return W4_ERR_MISALIGNED;
+  if (M > kMaxI32 || N > kMaxI32 || K > kMaxI32 || M * N > ((int64_t)1 << 40) ||
+      N * (K / 8) > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (K == 0) return hip_status(w4::launch_zero_bf16(Y, M * N, as_stream(stream)));
+  if (!X || !Wq || !S) return W4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
+  if (M <= 32) return hip_status(w4::launch_gemv(X, Wq, S, Y, M, N, K, as_stream(stream)));
+  if ((M + 255) / 256 > 65535) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_gemm(X, Wq, S, Y, M, N, K, as_stream(stream)));
+}
+
+int32_t w4_pick_block_size(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const int64_t mean = (T * k + E - 1) / E;
+  int64_t p = 1;
+  while (p < mean) p *= 2;
+  if (p < 16) p = 16;
+  if (p > 64) p = 64;
+  return (int32_t)p;
+}
+
+int64_t w4_moe_align_capacity(int64_t T, int32_t k, int32_t E, int32_t B) {
+  if (T < 0 || k < 1 || E < 1 || B < 1) return -1;
+  const int64_t n = T * k + (int64_t)E * (B - 1);
+  return ((n + B - 1) / B) * B;
+}
+
+int moe_align_block_size(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t B,
+                         int32_t* sorted_token_ids, int32_t* expert_ids,
+                         int32_t* num_tokens_post_padded, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || B < 1) return W4_ERR_SHAPE;
+  if (E > 1024 || B > 1024) return W4_ERR_UNSUPPORTED;
+  if (T * k + (int64_t)E * B >= kMaxI32) return W4_ERR_UNSUPPORTED;
+  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded) return W4_ERR_NULL;
+  if (T > 0 && !topk_ids) return W4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4))
+    return W4_ERR_MISALIGNED;
+  const int64_t cap = w4_moe_align_capacity(T, k, E, B);
+  return hip_status(w4::launch_align(topk_ids, T, k, E, B, cap, sorted_token_ids, expert_ids,
+                                     num_tokens_post_padded, as_stream(stream)));
+}
+
+int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, const float* topk_weights, uint16_t* Y,
+                   int64_t T, int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
+                   int32_t x_row_div, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
+  if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
+  if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
+  if (T * k + (int64_t)E * B >= kMaxI32 || N > kMaxI32 || K > kMaxI32 ||
+      (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (T == 0) return W4_OK;
+  if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y)
+    return W4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2) || !aligned(Y, 4) ||
+      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4) || !aligned(topk_weights, 4))
+    return W4_ERR_MISALIGNED;
+  const int64_t blocks = w4_moe_align_capacity(T, k, E, B) / B;
+  if (blocks > 65535) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids,
+                                        num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B,
+                                        x_row_div, as_stream(stream)));
+}
+
+int w4_silu_mul(const uint16_t* H1, uint16_t* A, int64_t R, int64_t I, void* stream) {
+  if (R < 0 || I < 0 || I % 2 != 0) return W4_ERR_SHAPE;
+  if (R == 0 || I == 0) return W4_OK;
+  if (!H1 || !A) return W4_ERR_NULL;
+  if (!aligned(H1, 4) || !aligned(A, 4)) return W4_ERR_MISALIGNED;
+  return hip_status(w4::launch_silu_mul(H1, A, R, I, as_stream(stream)));
+}
+
+int w4_moe_sum(const uint16_t* H2, const float* topk_weights, uint16_t* Out, int64_t T, int32_t k,
+               int64_t H, void* stream) {
+  if (T < 0 || k < 1 || H < 0 || H % 2 != 0) return W4_ERR_SHAPE;
+  if (T == 0 || H == 0) return W4_OK;
+  if (!H2 || !Out) return W4_ERR_NULL;
+  if (!aligned(H2, 4) || !aligned(Out, 4) || !aligned(topk_weights, 4)) return W4_ERR_MISALIGNED;
+  return hip_status(w4::launch_moe_sum(H2, topk_weights, Out, T, k, H, as_stream(stream)));
+}
+
+int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                 float* topk_weights, void* stream) {
+  if (T < 0 || E < 1 || k < 1) return W4_ERR_SHAPE;
+  if (E > 1024 || k > 16 || k > E) return W4_ERR_UNSUPPORTED;
+  if (T == 0) return W4_OK;
+  if (!logits || !topk_ids || !topk_weights) return W4_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return W4_ERR_MISALIGNED;
+  return hip_status(w4::launch_route(logits, T, E, k, topk_ids, topk_weights, as_stream(stream)));
+}
+
+}  // extern "C"

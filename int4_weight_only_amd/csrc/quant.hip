@@ -1,0 +1,89 @@
+// Symmetric group-wise INT4 quantization, packing and fake quantization.
+//
+// Method: "Quantization basics: from FP32 to INT4", §2.2 (z = 0,
+// s = max|w| / q_max, q = clamp(round(w / s))) and §5 (round half to even,
+// never a truncating cast); "Quantization-aware training" tag summary [11]
+// (one scale per 1 x 32 group); "INT4 QAT end-to-end for RL" §3.2 (eight
+// INT4 codes packed into one INT32) and §2.1 (fake quantization restores
+// the weight to bf16 right after mapping it onto the INT4 grid).
+//
+// Mapping: one lane owns 8 consecutive elements (16 bytes in, one packed
+// word out), four neighbouring lanes own one 32-element group.  The group
+// maximum is combined across the quad with two DPP quad permutes, so every
+// load and store is a contiguous, fully coalesced vector access and no LDS
+// is used.  K % 32 == 0 makes groups tile the flattened [N*K] array, so the
+// kernel works on flat word indices.
+#include "common.h"
+
+namespace w4 {
+
+template <bool FAKE>
+__global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, int64_t words,
+                                                  uint32_t* __restrict__ Wq,
+                                                  uint16_t* __restrict__ S, u32x4* Wfq) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // words % 4 == 0 and blocks start on multiples of 4, so a quad is either
+  // entirely inside or entirely past the end: no DPP reads an exited lane.
+  if (i >= words) return;
+  const u32x4 v = W[i];
+  const float w[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  // For finite bf16, |w| orders like its 15-bit magnitude field.
+  uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  a = max(a, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+  a = max(a, quad_xor1(a));
+  a = max(a, quad_xor2(a));
+  const float amax = __uint_as_float(a << 16);
+  const uint16_t sb = to_bf16(amax / 7.0f);   // IEEE fp32 division, then RNE
+  const float s = bf16f(sb);
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = rintf(w[j] / s);         // IEEE division, half to even
+    q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r, -8.0f), 7.0f);
+  }
+  if constexpr (!FAKE) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= ((uint32_t)(int)q[j] & 0xFu) << (4 * j);
+    Wq[i] = word;
+    if ((i & 3) == 0) S[i >> 2] = sb;
+  } else {
+    // q * s is exact in fp32; one rounding to bf16.  Adding +0 turns the
+    // -0 that rintf gives for small negative w into the code 0's +0.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = q[j] + 0.0f;
+    u32x4 o;
+    o.x = pk_bf16(q[0] * s, q[1] * s);
+    o.y = pk_bf16(q[2] * s, q[3] * s);
+    o.z = pk_bf16(q[4] * s, q[5] * s);
+    o.w = pk_bf16(q[6] * s, q[7] * s);
+    Wfq[i] = o;
+  }
+}
+
+hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16_t* S,
+                           uint16_t* Wfq, bool fake, hipStream_t st) {
+  const int64_t blocks = (words + 255) / 256;
+  if (fake)
+    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const u32x4*)W, words, nullptr, nullptr, (u32x4*)Wfq);
+  else
+    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const u32x4*)W, words, (uint32_t*)Wq, S, nullptr);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero_bf16(uint16_t* __restrict__ Y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    Y[i] = 0;
+}
+
+hipError_t launch_zero_bf16(uint16_t* Y, int64_t n, hipStream_t st) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_zero_bf16, dim3((unsigned)blocks), dim3(256), 0, st, Y, n);
+  return hipGetLastError();
+}
+
+}  // namespace w4

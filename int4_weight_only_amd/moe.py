@@ -1,0 +1,115 @@
+"""A top-k routed MoE layer with W4A16 experts, composed from the C ABI.
+
+Every step is one library call; this module only allocates buffers with
+PyTorch and passes them along ("INT4 QAT end-to-end for RL", §4: routing,
+moe_align_block_size, the fused expert GEMMs):
+
+    logits --w4_moe_route--> ids, weights
+    ids --moe_align_block_size--> sorted_token_ids, expert_ids, ntpp
+    X --w4a16_moe_gemm (gate_up, x_row_div = k)--> H1 [T*k, 2I]
+    H1 --w4_silu_mul--> A [T*k, I]
+    A --w4a16_moe_gemm (down, x_row_div = 1)--> H2 [T*k, H]
+    H2, weights --w4_moe_sum--> Out [T, H]
+
+The activation (silu(gate) * up, gate = the first I rows of gate_up) and
+the combine (weights applied after the down projection) are readings: the
+pages name the gate_up / down pair but give no formula.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
+               w4_pick_block_size, w4_quantize_pack, w4_silu_mul, w4a16_moe_gemm)
+
+
+@dataclass
+class ExpertWeights:
+    """Stacked packed weights of E experts: Wq int32 [E, N, K/8], S bf16 [E, N, K/32]."""
+    Wq: torch.Tensor
+    S: torch.Tensor
+
+    @property
+    def E(self):
+        return self.Wq.shape[0]
+
+    @property
+    def N(self):
+        return self.Wq.shape[1]
+
+    @property
+    def K(self):
+        return self.Wq.shape[2] * 8
+
+    def nbytes(self):
+        return self.Wq.numel() * 4 + self.S.numel() * 2
+
+
+def quantize_experts(E, N, K, source, device):
+    """Quantize E expert matrices one at a time into stacked buffers.
+
+    ``source(e)`` returns expert e's bf16 [N, K] weight on ``device``; only
+    one source matrix is alive at a time.
+    """
+    Wq = torch.empty((E, N, K // 8), dtype=torch.int32, device=device)
+    S = torch.empty((E, N, K // 32), dtype=torch.bfloat16, device=device)
+    for e in range(E):
+        w = source(e)
+        w4_quantize_pack(w, Wq[e], S[e])
+        del w
+    return ExpertWeights(Wq, S)
+
+
+@dataclass
+class MoEBuffers:
+    sorted_token_ids: torch.Tensor
+    expert_ids: torch.Tensor
+    ntpp: torch.Tensor
+    H1: torch.Tensor
+    A: torch.Tensor
+    H2: torch.Tensor
+    out: torch.Tensor
+
+
+def alloc_buffers(T, k, E, H, I, B, device):
+    cap = w4_moe_align_capacity(T, k, E, B)
+    i32 = dict(dtype=torch.int32, device=device)
+    bf = dict(dtype=torch.bfloat16, device=device)
+    return MoEBuffers(torch.empty(cap, **i32), torch.empty(cap // B, **i32),
+                      torch.empty(1, **i32), torch.empty((T * k, 2 * I), **bf),
+                      torch.empty((T * k, I), **bf), torch.empty((T * k, H), **bf),
+                      torch.empty((T, H), **bf))
+
+
+def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None):
+    """Expert part of the layer for routed tokens.
+
+    X bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
+    gate_up: E experts of [2I, H]; down: E experts of [H, I].  B defaults to
+    ``w4_pick_block_size``.  Returns (Out bf16 [T, H], buffers).
+    """
+    T, H = X.shape
+    k = topk_ids.shape[1]
+    E = gate_up.E
+    I = gate_up.N // 2
+    if down.E != E or down.N != H or down.K != I or gate_up.K != H:
+        raise ValueError("expert weight shapes do not match X")
+    if B is None:
+        B = w4_pick_block_size(T, k, E)
+    b = buffers or alloc_buffers(T, k, E, H, I, B, X.device)
+    moe_align_block_size(topk_ids, E, B, b.sorted_token_ids, b.expert_ids, b.ntpp)
+    w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
+                   T, k, B, k, out=b.H1)
+    w4_silu_mul(b.H1, out=b.A)
+    w4a16_moe_gemm(b.A, down.Wq, down.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
+                   T, k, B, 1, out=b.H2)
+    w4_moe_sum(b.H2, topk_weights, T, k, out=b.out)
+    return b.out, b
+
+
+def moe_layer(X, logits, k, gate_up, down, B=None, buffers=None):
+    """Routing plus ``moe_forward``: logits fp32 [T, E] -> Out bf16 [T, H]."""
+    ids, w = w4_moe_route(logits, k)
+    out, b = moe_forward(X, ids, w, gate_up, down, B, buffers)
+    return out, ids, w, b

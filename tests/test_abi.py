@@ -1,0 +1,206 @@
+"""The C ABI without a GPU: exported symbols, host-side helpers, and every
+argument check that returns before anything is enqueued.
+
+None of these calls reaches the HIP runtime: each one fails validation, or
+is a pure host function, so they run on a CPU-only machine as long as the
+library loads.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import moe as omoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+# fake, never-dereferenced device addresses
+A16 = ctypes.c_void_p(0x10000)        # 16-byte aligned
+A4 = ctypes.c_void_p(0x10004)         # 4-byte aligned only
+A2 = ctypes.c_void_p(0x10002)         # 2-byte aligned only
+A1 = ctypes.c_void_p(0x10001)
+
+OK, NULL, SHAPE, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3, 4
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"#[^\n]*", "", text)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}]*\)\s*;", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from int4_weight_only_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for must in ("w4_quantize_pack", "w4_fake_quant", "w4a16_gemm", "moe_align_block_size",
+                 "w4a16_moe_gemm"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from int4_weight_only_amd import _lib
+    names = header_functions()
+    assert sorted(_lib.SIGNATURES) == names
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_binding_names_match_the_abi():
+    import int4_weight_only_amd as w
+    for n in header_functions():
+        if n in ("w4_status_string", "w4_last_hip_error", "w4_version"):
+            continue
+        assert callable(getattr(w, n)), n
+
+
+def test_status_strings(lib):
+    assert lib.w4_status_string(0) == b"ok"
+    for s in range(1, 6):
+        assert lib.w4_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.w4_status_string(99) == b"unknown status"
+    assert lib.w4_last_hip_error() == 0
+    assert lib.w4_version().startswith(b"w4a16")
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    from int4_weight_only_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libw4a16.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()
+
+
+# ---------------------------------------------------------------- helpers --
+
+@pytest.mark.parametrize("T,k,E", [(256, 8, 128), (4096, 8, 384), (1, 1, 1), (0, 8, 16),
+                                   (7, 3, 5), (100000, 8, 64), (3, 2, 1000)])
+def test_pick_block_size_matches_rule(lib, T, k, E):
+    assert lib.w4_pick_block_size(T, k, E) == omoe.pick_block_size(T, k, E)
+
+
+def test_pick_block_size_bad_args(lib):
+    assert lib.w4_pick_block_size(-1, 8, 16) == 0
+    assert lib.w4_pick_block_size(4, 0, 16) == 0
+    assert lib.w4_pick_block_size(4, 8, 0) == 0
+
+
+@pytest.mark.parametrize("T,k,E,B", [(256, 8, 128, 16), (4096, 8, 384, 64), (0, 1, 1, 1),
+                                     (5, 3, 7, 1), (3, 2, 1024, 1024), (1, 8, 3, 5)])
+def test_capacity_matches_oracle(lib, T, k, E, B):
+    assert lib.w4_moe_align_capacity(T, k, E, B) == omoe.capacity(T, k, E, B)
+
+
+def test_capacity_bad_args(lib):
+    assert lib.w4_moe_align_capacity(-1, 1, 1, 1) == -1
+    assert lib.w4_moe_align_capacity(1, 0, 1, 1) == -1
+    assert lib.w4_moe_align_capacity(1, 1, 0, 1) == -1
+    assert lib.w4_moe_align_capacity(1, 1, 1, 0) == -1
+
+
+# ---------------------------------------------------- validation, no launch --
+
+def test_quantize_pack_validation(lib):
+    f = lib.w4_quantize_pack
+    assert f(A16, 4, 33, A16, A2, None) == SHAPE
+    assert f(A16, -1, 32, A16, A2, None) == SHAPE
+    assert f(None, 0, 32, None, None, None) == OK            # empty: no-op
+    assert f(A16, 4, 0, A16, A2, None) == OK
+    assert f(None, 4, 32, A16, A2, None) == NULL
+    assert f(A16, 4, 32, None, A2, None) == NULL
+    assert f(A16, 4, 32, A16, None, None) == NULL
+    assert f(A4, 4, 32, A16, A2, None) == MISALIGNED
+    assert f(A16, 4, 32, A4, A2, None) == MISALIGNED
+    assert f(A16, 4, 32, A16, A1, None) == MISALIGNED
+
+
+def test_fake_quant_validation(lib):
+    f = lib.w4_fake_quant
+    assert f(A16, 4, 48, A16, None) == SHAPE
+    assert f(None, 4, 32, A16, None) == NULL
+    assert f(A16, 4, 32, None, None) == NULL
+    assert f(A4, 4, 32, ctypes.c_void_p(0x20000), None) == MISALIGNED
+    # partial overlap is refused, exact aliasing is allowed (not launched here)
+    assert f(ctypes.c_void_p(0x10000), 4, 32, ctypes.c_void_p(0x10010), None) == UNSUPPORTED
+
+
+def test_gemm_validation(lib):
+    f = lib.w4a16_gemm
+    assert f(A16, A16, A2, A4, 4, 8, 40, None) == SHAPE
+    assert f(A16, A16, A2, A4, -1, 8, 32, None) == SHAPE
+    assert f(None, None, None, None, 0, 8, 32, None) == OK    # M == 0
+    assert f(None, None, None, None, 4, 0, 32, None) == OK    # N == 0
+    assert f(None, A16, A2, A4, 4, 8, 32, None) == NULL
+    assert f(A16, None, A2, A4, 4, 8, 32, None) == NULL
+    assert f(A16, A16, None, A4, 4, 8, 32, None) == NULL
+    assert f(A16, A16, A2, None, 4, 8, 32, None) == NULL
+    assert f(A4, A16, A2, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A4, A2, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A2, A2, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A2, A4, 1 << 40, 8, 32, None) == UNSUPPORTED
+
+
+def test_align_validation(lib):
+    f = lib.moe_align_block_size
+    assert f(A4, 4, 0, 8, 16, A4, A4, A4, None) == SHAPE
+    assert f(A4, 4, 2, 0, 16, A4, A4, A4, None) == SHAPE
+    assert f(A4, 4, 2, 8, 0, A4, A4, A4, None) == SHAPE
+    assert f(A4, -1, 2, 8, 16, A4, A4, A4, None) == SHAPE
+    assert f(A4, 4, 2, 1025, 16, A4, A4, A4, None) == UNSUPPORTED
+    assert f(A4, 4, 2, 8, 1025, A4, A4, A4, None) == UNSUPPORTED
+    assert f(A4, 1 << 30, 8, 8, 16, A4, A4, A4, None) == UNSUPPORTED
+    assert f(None, 4, 2, 8, 16, A4, A4, A4, None) == NULL
+    assert f(A4, 4, 2, 8, 16, None, A4, A4, None) == NULL
+    assert f(A4, 4, 2, 8, 16, A4, None, A4, None) == NULL
+    assert f(A4, 4, 2, 8, 16, A4, A4, None, None) == NULL
+    assert f(A2, 4, 2, 8, 16, A4, A4, A4, None) == MISALIGNED
+    assert f(A4, 4, 2, 8, 16, A2, A4, A4, None) == MISALIGNED
+
+
+def test_moe_gemm_validation(lib):
+    f = lib.w4a16_moe_gemm
+    good = [A16, A16, A2, A4, A4, A4, None, A4]
+    assert f(*good, 4, 2, 8, 64, 48, 16, 1, None) == SHAPE        # K % 32
+    assert f(*good, 4, 2, 8, 64, 64, 16, 3, None) == SHAPE        # x_row_div
+    assert f(*good, 4, 2, 8, 0, 64, 16, 1, None) == SHAPE         # N
+    assert f(*good, 4, 0, 8, 64, 64, 16, 1, None) == SHAPE        # k
+    assert f(*good, 4, 2, 8, 64, 64, 0, 1, None) == SHAPE         # B
+    assert f(*good, 4, 2, 2000, 64, 64, 16, 1, None) == UNSUPPORTED
+    assert f(*good, 0, 2, 8, 64, 64, 16, 1, None) == OK           # T == 0: no-op
+    bad_null = list(good)
+    bad_null[3] = None
+    assert f(*bad_null, 4, 2, 8, 64, 64, 16, 1, None) == NULL
+    bad_al = list(good)
+    bad_al[0] = A4
+    assert f(*bad_al, 4, 2, 8, 64, 64, 16, 1, None) == MISALIGNED
+    bad_tw = list(good)
+    bad_tw[6] = A2
+    assert f(*bad_tw, 4, 2, 8, 64, 64, 16, 1, None) == MISALIGNED
+
+
+def test_elementwise_validation(lib):
+    assert lib.w4_silu_mul(A4, A4, 4, 3, None) == SHAPE
+    assert lib.w4_silu_mul(None, A4, 4, 4, None) == NULL
+    assert lib.w4_silu_mul(A2, A4, 4, 4, None) == MISALIGNED
+    assert lib.w4_silu_mul(None, None, 0, 4, None) == OK
+    assert lib.w4_moe_sum(A4, None, A4, 4, 2, 3, None) == SHAPE
+    assert lib.w4_moe_sum(A4, None, A4, 4, 0, 4, None) == SHAPE
+    assert lib.w4_moe_sum(None, None, A4, 4, 2, 4, None) == NULL
+    assert lib.w4_moe_sum(A4, A2, A4, 4, 2, 4, None) == MISALIGNED
+    assert lib.w4_moe_route(A4, 4, 8, 9, A4, A4, None) == UNSUPPORTED
+    assert lib.w4_moe_route(A4, 4, 2000, 8, A4, A4, None) == UNSUPPORTED
+    assert lib.w4_moe_route(A4, 4, 64, 17, A4, A4, None) == UNSUPPORTED
+    assert lib.w4_moe_route(None, 4, 64, 8, A4, A4, None) == NULL
+    assert lib.w4_moe_route(A2, 4, 64, 8, A4, A4, None) == MISALIGNED
+    assert lib.w4_moe_route(None, 0, 64, 8, None, None, None) == OK
