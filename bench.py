@@ -1,0 +1,345 @@
+"""Throughput of the INT4 weight-only hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections ...]
+                    [--no-cpu-baseline]
+
+Headline line (one JSON object on stdout): the decode W4A16 product over
+packed INT4 weights W[12288 x 4096] (group 32, bf16 scales) against
+M in {1, 8, 16, 32} bf16 activation rows.  One step = those four products,
+each on its own copy of the weights (24 copies rotate, 680 MB in all, so
+the 256 MB last-level cache never holds the step's weights).  ``value`` is
+the algorithmic HBM traffic of the step (packed codes + scales + X + Y)
+over the step time, HIP events on the launch stream around exactly K steps.
+
+The other workloads of the path are timed in the same run and reported
+under "detail": the prefill product (M = 4096, N = 14336, K = 4096,
+TFLOP/s), quantize + pack and fake quant of that weight (GB/s), and the two
+routed MoE layers (128 experts / top-8 / hidden 4096 / intermediate 1536 at
+256 tokens; 384 experts / top-8 / hidden 7168 / intermediate 2048 at 4096
+tokens with skewed routing), per stage and whole layer.
+
+The CPU oracle is timed on this host on one full decode step (the same
+four products over the same weight shape), as a reported baseline.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMM: decode HBM GB/s (% peak) + prefill/MoE TFLOP/s (% MFMA peak)"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+DECODE_N, DECODE_K, DECODE_MS = 12288, 4096, (1, 8, 16, 32)
+ROTATE = 24
+
+
+def decode_bytes(M, N=DECODE_N, K=DECODE_K):
+    """Algorithmic bytes of one decode product: codes + scales + X + Y."""
+    return N * K // 2 + 2 * N * (K // 32) + 2 * M * K + 2 * M * N
+
+
+def gemm_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sections", default="decode,prefill,quant,moe_qwen,moe_kimi")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the current (launch) stream around a region."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters):
+        torch = self.torch
+        st = torch.cuda.current_stream()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(st)
+        for i in range(iters):
+            fn(i)
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)          # ms for all iterations
+
+
+def source_hash():
+    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int4_weight_only_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------- sections --
+
+def bench_decode(w4, synth, torch, steps, warmup, timer):
+    dev = torch.device("cuda")
+    src = synth.weights(DECODE_N, DECODE_K, synth.WORKLOADS["decode"]["seed"], device=dev)
+    Wq0, S0 = w4.w4_quantize_pack(src)
+    del src
+    Wqs = [Wq0] + [Wq0.clone() for _ in range(ROTATE - 1)]
+    Ss = [S0] + [S0.clone() for _ in range(ROTATE - 1)]
+    Xs = {M: synth.activations(M, DECODE_K, 1, device=dev) for M in DECODE_MS}
+    Ys = {M: torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
+
+    def step(i):
+        for j, M in enumerate(DECODE_MS):
+            r = (4 * i + j) % ROTATE
+            w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
+
+    timer.run(step, warmup)
+    ms = timer.run(step, steps)
+    step_bytes = sum(decode_bytes(M) for M in DECODE_MS)
+    per_m = {}
+    for M in DECODE_MS:
+        def one(i, M=M):
+            r = i % ROTATE
+            w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
+        timer.run(one, warmup)
+        t = timer.run(one, steps) / steps
+        per_m[str(M)] = {"us": round(t * 1e3, 3),
+                         "GB/s": round(decode_bytes(M) / (t * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(decode_bytes(M) / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    launches = steps * len(DECODE_MS)
+    return dict(ms_step=ms / steps, step_bytes=step_bytes, launches=launches, total_ms=ms,
+                per_m=per_m)
+
+
+def bench_prefill(w4, synth, torch, iters, timer):
+    wl = synth.WORKLOADS["prefill"]
+    M, N, K = wl["M"][0], wl["N"], wl["K"]
+    dev = torch.device("cuda")
+    W = synth.weights(N, K, wl["seed"], device=dev)
+    X = synth.activations(M, K, wl["seed"], device=dev)
+    Wq, S = w4.w4_quantize_pack(W)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    f = lambda i: w4.w4a16_gemm(X, Wq, S, out=Y)
+    timer.run(f, 2)
+    t = timer.run(f, iters) / iters
+    tf = gemm_flops(M, N, K) / (t * 1e-3) / 1e12
+    return {"M": M, "N": N, "K": K, "us": round(t * 1e3, 1), "TFLOP/s": round(tf, 1),
+            "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_quant(w4, synth, torch, iters, timer):
+    wl = synth.WORKLOADS["prefill"]
+    N, K = wl["N"], wl["K"]
+    dev = torch.device("cuda")
+    W = synth.weights(N, K, wl["seed"], device=dev)
+    Wq = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    S = torch.empty((N, K // 32), dtype=torch.bfloat16, device=dev)
+    Wf = torch.empty_like(W)
+    out = {}
+    qp_bytes = 2 * N * K + N * K // 2 + 2 * N * (K // 32)
+    fq_bytes = 4 * N * K
+    for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
+                             ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes)):
+        timer.run(fn, 3)
+        t = timer.run(fn, iters) / iters
+        gbs = nbytes / (t * 1e-3) / 1e9
+        out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "bytes": nbytes,
+                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
+    wl = synth.WORKLOADS[name]
+    T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
+    dev = torch.device("cuda")
+    gate_up = wmoe.quantize_experts(E, 2 * I, H,
+                                    lambda e: synth.expert_gate_up(e, I, H, seed, dev), dev)
+    down = wmoe.quantize_experts(E, H, I, lambda e: synth.expert_down(e, I, H, seed, dev), dev)
+    X = synth.activations(T, H, seed, device=dev)
+    logits = synth.router_logits(T, E, seed, wl["skew"], device=dev)
+    B = w4.w4_pick_block_size(T, k, E)
+    ids, tw = w4.w4_moe_route(logits, k)
+    buf = wmoe.alloc_buffers(T, k, E, H, I, B, dev)
+    tw_flat = tw.reshape(-1)
+
+    stages = {
+        "route": lambda: w4.w4_moe_route(logits, k, ids, tw),
+        "align": lambda: w4.moe_align_block_size(ids, E, B, buf.sorted_token_ids,
+                                                 buf.expert_ids, buf.ntpp),
+        "gate_up": lambda: w4.w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, buf.sorted_token_ids,
+                                             buf.expert_ids, buf.ntpp, T, k, B, k, out=buf.H1),
+        "silu_mul": lambda: w4.w4_silu_mul(buf.H1, out=buf.A),
+        "down": lambda: w4.w4a16_moe_gemm(buf.A, down.Wq, down.S, buf.sorted_token_ids,
+                                          buf.expert_ids, buf.ntpp, T, k, B, 1, out=buf.H2),
+        "combine": lambda: w4.w4_moe_sum(buf.H2, tw, T, k, out=buf.out),
+    }
+
+    def layer(i):
+        for fn in stages.values():
+            fn()
+
+    timer.run(layer, 2)
+    t_layer = timer.run(layer, iters) / iters
+    per = {}
+    for sname, fn in stages.items():
+        t = timer.run(lambda i: fn(), iters) / iters
+        per[sname] = round(t * 1e3, 2)
+    pairs = T * k
+    fl_gu = gemm_flops(pairs, 2 * I, H)
+    fl_dn = gemm_flops(pairs, H, I)
+    wbytes = gate_up.nbytes() + down.nbytes()
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=E)
+    ntpp = int(buf.ntpp.item())
+    res = {
+        "T": T, "E": E, "k": k, "H": H, "I": I, "B": B,
+        "layer_us": round(t_layer * 1e3, 1),
+        "stage_us": per,
+        "layer_TFLOP/s": round((fl_gu + fl_dn) / (t_layer * 1e-3) / 1e12, 1),
+        "gate_up_TFLOP/s": round(fl_gu / (per["gate_up"] * 1e-6) / 1e12, 1),
+        "down_TFLOP/s": round(fl_dn / (per["down"] * 1e-6) / 1e12, 1),
+        "weight_bytes": wbytes,
+        "gemm_weight_GB/s": round(wbytes / ((per["gate_up"] + per["down"]) * 1e-6) / 1e9, 1),
+        "frac_mfma_bf16_gemms": round((fl_gu + fl_dn) / ((per["gate_up"] + per["down"]) * 1e-6)
+                                      / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "frac_hbm_gemms": round(wbytes / ((per["gate_up"] + per["down"]) * 1e-6) / 1e9
+                                / PEAK_HBM_GBS, 4),
+        "rows_per_expert_max": int(counts.max().item()),
+        "rows_per_expert_min": int(counts.min().item()),
+        "padding_frac": round(1.0 - pairs / ntpp, 4),
+    }
+    del gate_up, down, buf
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on one full decode step on this host."""
+    import numpy as np  # noqa: F401
+    import synth
+    from oracle import gemm, quant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    seed = synth.WORKLOADS["decode"]["seed"]
+    Wb = synth.bits(synth.weights(DECODE_N, DECODE_K, seed))
+    Wq, S = quant.quantize_pack(Wb)
+    Xs = {M: synth.bits(synth.activations(M, DECODE_K, 1)) for M in DECODE_MS}
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for M in DECODE_MS:
+            gemm.w4a16_gemm(Xs[M], Wq, S)
+        reps += 1
+        if reps >= 2 or time.perf_counter() - t0 > 20:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = reps * sum(decode_bytes(M) for M in DECODE_MS)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full decode step(s): M in {{1,8,16,32}} x W[12288x4096] "
+                      f"int4 g32, numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(no collectives, no sharding); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_weight_only_amd as w4
+    from int4_weight_only_amd import moe as wmoe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    sections = [s for s in args.sections.split(",") if s]
+    detail = {}
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    dec = None
+    if "decode" in sections:
+        log("bench: decode sweep")
+        dec = bench_decode(w4, synth, torch, args.steps, args.warmup, timer)
+        detail["decode_per_M"] = dec["per_m"]
+    iters = max(3, min(args.steps, 20))
+    if "prefill" in sections:
+        log("bench: prefill")
+        detail["prefill"] = bench_prefill(w4, synth, torch, iters, timer)
+    if "quant" in sections:
+        log("bench: quantize_pack / fake_quant")
+        detail.update(bench_quant(w4, synth, torch, iters, timer))
+    for name in ("moe_qwen", "moe_kimi"):
+        if name in sections:
+            log(f"bench: {name}")
+            detail[name] = bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu oracle baseline")
+        cpu = cpu_baseline()
+
+    line = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "decode W4A16 GEMV sweep: packed int4 W[12288x4096] group 32 "
+                                   "bf16 scales, X[M,4096] bf16, M in {1,8,16,32}",
+                       "rotating_weight_copies": ROTATE}}
+    if dec is not None:
+        value = dec["step_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
+        per_launch_bytes = dec["step_bytes"] / len(DECODE_MS)
+        per_launch_us = dec["total_ms"] * 1e3 / dec["launches"]
+        achieved = per_launch_bytes / (per_launch_us * 1e-6) / 1e9
+        traffic = stored_traffic("decode_gemv")
+        line.update(value=round(value, 1), ms_per_step=round(dec["ms_step"], 5))
+        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(achieved / PEAK_HBM_GBS, 4),
+                            "traffic": traffic,
+                            "kernel": "k_gemv (decode W4A16 product)",
+                            "algorithmic_bytes_per_launch": per_launch_bytes,
+                            "avg_launch_us": round(per_launch_us, 3)}
+    else:
+        line.update(value=None, ms_per_step=None)
+    line["cpu_baseline"] = cpu
+    line["detail"] = detail
+    line["source_hash"] = source_hash()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
-    const float* __restrict__ topk_w, int n_pairs, int B, int x_row_div) {
+    const float* __restrict__ topk_w, int n_pairs, int B, int x_row_div, int E) {
   constexpr int NT = NW * 64;
   constexpr int MS = BM / 32;          // 32-row MFMA tiles along M
   constexpr int NS = WN / 32;          // 32-col MFMA tiles along N per wave
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
           if (expert_ids[mid] <= e) lo = mid + 1; else hi = mid;
         }
         const int blocks_per_wg = BM >= B ? BM / B : 1;
-        if (e >= 0 && ((b - first) % blocks_per_wg) == 0) {
+        if (e >= 0 && e < E && ((b - first) % blocks_per_wg) == 0) {
           lead = 1;
           last = min(lo, b + blocks_per_wg);
         }
@@ -264,7 +264,7 @@ hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
   const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)), (unsigned)((M + kBM - 1) / kBM));
   hipLaunchKernelGGL((k_gemm<kBM, kWN, kNW, false>), grid, dim3(kNW * 64), 0, st, X,
                      (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr,
-                     nullptr, 0, 1, 1);
+                     nullptr, 0, 1, 1, 0);
   return hipGetLastError();
 }
 
@@ -273,13 +273,12 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                            int32_t x_row_div, hipStream_t st) {
-  (void)E;
   const int64_t n_pairs = T * k;
   const int64_t cap = ((n_pairs + (int64_t)E * (B - 1) + B - 1) / B) * B;
   const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)), (unsigned)(cap / B));
   hipLaunchKernelGGL((k_gemm<kBM, kWN, kNW, true>), grid, dim3(kNW * 64), 0, st, X,
                      (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
-                     topk_w, (int)n_pairs, (int)B, (int)x_row_div);
+                     topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
 }
 

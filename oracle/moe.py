@@ -113,13 +113,15 @@ def align(ids, E, B):
 # --------------------------------------------------------------------------
 
 def grouped_gemm(X, weights, sorted_ids, expert_ids, ntpp, B, x_row_div,
-                 n_pairs, topk_weights=None):
+                 n_pairs, topk_weights=None, experts=None):
     """Reference of the aligned grouped W4A16 GEMM.
 
     For every block b < ntpp / B with expert e = expert_ids[b], and every
     slot holding a valid pair f (f < n_pairs): row f of the result is
     X[f // x_row_div] * dequant(W_e)^T, multiplied by topk_weights.flat[f]
     when given.  ``weights(e)`` returns (Wq int32 [N, K/8], S bf16 [N, K/32]).
+    ``experts``, when given, restricts the product to blocks of those experts
+    (a sampled check at sizes where the whole product is too slow here).
     Returns {f: float64 row} for the rows written.
     """
     x = bf16.to_f32(X).astype(np.float64)
@@ -128,6 +130,8 @@ def grouped_gemm(X, weights, sorted_ids, expert_ids, ntpp, B, x_row_div,
     cache = {}
     for b in range(ntpp // B):
         e = int(expert_ids[b])
+        if experts is not None and e not in experts:
+            continue
         if e not in cache:
             cache.clear()
             Wq, S = weights(e)

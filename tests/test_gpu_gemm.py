@@ -1,0 +1,123 @@
+"""GPU parity: w4a16_gemm (decode GEMV path and MFMA GEMM path) against the
+fp64 oracle.
+
+Tolerance (per element, against the unrounded fp64 product):
+    |y - y_ref| <= 2e-2 + 1e-2 * |y_ref|
+Where every partial sum is an exact integer the output must be bit-exact.
+The weights fed to each side are quantized by that side (the GPU packing is
+asserted bit-exact against the oracle's first).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_amd as w4
+import synth
+from gpu_util import down, down_bits, say, up_bits
+from oracle import bf16, gemm, quant
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-2, 1e-2
+
+
+def quantized_pair(Wbits):
+    """(GPU Wq, GPU S, oracle Wq, oracle S) with the two packings equal."""
+    Wq_ref, S_ref = quant.quantize_pack(Wbits)
+    Wq, S = w4.w4_quantize_pack(up_bits(Wbits))
+    np.testing.assert_array_equal(down(Wq), Wq_ref)
+    np.testing.assert_array_equal(down_bits(S), S_ref)
+    return Wq, S, Wq_ref, S_ref
+
+
+def assert_close(y_bits, y_ref, label):
+    ok, max_abs, max_rel = gemm.within_tolerance(y_bits, y_ref, ATOL, RTOL)
+    assert ok, f"{label}: max abs {max_abs:.3e}, max rel {max_rel:.3e}"
+
+
+def run_case(M, N, K, seed, label):
+    say(f"gemm {label} M={M} N={N} K={K}")
+    Wb = synth.bits(synth.weights(N, K, seed))
+    Xb = synth.bits(synth.activations(M, K, seed))
+    Wq, S, Wq_ref, S_ref = quantized_pair(Wb)
+    y = down_bits(w4.w4a16_gemm(up_bits(Xb), Wq, S))
+    assert_close(y, gemm.w4a16_gemm(Xb, Wq_ref, S_ref), label)
+
+
+def test_dense_small_seed0():
+    wl = synth.WORKLOADS["dense_small"]
+    run_case(4, wl["N"], wl["K"], wl["seed"], "512x512")
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 16, 17, 31, 32, 33, 64, 127, 129, 300])
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (100, 544), (300, 64)])
+def test_ragged(M, N, K):
+    run_case(M, N, K, 100 + M + N + K, "ragged")
+
+
+@pytest.mark.parametrize("M", [1, 8, 17, 32, 33, 200])
+def test_integer_exact(M):
+    """amax = 7 in every group gives s = 1 and q = w; integer activations in
+    [-2, 2] keep every fp32 partial sum an exact integer, so Y must equal
+    bf16(X @ q^T) bit for bit whatever the summation order."""
+    N, K = 96, 4096
+    say(f"gemm integer-exact M={M}")
+    rng = np.random.default_rng(M)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.float32)
+    q.reshape(N, K // 32, 32)[:, :, 0] = 7.0
+    Xi = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wb, Xb = bf16.rne(q), bf16.rne(Xi)
+    Wq, S, _, S_ref = quantized_pair(Wb)
+    assert np.all(bf16.to_f32(S_ref) == 1.0)
+    y = down_bits(w4.w4a16_gemm(up_bits(Xb), Wq, S))
+    exact = Xi.astype(np.float64) @ q.astype(np.float64).T
+    np.testing.assert_array_equal(y, gemm.to_bf16(exact))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_decode_full(M):
+    wl = synth.WORKLOADS["decode"]
+    run_case(M, wl["N"], wl["K"], wl["seed"], "decode")
+
+
+def test_prefill_sampled():
+    """Full prefill shape; the oracle checks 96 sampled rows (all N) and 48
+    sampled columns (all M)."""
+    wl = synth.WORKLOADS["prefill"]
+    M, N, K = wl["M"][0], wl["N"], wl["K"]
+    say(f"gemm prefill M={M} N={N} K={K}")
+    Wb = synth.bits(synth.weights(N, K, wl["seed"]))
+    Xb = synth.bits(synth.activations(M, K, wl["seed"]))
+    Wq, S, Wq_ref, S_ref = quantized_pair(Wb)
+    y = down_bits(w4.w4a16_gemm(up_bits(Xb), Wq, S))
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(M, 96, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    assert_close(y[rows], gemm.w4a16_gemm(Xb[rows], Wq_ref, S_ref), "prefill rows")
+    cols = np.sort(rng.choice(N, 48, replace=False))
+    cols[-1] = N - 1
+    assert_close(y[:, cols], gemm.w4a16_gemm(Xb, Wq_ref[cols], S_ref[cols]), "prefill cols")
+
+
+def test_deterministic():
+    wl = synth.WORKLOADS["decode"]
+    Wq, S = w4.w4_quantize_pack(synth.weights(2048, wl["K"], 3).cuda())
+    for M in (8, 96):
+        X = synth.activations(M, wl["K"], 3).cuda()
+        a = down_bits(w4.w4a16_gemm(X, Wq, S))
+        b = down_bits(w4.w4a16_gemm(X, Wq, S))
+        np.testing.assert_array_equal(a, b)
+
+
+def test_k_zero_writes_zeros_and_m_zero_is_noop():
+    Y = torch.full((3, 5), 1.0, dtype=torch.bfloat16, device="cuda")
+    X = torch.empty((3, 0), dtype=torch.bfloat16, device="cuda")
+    Wq = torch.empty((5, 0), dtype=torch.int32, device="cuda")
+    S = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(X, Wq, S, out=Y)
+    assert torch.count_nonzero(Y).item() == 0
+    X0 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    Wq0 = torch.zeros((5, 8), dtype=torch.int32, device="cuda")
+    S0 = torch.zeros((5, 2), dtype=torch.bfloat16, device="cuda")
+    assert w4.w4a16_gemm(X0, Wq0, S0).shape == (0, 5)

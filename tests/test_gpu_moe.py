@@ -1,0 +1,284 @@
+"""GPU parity: routing, moe_align_block_size, the grouped W4A16 expert GEMM,
+SwiGLU, the top-k combine and the whole MoE layer, against the oracle.
+
+* moe_align_block_size: bit-exact over the whole output buffers (sentinels
+  and the -1 tail included), many shapes, block sizes and id patterns.
+* routing: ids exact (the oracle orders the same fp32 logits), weights to
+  fp32 rounding.
+* GEMMs and the layer: |y - y_ref| <= 2e-2 + 1e-2 |y_ref| against fp64.
+* Full-size expert layers (128 experts x [3072 x 4096] + [4096 x 1536],
+  and 384 experts x [4096 x 7168] + [7168 x 2048] with skewed routing):
+  alignment in full, GEMM rows of sampled experts and the layer output of
+  sampled tokens.  The GPU side is fed the oracle's routing (ids, weights)
+  so that the later stages never depend on a near-tie in fp32 softmax.
+Expert weight sources are drawn on the GPU by ``synth`` (seeded); the
+oracle gets the same bf16 sources downloaded and quantizes them itself.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_amd as w4
+from int4_weight_only_amd import moe as wmoe
+import synth
+from gpu_util import CANARY, canary_bf16, down, down_bits, say, up, up_bits
+from oracle import bf16, gemm, quant
+from oracle import moe as omoe
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-2, 1e-2
+
+
+def assert_rows_close(y_bits, ref_rows, label):
+    assert ref_rows, f"{label}: nothing to compare"
+    fs = sorted(ref_rows)
+    ref = np.stack([ref_rows[f] for f in fs])
+    ok, max_abs, max_rel = gemm.within_tolerance(y_bits[fs], ref, ATOL, RTOL)
+    assert ok, f"{label}: max abs {max_abs:.3e}, max rel {max_rel:.3e} over {len(fs)} rows"
+
+
+# ------------------------------------------------------------------ align --
+
+def id_cases():
+    rng = np.random.default_rng(0)
+    c3 = synth.WORKLOADS["moe_qwen"]
+    c4 = synth.WORKLOADS["moe_kimi"]
+    lg3 = synth.router_logits(c3["T"], c3["E"], c3["seed"]).numpy()
+    lg4 = synth.router_logits(c4["T"], c4["E"], c4["seed"], c4["skew"]).numpy()
+    ids3 = omoe.route(lg3, c3["k"])[0]
+    ids4 = omoe.route(lg4, c4["k"])[0]
+    cases = []
+    for B in (16, 32, 64):
+        cases.append(("qwen_route", ids3, c3["E"], B))
+    for B in (32, 64):
+        cases.append(("kimi_skew_route", ids4, c4["E"], B))
+    cases.append(("random_B1", synth.random_ids(256, 8, 128, 1).numpy(), 128, 1))
+    cases.append(("random_B5", synth.random_ids(97, 3, 40, 2).numpy(), 40, 5))
+    cases.append(("one_expert", np.zeros((300, 1), np.int32), 1, 16))
+    cases.append(("empty_T0", np.zeros((0, 8), np.int32), 16, 16))
+    cases.append(("single_pair", np.array([[3]], np.int32), 8, 16))
+    cases.append(("out_of_range", rng.integers(-3, 67, size=(500, 6)).astype(np.int32), 64, 16))
+    cases.append(("all_same", np.full((1000, 8), 5, np.int32), 64, 64))
+    cases.append(("E1024_B1024", rng.integers(0, 1024, size=(50, 4)).astype(np.int32), 1024, 1024))
+    cases.append(("big_T_small_E", rng.integers(0, 4, size=(9000, 2)).astype(np.int32), 4, 64))
+    return cases
+
+
+@pytest.mark.parametrize("case", id_cases(), ids=lambda c: c[0])
+def test_align_bit_exact(case):
+    name, ids, E, B = case
+    T, k = ids.shape
+    say(f"align {name} T={T} k={k} E={E} B={B}")
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    cap = w4.w4_moe_align_capacity(T, k, E, B)
+    # poison the outputs so that any slot the kernel leaves alone shows up
+    s = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    e = torch.full((cap // B,), -7, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    w4.moe_align_block_size(up(ids.astype(np.int32)), E, B, s, e, n)
+    np.testing.assert_array_equal(down(s), s_ref)
+    np.testing.assert_array_equal(down(e), e_ref)
+    assert int(down(n)[0]) == n_ref
+
+
+# ------------------------------------------------------------------ route --
+
+@pytest.mark.parametrize("T,E,k,kind", [(256, 128, 8, "qwen"), (4096, 384, 8, "kimi"),
+                                        (33, 5, 5, "rand"), (17, 1000, 16, "rand"),
+                                        (10, 64, 1, "rand"), (6, 32, 4, "ties")])
+def test_route(T, E, k, kind):
+    say(f"route {kind} T={T} E={E} k={k}")
+    if kind == "qwen":
+        c = synth.WORKLOADS["moe_qwen"]
+        lg = synth.router_logits(T, E, c["seed"]).numpy()
+    elif kind == "kimi":
+        c = synth.WORKLOADS["moe_kimi"]
+        lg = synth.router_logits(T, E, c["seed"], c["skew"]).numpy()
+    elif kind == "ties":
+        lg = np.zeros((T, E), np.float32)
+        lg[1, 7] = lg[1, 3] = 2.0
+        lg[2, :] = -1.5
+    else:
+        lg = synth.router_logits(T, E, T * E).numpy()
+    ids_ref, w_ref = omoe.route(lg, k)
+    ids, w = w4.w4_moe_route(up(lg), k)
+    np.testing.assert_array_equal(down(ids), ids_ref)
+    np.testing.assert_allclose(down(w), w_ref, rtol=2e-6, atol=1e-7)
+
+
+# ------------------------------------------------------ element-wise steps --
+
+def test_silu_mul():
+    R, I = 37, 96
+    say("silu_mul")
+    g = torch.Generator().manual_seed(9)
+    H1 = (torch.randn((R, 2 * I), generator=g) * 3.0).to(torch.bfloat16)
+    H1[0, :4] = torch.tensor([-100.0, 100.0, 0.0, -0.0])
+    Hb = synth.bits(H1)
+    ref = omoe.silu_mul(Hb)
+    A = down_bits(w4.w4_silu_mul(up_bits(Hb)))
+    a = bf16.to_f32(A).astype(np.float64)
+    # one bf16 rounding of an fp32 result: at most half a bf16 ulp + fp32 noise
+    assert np.all(np.abs(a - ref) <= 2.0 ** -8 * np.abs(ref) * 1.0001 + 1e-30)
+
+
+@pytest.mark.parametrize("weighted", [True, False])
+def test_moe_sum(weighted):
+    T, k, H = 23, 8, 96
+    say(f"moe_sum weighted={weighted}")
+    H2b = synth.bits(synth.activations(T * k, H, 5))
+    if weighted:
+        w = omoe.route(synth.router_logits(T, 64, 5).numpy(), k)[1]
+    else:
+        w = np.ones((T, k), np.float32)
+    ref = omoe.moe_sum(H2b, w)
+    out = down_bits(w4.w4_moe_sum(up_bits(H2b), up(w) if weighted else None, T, k))
+    o = bf16.to_f32(out).astype(np.float64)
+    scale = np.abs(bf16.to_f32(H2b)).max()
+    assert np.all(np.abs(o - ref) <= 2.0 ** -8 * np.abs(ref) * 1.0001 + 1e-5 * scale)
+
+
+# ------------------------------------------------------------ grouped GEMM --
+
+def small_experts(E, N, K, seed):
+    """E experts of bf16 [N, K] -> (GPU Wq [E,N,K/8], GPU S, oracle lookup)."""
+    srcs = [synth.bits(synth.weights(N, K, seed, stream=50 + e)) for e in range(E)]
+    ref = [quant.quantize_pack(s) for s in srcs]
+    Wq = torch.stack([up(r[0]) for r in ref])
+    S = torch.stack([up_bits(r[1]) for r in ref])
+    # the GPU packing of the same sources must match bit for bit
+    for e in range(E):
+        q, s = w4.w4_quantize_pack(up_bits(srcs[e]))
+        np.testing.assert_array_equal(down(q), ref[e][0])
+        np.testing.assert_array_equal(down_bits(s), ref[e][1])
+        Wq[e].copy_(q)
+        S[e].copy_(s)
+    return Wq, S, (lambda e: ref[e])
+
+
+@pytest.mark.parametrize("B", [1, 4, 16, 64, 200])
+@pytest.mark.parametrize("x_row_div_is_k", [True, False])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_moe_gemm_small(B, x_row_div_is_k, weighted):
+    E, T, k, N, K = 6, 40, 3, 96, 160
+    say(f"moe_gemm small B={B} div_k={x_row_div_is_k} weighted={weighted}")
+    rng = np.random.default_rng(B)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[0, 0] = -1                      # skipped pair: its row stays untouched
+    ids[5, 2] = E + 2
+    Wq, S, ref_w = small_experts(E, N, K, 21)
+    div = k if x_row_div_is_k else 1
+    Xb = synth.bits(synth.activations(T * k // div, K, 22))
+    tw = rng.random((T, k)).astype(np.float32) if weighted else None
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    Y = canary_bf16((T * k, N))
+    w4.w4a16_moe_gemm(up_bits(Xb), Wq, S, s, e, n, T, k, B, div,
+                      topk_weights=None if tw is None else up(tw), out=Y)
+    y = down_bits(Y)
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, div, T * k, tw)
+    assert sorted(ref) == [f for f in range(T * k) if 0 <= ids.flat[f] < E]
+    assert_rows_close(y, ref, "moe small")
+    untouched = [f for f in range(T * k) if f not in ref]
+    assert np.all(y[untouched] == CANARY)
+
+
+def test_moe_gemm_one_expert_is_dense():
+    """E = 1, k = 1: the grouped product is the dense product of all rows."""
+    T, N, K = 300, 100, 544
+    say("moe_gemm E=1 k=1")
+    Wq, S, ref_w = small_experts(1, N, K, 31)
+    Xb = synth.bits(synth.activations(T, K, 32))
+    ids = np.zeros((T, 1), np.int32)
+    s, e, n = w4.moe_align_block_size(up(ids), 1, 16)
+    y = down_bits(w4.w4a16_moe_gemm(up_bits(Xb), Wq, S, s, e, n, T, 1, 16, 1))
+    Wq_r, S_r = ref_w(0)
+    ok, a, r = gemm.within_tolerance(y, gemm.w4a16_gemm(Xb, Wq_r, S_r), ATOL, RTOL)
+    assert ok, (a, r)
+
+
+# --------------------------------------------------- full-size MoE layers --
+
+class Experts:
+    """Full-size stacked experts quantized on the GPU from GPU-drawn sources,
+    plus the oracle's own quantization of any expert on request."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        H, I, E, seed = wl["H"], wl["I"], wl["E"], wl["seed"]
+        dev = torch.device("cuda")
+        self.gate_up = wmoe.quantize_experts(
+            E, 2 * I, H, lambda e: synth.expert_gate_up(e, I, H, seed, dev), dev)
+        self.down = wmoe.quantize_experts(
+            E, H, I, lambda e: synth.expert_down(e, I, H, seed, dev), dev)
+        self._ref = {}
+
+    def ref(self, kind, e):
+        key = (kind, e)
+        if key not in self._ref:
+            H, I, seed = self.wl["H"], self.wl["I"], self.wl["seed"]
+            draw = synth.expert_gate_up if kind == "gate_up" else synth.expert_down
+            src = synth.bits(draw(e, I, H, seed, torch.device("cuda")))
+            Wq, S = quant.quantize_pack(src)
+            stacked = self.gate_up if kind == "gate_up" else self.down
+            np.testing.assert_array_equal(down(stacked.Wq[e]), Wq)
+            np.testing.assert_array_equal(down_bits(stacked.S[e]), S)
+            self._ref[key] = (Wq, S)
+        return self._ref[key]
+
+
+def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
+    wl = synth.WORKLOADS[name]
+    T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
+    say(f"moe layer {name}: drawing and quantizing {E} experts")
+    ex = Experts(wl)
+    lg = synth.router_logits(T, E, seed, wl["skew"]).numpy()
+    ids, tw = omoe.route(lg, k)
+    Xb = synth.bits(synth.activations(T, H, seed))
+    X = up_bits(Xb)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    rng = np.random.default_rng(seed)
+    busiest, idlest = int(np.argmax(counts)), int(np.argmin(counts))
+    pool = [e for e in range(E) if e not in (busiest, idlest)]
+    extra = list(rng.choice(pool, max(0, n_gate_up_experts - 2), replace=False))
+    gu_experts = {busiest, idlest, *map(int, extra)}
+    for B in B_list:
+        say(f"moe layer {name}: B={B}")
+        s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+        out, buf = wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B)
+        np.testing.assert_array_equal(down(buf.sorted_token_ids), s_ref)
+        np.testing.assert_array_equal(down(buf.expert_ids), e_ref)
+        assert int(down(buf.ntpp)[0]) == n_ref
+        h1 = down_bits(buf.H1)
+        ref = omoe.grouped_gemm(Xb, lambda e: ex.ref("gate_up", e), s_ref, e_ref, n_ref, B, k,
+                                T * k, experts=gu_experts)
+        assert_rows_close(h1, ref, f"{name} gate_up B={B}")
+    # down projection on its own, on seeded activations
+    say(f"moe layer {name}: down projection")
+    B = B_list[0]
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    Ab = synth.bits(synth.activations(T * k, I, seed, stream=77))
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    h2 = down_bits(w4.w4a16_moe_gemm(up_bits(Ab), ex.down.Wq, ex.down.S, s, e, n, T, k, B, 1))
+    dn_experts = set(sorted(gu_experts)[:n_down_experts]) | {busiest}
+    ref = omoe.grouped_gemm(Ab, lambda e: ex.ref("down", e), s_ref, e_ref, n_ref, B, 1, T * k,
+                            experts=dn_experts)
+    assert_rows_close(h2, ref, f"{name} down")
+    # the whole layer on sampled tokens
+    say(f"moe layer {name}: sampled tokens")
+    out, _ = wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B_list[0])
+    o = down_bits(out)
+    toks = sorted({0, T - 1, *map(int, rng.choice(T, max(0, n_tokens - 2), replace=False))})
+    ref = omoe.moe_layer(Xb, ids, tw, lambda e: ex.ref("gate_up", e),
+                         lambda e: ex.ref("down", e), tokens=toks)
+    assert_rows_close(o, ref, f"{name} layer output")
+
+
+def test_moe_qwen_layer():
+    run_layer("moe_qwen", [16, 32, 64], 5, 3, 3)
+
+
+def test_moe_kimi_layer():
+    run_layer("moe_kimi", [64], 3, 2, 2)

@@ -1,0 +1,89 @@
+"""GPU parity: w4_quantize_pack and w4_fake_quant against the oracle.
+
+Bit-exact on every byte: the packed codes, the bf16 scales and the
+fake-quantized weights, on the small dense workload, on the full decode and
+prefill weight shapes, on ragged shapes and on hand-built groups that hit
+exact rounding ties, zero groups, subnormal magnitudes and extreme values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_amd as w4
+import synth
+from gpu_util import down, down_bits, say, up_bits
+from oracle import bf16, quant
+
+pytestmark = pytest.mark.gpu
+
+
+def check_quantize(Wbits, label):
+    say(f"quantize_pack {label} shape={Wbits.shape}")
+    Wq_ref, S_ref = quant.quantize_pack(Wbits)
+    W = up_bits(Wbits)
+    Wq, S = w4.w4_quantize_pack(W)
+    np.testing.assert_array_equal(down(Wq), Wq_ref)
+    np.testing.assert_array_equal(down_bits(S), S_ref)
+    say(f"fake_quant {label}")
+    ref = quant.fake_quant(Wbits)
+    np.testing.assert_array_equal(down_bits(w4.w4_fake_quant(W)), ref)
+    # in place
+    W2 = W.clone()
+    w4.w4_fake_quant(W2, out=W2)
+    np.testing.assert_array_equal(down_bits(W2), ref)
+
+
+def test_dense_small_seed0():
+    wl = synth.WORKLOADS["dense_small"]
+    check_quantize(synth.bits(synth.weights(wl["N"], wl["K"], wl["seed"])), "512x512")
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (7, 160), (129, 64), (2, 4096), (5, 32 * 37)])
+def test_ragged_shapes(N, K):
+    check_quantize(synth.bits(synth.weights(N, K, 11 + N + K)), f"{N}x{K}")
+
+
+def special_groups():
+    """Rows of hand-built 32-element groups (bf16 bits), K = 32 * groups."""
+    f32 = np.float32
+    groups = []
+    # s = bf16(7/7) = 1: w/s = w, exact half-way points must round to even
+    g = np.array([7, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, -3.5, 4.5, -4.5, 5.5, -5.5, 6.5,
+                  -6.5, 0.25, -0.25, 0.75, 1, 2, 3, 4, 5, 6, -1, -2, -3, -4, -5, -6, -7, 0],
+                 dtype=f32)
+    groups.append(g)
+    groups.append(-g)
+    groups.append(np.zeros(32, f32))                              # zero group: s = 0
+    groups.append(np.full(32, -0.0, f32))
+    tiny = np.float32(1e-39) * np.arange(-16, 16, dtype=f32)      # subnormal magnitudes
+    groups.append(tiny)
+    groups.append(np.full(32, np.float32(9.2e-41)))               # amax/7 underflows bf16
+    big = np.linspace(-3.0e38, 3.0e38, 32, dtype=f32)             # near the top of bf16
+    groups.append(big)
+    one = np.zeros(32, f32)
+    one[17] = -0.015625                                           # single nonzero, negative
+    groups.append(one)
+    rng = np.random.default_rng(5)
+    for scale in (1e-30, 1e-3, 1.0, 1e20):
+        groups.append((rng.standard_normal(32) * scale).astype(f32))
+    row = np.concatenate(groups)
+    bits = bf16.rne(row).reshape(1, -1)
+    return np.concatenate([bits, bits[:, ::-1].copy()], axis=0)
+
+
+def test_special_groups():
+    check_quantize(special_groups(), "special groups")
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_full_size(name):
+    wl = synth.WORKLOADS[name]
+    check_quantize(synth.bits(synth.weights(wl["N"], wl["K"], wl["seed"])), name)
+
+
+def test_empty_is_noop():
+    W = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    Wq, S = w4.w4_quantize_pack(W)
+    assert Wq.numel() == 0 and S.numel() == 0
+    assert w4.w4_fake_quant(W).numel() == 0
