@@ -175,6 +175,19 @@ def bench_quant(w4, synth, torch, iters, timer):
     return out
 
 
+def bench_copy(torch, iters, timer):
+    """A plain device copy of known size (256 MiB read + 256 MiB written):
+    the calibration kernel for the HBM byte counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    f = lambda i: b.copy_(a)
+    timer.run(f, 2)
+    t = timer.run(f, iters) / iters
+    return {"bytes_read": n, "bytes_written": n, "us": round(t * 1e3, 2),
+            "GB/s": round(2 * n / (t * 1e-3) / 1e9, 1)}
+
+
 def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     wl = synth.WORKLOADS[name]
     T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
@@ -303,6 +316,9 @@ def main():
     if "quant" in sections:
         log("bench: quantize_pack / fake_quant")
         detail.update(bench_quant(w4, synth, torch, iters, timer))
+    if "copy" in sections:
+        log("bench: copy calibration")
+        detail["copy"] = bench_copy(torch, iters, timer)
     for name in ("moe_qwen", "moe_kimi"):
         if name in sections:
             log(f"bench: {name}")

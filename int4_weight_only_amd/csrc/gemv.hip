@@ -2,147 +2,357 @@
 //
 // Method: "INT4 QAT end-to-end for RL" §4 (INT4 weights are dequantized in
 // registers and multiplied against BF16 activations on BF16 matrix units);
-// "Quantization basics: from FP32 to INT4" §2.1 (w' = q * s) and the
+// "Quantization basics: from FP32 to INT4" §2.1 (w = q * s, z = 0) and the
 // tutorial's opening remark that decode reads every weight once per token,
 // so this path is bound by HBM bandwidth.
 //
-// Mapping (MI355X): a workgroup owns RT*16 consecutive weight rows n and
-// all of M; its WAVES waves split K into contiguous ranges of 128-element
-// chunks.  In a chunk, lane l = (r = l % 16, kq = l / 16) loads one whole
-// 32-element group (16 bytes: four packed words) of weight row r and its
-// bf16 scale: a 16-row tile is one fully used 1 KB load per chunk.  Word j
-// of every lane feeds MFMA j of the chunk (v_mfma_f32_16x16x32_bf16), so
-// each MFMA contracts a permuted set of 32 k; the activation operand uses
-// the same permutation (lane (m, kq) loads X[m, 32 g + 8 j .. + 7]), which
-// leaves the sum unchanged.  The weight row tile is the A operand, the
-// activation rows the B operand: D[n][m], fp32 accumulation.  Each wave
-// issues the weight loads of CPW chunks before touching them, to keep
-// enough bytes in flight per CU; the activations (at most 32 x K bf16)
-// come from L2.  The per-wave partial sums are combined in LDS in wave
-// order (deterministic), converted to bf16 once, and stored coalesced.
+// Arithmetic.  Within one 32-element group every weight shares the scale
+// s, so   sum_k x_k q_k s = s * sum_k x_k q_k :  the MFMA contracts the
+// integer codes of exactly one group and the fp32 partial is scaled once
+// (4 FMAs per lane per 16 x 32 weights instead of one per weight).  A code
+// becomes a bf16 MFMA operand with one AND-OR: the bit pattern 0x4300 | n
+// is the bf16 number 128 + n, and n = q + 8 after flipping each nibble's
+// top bit (XOR 0x8 per nibble turns two's complement into offset binary).
+// The MFMA therefore sums x * (136 + q); its C operand starts at
+// -136 * sum_k x_k (itself one MFMA of X against the constant -136), so the
+// result is sum_k x_k q_k up to fp32 rounding.  Exact integer inputs stay
+// exact.  The scaled product is q * s exactly, not bf16(q * s): within the
+// fp32-accumulation tolerance of the definition.
+//
+// Mapping (MI355X).  One workgroup of 16 waves per CU; wave w owns a
+// 256-element K slice (two 128-element "chunks") and keeps its slice of X
+// in registers for the whole kernel (loaded once, reused for every weight
+// row).  The workgroup walks TPW tiles of 16 weight rows.  For one chunk,
+// lane (n = l % 16, kq = l / 16) loads 16 bytes = group 4c + kq of row n
+// (a 16-row tile is 16 contiguous 64-byte runs) with a raw buffer load:
+// rows or groups past the end read as zero in hardware, so no load sits
+// behind a branch and all of them are in flight together.  A 4 x 4
+// transpose across the four 16-lane rows (v_permlane32_swap +
+// v_permlane16_swap) then gives lane (n, kq) word kq of all four groups,
+// which is exactly its B operand slot for a one-group MFMA
+// (v_mfma_f32_16x16x32_bf16: A = X rows, B = weight rows).  Per-wave
+// partials meet in LDS (fixed wave order, deterministic) once per tile;
+// each output is owned by one thread across tiles and K passes.
 #include "common.h"
 
 namespace w4 {
 
-template <int MT, int RT, int WAVES, int CPW>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint16_t* __restrict__ X,
-                                                     const uint32_t* __restrict__ Wq,
-                                                     const uint16_t* __restrict__ S,
-                                                     uint16_t* __restrict__ Y, int M, int N,
-                                                     int K) {
-  constexpr int ROWS = RT * 16;
-  constexpr int PAD = 4;
-  __shared__ __attribute__((aligned(16))) float part[WAVES][MT * 16][ROWS + PAD];
+namespace {
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
+constexpr int kWaves = 16;
+constexpr int kCPW = 2;                 // 128-element chunks per wave per pass
+constexpr int kPassK = kWaves * kCPW * 128;
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset past any buffer: reads 0
+constexpr uint32_t kNeg136 = 0xC308C308u;   // bf16 pair (-136, -136)
+constexpr int kNonTemporal = 2;             // buffer-load cache policy: streaming
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 8 bf16 from 16 bytes of X in the slot order the weight operand uses:
+// (x0, x4), (x1, x5), (x2, x6), (x3, x7).
+__device__ __forceinline__ u32x4 x_slots(u32x4 d) {
+  u32x4 o;
+  o.x = (d.x & 0xFFFFu) | (d.z << 16);
+  o.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
+  o.z = (d.y & 0xFFFFu) | (d.w << 16);
+  o.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+  return o;
+}
+
+// One packed word (8 codes, nibble t = element t) -> bf16 operand holding
+// 136 + q in slot order (t0, t4), (t1, t5), (t2, t6), (t3, t7).  Each pair
+// is one v_bitop3: where the mask 0x000F000F is set the result is the
+// nibble XOR 8 (two's complement -> offset binary), elsewhere the bits of
+// 0x43004300 (bf16 128 with a zero mantissa); truth table 0x6A =
+// "mask ? x ^ c : c" with c = 0x43084308.
+__device__ __forceinline__ uint32_t code_pair(uint32_t x) {
+  return __builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x43084308u, 0x6A);
+}
+__device__ __forceinline__ u32x4 code_slots(uint32_t w) {
+  return u32x4{code_pair(w), code_pair(w >> 4), code_pair(w >> 8), code_pair(w >> 12)};
+}
+
+// 4 x 4 transpose across the four 16-lane rows: on entry lane row r holds
+// words 0..3 of group r; on exit it holds word r of groups 0..3.
+__device__ __forceinline__ u32x4 transpose_rows(u32x4 v) {
+  auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return u32x4{c[0], c[1], d[0], d[1]};
+}
+
+// Copies of v with all four 16-lane rows replaced by row 0, 1, 2, 3.
+__device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
+  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // [r0 r1 r0 r1], [r2 r3 r2 r3]
+  auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+}  // namespace
+
+// MT: 16-row activation tiles (M <= 16 * MT).  SALIGNED: K / 32 is a
+// multiple of 8 (a wave's eight scales of one row are one 16-byte load).  PF: weight
+// tiles in flight per wave (a ring of registers; bounded by the register
+// budget of 16 resident waves per CU).  The workgroup covers T tiles of 16
+// weight rows (T <= max_tpw(MT)), about one workgroup per CU.
+constexpr int max_tpw(int MT) { return MT == 1 ? 4 : 3; }   // LDS budget
+
+template <int MT, bool SALIGNED, int T, int PF>
+__global__ __launch_bounds__(kWaves * 64) void k_decode(const uint16_t* __restrict__ X,
+                                                         const uint32_t* __restrict__ Wq,
+                                                         const uint16_t* __restrict__ S,
+                                                         uint16_t* __restrict__ Y, int M,
+                                                         int N, int K) {
+  static_assert(PF >= 1 && PF <= 3 && PF <= T && T <= max_tpw(MT), "tile ring");
+  constexpr int MR = MT * 16;
+  constexpr int PSTR = MR + 4;                     // LDS row stride (floats)
+  // CFOLD: the -136 * sum(x) term is precomputed per group and enters as
+  // the MFMA C operand; otherwise a second MFMA against -136 adds it
+  // (fewer registers, more matrix-core cycles: used for 32 rows).
+  constexpr bool CFOLD = false;
+  constexpr int NC = CFOLD ? kCPW : 1;
+  constexpr int TMAX = T;
+  // per-wave partial sums of every tile: each wave runs through its tiles
+  // on its own (no barrier between tiles) and the sum over waves happens
+  // once per K pass
+  __shared__ __attribute__((aligned(16))) float part[TMAX][kWaves][16][PSTR];
+  __shared__ float ybuf[TMAX][MR * 16];            // partials across K passes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n16 = lane & 15;
   const int kq = lane >> 4;
-  const int n0 = blockIdx.x * ROWS;
-  const int G = K >> 5;                 // groups per row
-  const int C = (G + 3) >> 2;           // 128-element chunks
-  const int kw = K >> 3;                // packed words per row
+  const int G = K >> 5;
+  const int C = (G + 3) >> 2;
+  const uint32_t rowb = (uint32_t)K >> 1;          // packed bytes per weight row
+  const int n0 = blockIdx.x * (T * 16);
+  const int rows = min(T * 16, N - n0);
+  const int ntiles = (rows + 15) >> 4;
 
-  // contiguous chunk range of this wave
-  const int c_lo = (int)(((int64_t)C * wave) / WAVES);
-  const int c_hi = (int)(((int64_t)C * (wave + 1)) / WAVES);
+  const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
 
-  f32x4 acc[RT][MT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int npass = (K + kPassK - 1) / kPassK;
 
-  for (int c0 = c_lo; c0 < c_hi; c0 += CPW) {
-    u32x4 wv[CPW][RT];
-    float sc[CPW][RT];
-    // issue every weight load of this pass first
+  for (int pass = 0; pass < npass; ++pass) {
+    // ---- activation slice of this wave: operands and the offset term
+    u32x4 xop[kCPW][4][MT];
+    f32x4 cst[NC][4][MT];
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int g = 4 * (c0 + cc) + kq;
-      const bool gv = (c0 + cc < c_hi) && (g < G);
+    for (int cc = 0; cc < kCPW; ++cc) {
+      const int c = pass * (kWaves * kCPW) + wave * kCPW + cc;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int row = n0 + rt * 16 + r16;
-        if (gv && row < N) {
-          wv[cc][rt] = *(const u32x4*)(Wq + (int64_t)row * kw + 4 * g);
-          sc[cc][rt] = bf16f(S[(int64_t)row * G + g]);
-        } else {
-          wv[cc][rt] = u32x4{0u, 0u, 0u, 0u};
-          sc[cc][rt] = 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int g = 4 * (c0 + cc) + kq;
-      const bool gv = (c0 + cc < c_hi) && (g < G);
-      u32x4 xv[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + r16;
-        if (gv && m < M) {
-          const u32x4* xp = (const u32x4*)(X + (int64_t)m * K + 32 * g);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[mt][j] = xp[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[mt][j] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float s = sc[cc][rt];
-        const float m8s = -8.0f * s;
-        const u32x4 w = wv[cc][rt];
-        const u32x4 a0 = dequant8(w.x, s, m8s);
-        const u32x4 a1 = dequant8(w.y, s, m8s);
-        const u32x4 a2 = dequant8(w.z, s, m8s);
-        const u32x4 a3 = dequant8(w.w, s, m8s);
+      for (int j = 0; j < 4; ++j) {
+        const int g = 4 * c + j;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[rt][mt] = mfma16(a0, xv[mt][0], acc[rt][mt]);
-          acc[rt][mt] = mfma16(a1, xv[mt][1], acc[rt][mt]);
-          acc[rt][mt] = mfma16(a2, xv[mt][2], acc[rt][mt]);
-          acc[rt][mt] = mfma16(a3, xv[mt][3], acc[rt][mt]);
+          const int m = mt * 16 + n16;
+          const uint32_t off = (g < G && m < M)
+                                   ? ((uint32_t)m * (uint32_t)K + 32u * g + 8u * kq) * 2u
+                                   : kOOB;
+          xop[cc][j][mt] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
         }
       }
     }
-  }
+    const u32x4 neg136 = u32x4{kNeg136, kNeg136, kNeg136, kNeg136};
 
-  // lane holds D[4*kq + i][r16] of each (rt, mt) tile: weight row
-  // rt*16 + 4*kq + i, activation row mt*16 + r16
+    // ---- scales: one load per wave and pass.  Lane row r (lanes 16r ..
+    // 16r + 15) fetches the wave's eight group scales of row n16 of tile r
+    // (16 bytes); every tile's row is then broadcast to all four lane rows.
+    // Rows past the end read as zero; a group block past K is clamped into
+    // the row (its codes and activations are zero, so the scale is unused).
+    const int g0 = pass * (kWaves * kCPW * 4) + wave * (kCPW * 4);
+    uint32_t sc_t[4][4];                               // [tile][dword]: 8 bf16 scales
+    {
+      const uint32_t srow = (uint32_t)(kq * 16 + n16);
+      u32x4 raw;
+      if constexpr (SALIGNED) {
+        const uint32_t gb = (uint32_t)min(g0, G - 8);
+        raw = __builtin_amdgcn_raw_buffer_load_b128(sr, (srow * (uint32_t)G + gb) * 2u, 0, 0);
+      } else {
+        uint32_t h[8];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+        for (int j = 0; j < 8; ++j) {
+          const int gj = g0 + j;
+          const uint32_t soff = (gj < G) ? (srow * (uint32_t)G + gj) * 2u : kOOB;
+          h[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+        }
+        raw = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                    h[6] | (h[7] << 16)};
+      }
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *(f32x4*)&part[wave][mt * 16 + r16][rt * 16 + 4 * kq] = acc[rt][mt];
-  __syncthreads();
+      for (int d = 0; d < 4; ++d) {
+        uint32_t b[4];
+        broadcast_rows(rw[d], b);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc_t[t][d] = b[t];
+      }
+    }
 
-  constexpr int OUT = MT * 16 * ROWS;
-  for (int idx = threadIdx.x; idx < OUT; idx += WAVES * 64) {
-    const int m = idx / ROWS;
-    const int n = idx - m * ROWS;
-    float sum = 0.0f;
+    // ---- weight ring.  Rows of a tile past the end lie beyond the
+    // buffer's size and read as zero, so loads are never conditional (a
+    // condition that is the same for the whole wave would be compiled into
+    // a branch around the load, and a wait inside it); the only guards are
+    // per-lane selects.  Codes are read once: non-temporal loads.
+    u32x4 wv[PF][kCPW];
+    auto load_tile = [&](int slot, int t) {
+      const uint32_t nl = (uint32_t)(t * 16 + n16);          // row within the workgroup
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += part[w][m][n];
-    if (m < M && n0 + n < N) Y[(int64_t)m * N + n0 + n] = to_bf16(sum);
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const int c = pass * (kWaves * kCPW) + wave * kCPW + cc;
+        const int g = 4 * c + kq;
+        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
+        wv[slot][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, kNonTemporal);
+      }
+    };
+
+    // one tile: one-group MFMAs, scale, cross-wave sum, result
+    auto compute_tile = [&](int slot, int t) {
+      f32x4 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const u32x4 u = transpose_rows(wv[slot][cc]);
+        const uint32_t words[4] = {u.x, u.y, u.z, u.w};
+        const uint32_t s01 = sc_t[t][2 * cc], s23 = sc_t[t][2 * cc + 1];
+        const float sc[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 b = code_slots(words[j]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4 d;
+            if constexpr (CFOLD) {
+              d = mfma16(xop[cc][j][mt], b, cst[cc][j][mt]);
+            } else {
+              d = mfma16(xop[cc][j][mt], b, f32x4{0.f, 0.f, 0.f, 0.f});
+              d = mfma16(xop[cc][j][mt], neg136, d);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(d[r], sc[j], acc[mt][r]);
+          }
+        }
+      }
+      // lane holds D[m = mt*16 + 4 kq + r][n = n16]
+      float* pp = &part[t][wave][n16][0];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) *(f32x4*)(pp + mt * 16 + 4 * kq) = acc[mt];
+    };
+
+    // called once the weight prologue is in flight: wait for X, put it in
+    // slot order (and precompute the offset term when folded)
+    auto convert_x = [&]() {
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            xop[cc][j][mt] = x_slots(xop[cc][j][mt]);
+            if constexpr (CFOLD)
+              cst[cc][j][mt] = mfma16(xop[cc][j][mt], neg136, f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+    };
+
+    // tiles are unrolled at compile time (TMAX <= 4); a tile past the end
+    // costs its (out-of-range, traffic-free) loads and skips its compute
+#pragma unroll
+    for (int t = 0; t < PF - 1; ++t) load_tile(t, t);
+    if constexpr (PF == 1) load_tile(0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads above ahead of the X wait
+    convert_x();
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if constexpr (PF > 1) {
+        if (t + PF - 1 < TMAX) load_tile((t + PF - 1) % PF, t + PF - 1);
+      }
+      if (t < ntiles) compute_tile(t % PF, t);
+      if constexpr (PF == 1) {
+        if (t + 1 < TMAX) load_tile(0, t + 1);
+      }
+    }
+
+    // ---- sum over waves in wave order (deterministic); one thread per output
+    __syncthreads();
+    for (int o = tid; o < ntiles * MR * 16; o += kWaves * 64) {
+      const int t = o / (MR * 16);
+      const int m = (o >> 4) % MR;
+      const int n = o & 15;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += part[t][w][n][m];
+      const int row = t * 16 + n;
+      if (npass > 1) {
+        sum += (pass == 0) ? 0.0f : ybuf[t][m * 16 + n];
+        ybuf[t][m * 16 + n] = sum;
+      }
+      if (pass == npass - 1 && m < M && row < rows) Y[(size_t)m * N + n0 + row] = to_bf16(sum);
+    }
+    if (npass > 1) __syncthreads();   // part is rewritten by the next pass
   }
 }
 
-template <int MT, int RT, int WAVES, int CPW>
-static hipError_t run_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                           int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const int64_t blocks = (N + RT * 16 - 1) / (RT * 16);
-  hipLaunchKernelGGL((k_gemv<MT, RT, WAVES, CPW>), dim3((unsigned)blocks), dim3(WAVES * 64), 0,
-                     st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K);
+namespace {
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int MT, bool SA, int T>
+hipError_t run_decode_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  constexpr int PFMAX = MT == 1 ? (SA ? 3 : 2) : 1;
+  constexpr int PF = T < PFMAX ? T : PFMAX;
+  const int64_t blocks = (N + T * 16 - 1) / (T * 16);
+  hipLaunchKernelGGL((k_decode<MT, SA, T, PF>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
+                     X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
+template <int MT, bool SA>
+hipError_t run_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
+                      int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t cus = cu_count();
+  const int64_t tpw = (tiles + cus - 1) / cus;
+  if (tpw <= 1) return run_decode_t<MT, SA, 1>(X, Wq, S, Y, M, N, K, st);
+  if (tpw == 2) return run_decode_t<MT, SA, 2>(X, Wq, S, Y, M, N, K, st);
+  if (tpw == 3 || MT == 2) return run_decode_t<MT, SA, 3>(X, Wq, S, Y, M, N, K, st);
+  return run_decode_t<MT, SA, max_tpw(MT)>(X, Wq, S, Y, M, N, K, st);
+}
+
+}  // namespace
+
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M <= 16) return run_gemv<1, 2, 8, 4>(X, Wq, S, Y, M, N, K, st);
-  return run_gemv<2, 2, 8, 4>(X, Wq, S, Y, M, N, K, st);
+  const bool sa = ((K >> 5) & 7) == 0;
+  if (M <= 16)
+    return sa ? run_decode<1, true>(X, Wq, S, Y, M, N, K, st)
+              : run_decode<1, false>(X, Wq, S, Y, M, N, K, st);
+  return sa ? run_decode<2, true>(X, Wq, S, Y, M, N, K, st)
+            : run_decode<2, false>(X, Wq, S, Y, M, N, K, st);
 }
 
 }  // namespace w4
