@@ -27,11 +27,12 @@ namespace {
 
 constexpr int kStepK = 64;            // K per pipeline step (two groups)
 constexpr int kRowPad = kStepK + 8;   // LDS row length in bf16 (144 bytes)
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset past any buffer: reads 0
 
-struct DenseRows {
-  int M;
-  __device__ int x_row(int r) const { return r < M ? r : -1; }
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
 }  // namespace
 
@@ -40,7 +41,7 @@ struct DenseRows {
 // row r of the run is pair f = sorted_ids[row0 + r] (valid if f < n_pairs),
 // activation row f / x_row_div, output row f.
 template <int BM, int WN, int NW, bool MOE>
-__global__ __launch_bounds__(NW * 64) void k_gemm(
+__global__ __launch_bounds__(NW * 64, 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
@@ -111,6 +112,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
   const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
+  // raw buffer views: lanes whose offset lies past the end read zero, so
+  // no load needs a branch (a branch around a load makes the compiler wait
+  // for it inside the branch, serialising the loads)
+  const int x_rows = MOE ? n_pairs / x_row_div : M;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
 
   for (int pass0 = 0; pass0 < rows_total; pass0 += BM) {
     const int rows = min(BM, rows_total - pass0);
@@ -148,11 +156,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
         const int piece = tid + p * NT;
         const int r = piece >> 3;
         const int col = (piece & 7) * 8 + step * kStepK;
-        const int xr = xrow[r];
-        if (xr >= 0 && col < K)
-          xstage[p] = *(const u32x4*)(X + (int64_t)xr * K + col);
-        else
-          xstage[p] = u32x4{0u, 0u, 0u, 0u};
+        const int xr_ = xrow[r];
+        const uint32_t off =
+            (xr_ >= 0 && col < K) ? ((uint32_t)xr_ * (uint32_t)K + (uint32_t)col) * 2u : kOOB;
+        xstage[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
       }
     };
     auto store_x = [&](int buf) {
@@ -164,19 +171,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
       }
     };
     u32x4 wreg[NS];
-    float sreg[NS];
+    uint32_t sreg[NS];             // bf16 scale of this lane's group (low half)
     auto load_w = [&](int step) {
       const int g = 2 * step + h;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
-        const int n = n_base + ns * 32 + l32;
-        if (n < N && g < G) {
-          wreg[ns] = *(const u32x4*)(Wbase + (int64_t)n * kw + 4 * g);
-          sreg[ns] = bf16f(Sbase[(int64_t)n * G + g]);
-        } else {
-          wreg[ns] = u32x4{0u, 0u, 0u, 0u};
-          sreg[ns] = 0.0f;
-        }
+        const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
+        // rows past N lie past the buffer's end; a group past K reads zero
+        const uint32_t woff = (g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
+        wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+        const uint32_t soff = (g < G) ? (n * (uint32_t)G + (uint32_t)g) * 2u : kOOB;
+        sreg[ns] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
       }
     };
 
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(
       u32x4 bop[NS][4];
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
-        const float s = sreg[ns];
+        const float s = bf16_lo(sreg[ns]);
         const float m8s = -8.0f * s;
         bop[ns][0] = dequant8(wreg[ns].x, s, m8s);
         bop[ns][1] = dequant8(wreg[ns].y, s, m8s);
