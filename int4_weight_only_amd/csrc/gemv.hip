@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode(const uint16_t* __restri
     // Rows past the end read as zero; a group block past K is clamped into
     // the row (its codes and activations are zero, so the scale is unused).
     const int g0 = pass * (kWaves * kCPW * 4) + wave * (kCPW * 4);
-    uint32_t sc_t[4][4];                               // [tile][dword]: 8 bf16 scales
+    u32x4 sraw;                                        // this lane row's 8 scales
     {
       const uint32_t srow = (uint32_t)(kq * 16 + n16);
       u32x4 raw;
@@ -190,14 +190,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode(const uint16_t* __restri
         raw = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                     h[6] | (h[7] << 16)};
       }
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t b[4];
-        broadcast_rows(rw[d], b);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sc_t[t][d] = b[t];
-      }
+      sraw = raw;
     }
 
     // ---- weight ring.  Rows of a tile past the end lie beyond the
@@ -222,11 +215,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode(const uint16_t* __restri
       f32x4 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // tile t's scales, broadcast from lane row t (kept per tile: registers)
+      uint32_t sct[4];
+      {
+        const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t b[4];
+          broadcast_rows(rw[d], b);
+          sct[d] = b[t];
+        }
+      }
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) {
         const u32x4 u = transpose_rows(wv[slot][cc]);
         const uint32_t words[4] = {u.x, u.y, u.z, u.w};
-        const uint32_t s01 = sc_t[t][2 * cc], s23 = sc_t[t][2 * cc + 1];
+        const uint32_t s01 = sct[2 * cc], s23 = sct[2 * cc + 1];
         const float sc[4] = {bf16_lo(s01), bf16_hi(s01), bf16_lo(s23), bf16_hi(s23)};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -304,6 +308,176 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode(const uint16_t* __restri
   }
 }
 
+
+// M <= 16, group-outer.  All T tiles' codes of the wave's two chunks are in
+// registers at once, so for each group the offset term (X against -136) is
+// one MFMA whose result is the C operand of the T tile MFMAs: one MFMA per
+// group and tile.  RM: rows of each lane's D fragment that are accumulated
+// (for M = 1 only row 0 of lane row 0 exists; the other rows are skipped).
+template <bool SALIGNED, int T, int RM>
+__global__ __launch_bounds__(kWaves * 64) void k_decode1(const uint16_t* __restrict__ X,
+                                                          const uint32_t* __restrict__ Wq,
+                                                          const uint16_t* __restrict__ S,
+                                                          uint16_t* __restrict__ Y, int M, int N,
+                                                          int K) {
+  static_assert(T >= 1 && T <= 4 && (RM == 1 || RM == 4), "decode shape");
+  constexpr int PSTR = 20;                         // LDS row stride (floats)
+  constexpr int WSTR = 16 * PSTR + 4;              // per-wave block: padded off the bank period
+  __shared__ __attribute__((aligned(16))) float part[T][kWaves][WSTR];
+  __shared__ float ybuf[T][256];                   // partials across K passes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n16 = lane & 15;
+  const int kq = lane >> 4;
+  const int G = K >> 5;
+  const uint32_t rowb = (uint32_t)K >> 1;          // packed bytes per weight row
+  const int n0 = blockIdx.x * (T * 16);
+  const int rows = min(T * 16, N - n0);
+  const int ntiles = (rows + 15) >> 4;
+
+  const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
+  const int npass = (K + kPassK - 1) / kPassK;
+  const u32x4 neg136 = u32x4{kNeg136, kNeg136, kNeg136, kNeg136};
+
+  for (int pass = 0; pass < npass; ++pass) {
+    const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
+    // ---- activations (issued first: the first wait is for them alone)
+    u32x4 xop[kCPW][4];
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int g = 4 * (c0 + cc) + j;
+        const uint32_t off = (g < G && n16 < M)
+                                 ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u
+                                 : kOOB;
+        xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+      }
+    // ---- scales: lane row r fetches the wave's 8 group scales of row n16
+    // of tile r (rows past the end read zero; a group block past K is
+    // clamped into the row, where codes and activations are zero)
+    const int g0 = 4 * c0;
+    u32x4 sraw;
+    {
+      const uint32_t srow = (uint32_t)(kq * 16 + n16);
+      if constexpr (SALIGNED) {
+        const uint32_t gb = (uint32_t)min(g0, G - 8);
+        sraw = __builtin_amdgcn_raw_buffer_load_b128(sr, (srow * (uint32_t)G + gb) * 2u, 0, 0);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int gj = g0 + j;
+          const uint32_t soff = (gj < G) ? (srow * (uint32_t)G + gj) * 2u : kOOB;
+          h[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+        }
+        sraw = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16)};
+      }
+    }
+    // ---- codes of every tile (rows past the end read zero); a row's two
+    // chunks are adjacent requests (one 128-byte line)
+    u32x4 wv[T][kCPW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint32_t nl = (uint32_t)(t * 16 + n16);
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const int g = 4 * (c0 + cc) + kq;
+        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, kNonTemporal);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
+
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xop[cc][j] = x_slots(xop[cc][j]);
+    uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
+    {
+      const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t b[4];
+        broadcast_rows(rw[d], b);
+#pragma unroll
+        for (int t = 0; t < T; ++t) sct[t][d] = b[t];
+      }
+    }
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc) {
+      u32x4 u[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) u[t] = transpose_rows(wv[t][cc]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 cst = mfma16(xop[cc][j], neg136, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t word = j == 0 ? u[t].x : j == 1 ? u[t].y : j == 2 ? u[t].z : u[t].w;
+          const f32x4 d = mfma16(xop[cc][j], code_slots(word), cst);
+          const uint32_t sp = sct[t][2 * cc + (j >> 1)];
+          const float sc = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
+#pragma unroll
+          for (int r = 0; r < RM; ++r) acc[t][r] = __builtin_fmaf(d[r], sc, acc[t][r]);
+        }
+      }
+    }
+    // lane holds D[m = 4 kq + r][n = n16] of every tile
+#pragma unroll
+    for (int t = 0; t < T; ++t) *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc[t];
+
+    // ---- sum over waves in a fixed order (deterministic), rows m < M only.
+    // Few outputs (small M): four lanes share one, lane q adding waves
+    // 4q .. 4q+3, then two quad exchanges.  Otherwise one thread per output.
+    __syncthreads();
+    const int mrows = min(M, 16);
+    const int nout = ntiles * mrows * 16;
+    auto emit = [&](int o, float sum) {
+      const int t = o / (mrows * 16);
+      const int m = (o >> 4) % mrows;
+      const int n = o & 15;
+      const int row = t * 16 + n;
+      if (npass > 1) {
+        sum += (pass == 0) ? 0.0f : ybuf[t][m * 16 + n];
+        ybuf[t][m * 16 + n] = sum;
+      }
+      if (pass == npass - 1 && row < rows) Y[(size_t)m * N + n0 + row] = to_bf16(sum);
+    };
+    auto elem = [&](int o) { return ((o & 15) * PSTR) + (o >> 4) % mrows; };
+    if (nout * 4 <= kWaves * 64) {
+      const int o = min(tid >> 2, nout - 1);
+      const int q = tid & 3;
+      const int t = o / (mrows * 16);
+      const int e = elem(o);
+      float sum = part[t][4 * q][e] + part[t][4 * q + 1][e] + part[t][4 * q + 2][e] +
+                  part[t][4 * q + 3][e];
+      sum += __uint_as_float(quad_xor1(__float_as_uint(sum)));
+      sum += __uint_as_float(quad_xor2(__float_as_uint(sum)));
+      if (q == 0 && (tid >> 2) < nout) emit(o, sum);
+    } else {
+      for (int o = tid; o < nout; o += kWaves * 64) {
+        const int t = o / (mrows * 16);
+        const int e = elem(o);
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += part[t][w][e];
+        emit(o, sum);
+      }
+    }
+    if (npass > 1) __syncthreads();   // part is rewritten by the next pass
+  }
+}
+
 namespace {
 
 int cu_count() {
@@ -331,6 +505,27 @@ hipError_t run_decode_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
   return hipGetLastError();
 }
 
+template <bool SA, int T, int RM>
+hipError_t run_decode1_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
+                         int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t blocks = (N + T * 16 - 1) / (T * 16);
+  hipLaunchKernelGGL((k_decode1<SA, T, RM>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, X,
+                     (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+template <bool SA, int RM>
+hipError_t run_decode1(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
+                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t cus = cu_count();
+  const int64_t tpw = (tiles + cus - 1) / cus;
+  if (tpw <= 1) return run_decode1_t<SA, 1, RM>(X, Wq, S, Y, M, N, K, st);
+  if (tpw == 2) return run_decode1_t<SA, 2, RM>(X, Wq, S, Y, M, N, K, st);
+  if (tpw == 3) return run_decode1_t<SA, 3, RM>(X, Wq, S, Y, M, N, K, st);
+  return run_decode1_t<SA, 4, RM>(X, Wq, S, Y, M, N, K, st);
+}
+
 template <int MT, bool SA>
 hipError_t run_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
@@ -348,9 +543,12 @@ hipError_t run_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S, u
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const bool sa = ((K >> 5) & 7) == 0;
+  if (M == 1)
+    return sa ? run_decode1<true, 1>(X, Wq, S, Y, M, N, K, st)
+              : run_decode1<false, 1>(X, Wq, S, Y, M, N, K, st);
   if (M <= 16)
-    return sa ? run_decode<1, true>(X, Wq, S, Y, M, N, K, st)
-              : run_decode<1, false>(X, Wq, S, Y, M, N, K, st);
+    return sa ? run_decode1<true, 4>(X, Wq, S, Y, M, N, K, st)
+              : run_decode1<false, 4>(X, Wq, S, Y, M, N, K, st);
   return sa ? run_decode<2, true>(X, Wq, S, Y, M, N, K, st)
             : run_decode<2, false>(X, Wq, S, Y, M, N, K, st);
 }
