@@ -82,7 +82,7 @@ int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t
   // decode kernel: 32-bit buffer offsets cover M * K * 2 <= 2^31 bytes of X
   if (M <= 32 && K <= ((int64_t)1 << 24))
     return hip_status(w4::launch_gemv(X, Wq, S, Y, M, N, K, as_stream(stream)));
-  if ((M + 255) / 256 > 65535) return W4_ERR_UNSUPPORTED;
+  if (((M + 127) / 128) * ((N + 255) / 256) >= ((int64_t)1 << 31) - 8) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_gemm(X, Wq, S, Y, M, N, K, as_stream(stream)));
 }
 

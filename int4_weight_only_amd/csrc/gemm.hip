@@ -12,13 +12,23 @@
 // rows, so every weight is loaded from HBM and dequantized exactly once
 // per workgroup, straight into the MFMA B operand (no LDS round trip),
 // and the VALU cost of dequantization (about 3 ops per weight) is spread
-// over BM rows of MFMA work.  Activations are staged through LDS, double
-// buffered, rows padded to 144 bytes so 16-byte reads of eight
-// consecutive rows hit distinct banks.  K advances 64 per step: lane
-// (n = l % 32, h = l / 32) loads the whole 32-element group 2c + h of
-// weight row n (16 bytes, one scale) and word j of it feeds MFMA j
+// over BM rows of MFMA work.  K advances 64 per step: lane (n = l % 32,
+// h = l / 32) loads the whole 32-element group 2c + h of weight row n (16
+// bytes, one scale) and word j of it feeds MFMA j
 // (v_mfma_f32_32x32x16_bf16); the activation operand is read with the
 // same K permutation, which leaves the sum unchanged.
+//
+// Pipeline: activations go straight from HBM into LDS (16-byte
+// buffer_load ... lds, three stages, no staging registers); codes and
+// scales go to registers two steps ahead (two register sets, the K loop
+// unrolled by two).  In LDS a 64-element activation row is 128 bytes; its
+// eight 16-byte pieces are stored XOR-swizzled by (row / 2) % 8 so that
+// the MFMA operand reads of 32 consecutive rows spread over the banks.
+// Every load is a raw buffer load whose out-of-range lanes read zero
+// (rows past the end, K past the end, the padding step of an odd step
+// count), so no load is conditional.
+#include <type_traits>
+
 #include "common.h"
 
 namespace w4 {
@@ -26,7 +36,6 @@ namespace w4 {
 namespace {
 
 constexpr int kStepK = 64;            // K per pipeline step (two groups)
-constexpr int kRowPad = kStepK + 8;   // LDS row length in bf16 (144 bytes)
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past any buffer: reads 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -41,7 +50,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // row r of the run is pair f = sorted_ids[row0 + r] (valid if f < n_pairs),
 // activation row f / x_row_div, output row f.
 template <int BM, int WN, int NW, bool MOE>
-__global__ __launch_bounds__(NW * 64, 2) void k_gemm(
+__global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
@@ -49,11 +58,17 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
   constexpr int NT = NW * 64;
   constexpr int MS = BM / 32;          // 32-row MFMA tiles along M
   constexpr int NS = WN / 32;          // 32-col MFMA tiles along N per wave
-  constexpr int PIECES = BM * (kStepK / 8) / NT;   // 16-byte X pieces per thread per step
-  static_assert(BM % 32 == 0 && WN % 32 == 0, "tile shape");
-  static_assert((BM * (kStepK / 8)) % NT == 0, "X staging must divide evenly");
+  constexpr int XI = BM / 8;           // 1 KB direct-to-LDS loads per activation stage
+  constexpr int XPW = XI / NW;         // ... issued by each wave
+  constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage (three stages)
+  static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][kRowPad];
+  // three separately declared stages: each DMA target and each operand
+  // read names one object, so the compiler can tell that reading stage s
+  // does not wait on the DMA still filling stage s + 2
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
   __shared__ int xrow[BM];     // activation row of each tile row (-1: none)
   __shared__ int orow[BM];     // output row of each tile row (-1: none)
   __shared__ int run_info[4];
@@ -63,7 +78,32 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int n_base = blockIdx.x * (NW * WN) + wave * WN;
+  // Tile of this workgroup.  MoE: (blockIdx.x = weight-row tile,
+  // blockIdx.y = alignment block).  Dense: a 1-D grid; workgroups are
+  // dispatched round-robin over the 8 XCDs (each with its own L2), so XCD x
+  // takes the contiguous tile range [x * per, (x + 1) * per), walked in
+  // groups of GM activation row-blocks: the workgroups running together on
+  // one XCD share activation rows and weight rows in that XCD's L2.
+  int tile_n, tile_m;
+  if constexpr (MOE) {
+    tile_n = blockIdx.x;
+    tile_m = 0;
+  } else {
+    constexpr int kXcds = 8, GM = 8;
+    const int mt = (M + BM - 1) / BM, nt = (N + NW * WN - 1) / (NW * WN);
+    const int tiles = mt * nt;
+    const int per = (tiles + kXcds - 1) / kXcds;
+    const int pid = blockIdx.x;
+    const int t = (pid % kXcds) * per + pid / kXcds;
+    if (t >= tiles) return;
+    const int group = t / (GM * nt);
+    const int first_m = group * GM;
+    const int gm = min(GM, mt - first_m);
+    const int in_group = t - group * (GM * nt);
+    tile_m = first_m + in_group % gm;
+    tile_n = in_group / gm;
+  }
+  const int n_base = tile_n * (NW * WN) + wave * WN;
   const int G = K >> 5;
   const int kw = K >> 3;
 
@@ -71,34 +111,43 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
   int row0 = 0;                // MoE: first sorted slot of the run
   int expert = 0;
   if constexpr (MOE) {
-    if (tid == 0) {
+    // Find this block's run of one expert with wave 0: expert_ids[0, nblk)
+    // is non-decreasing, so the blocks of expert e are contiguous.  Lanes
+    // read the 64 ids ending at b and the 64 ids starting at b in two
+    // parallel loads; ballots give the distance to the run's first block
+    // (a longer run walks back 64 blocks at a time) and its end.
+    if (wave == 0) {
       const int b = blockIdx.y;
       const int nblk = ntpp[0] / B;
-      int lead = 0, first = 0, last = 0, e = -1;
+      int lead = 0, e = -1, last = 0;
       if (b < nblk) {
         e = expert_ids[b];
-        // expert_ids[0, nblk) is non-decreasing: binary search the run
-        int lo = 0, hi = b;                  // first index with id == e
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (expert_ids[mid] < e) lo = mid + 1; else hi = mid;
+        const int bpw = BM >= B ? BM / B : 1;
+        // backwards: first block of the run
+        int first = b;
+        for (int base = b;; base -= 64) {
+          const int idx = base - lane;                       // lane 0 = base
+          const int id = idx >= 0 ? expert_ids[idx] : -2;
+          const uint64_t same = __ballot(id == e);           // contiguous from lane 0
+          const int run = __popcll(same);
+          first = base - run + 1;
+          if (run < 64 || base - 64 < 0) break;
         }
-        first = lo;
-        lo = b; hi = nblk;                   // first index with id > e
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (expert_ids[mid] <= e) lo = mid + 1; else hi = mid;
-        }
-        const int blocks_per_wg = BM >= B ? BM / B : 1;
-        if (e >= 0 && e < E && ((b - first) % blocks_per_wg) == 0) {
+        // forwards: end of the run, capped at bpw blocks from b
+        const int fidx = b + lane;
+        const int fid = (fidx < nblk && lane < bpw) ? expert_ids[fidx] : -2;
+        const int fwd = __popcll(__ballot(fid == e));      // blocks of the run in [b, b + bpw)
+        if (e >= 0 && e < E && ((b - first) % bpw) == 0) {
           lead = 1;
-          last = min(lo, b + blocks_per_wg);
+          last = b + fwd;
         }
       }
-      run_info[0] = lead;
-      run_info[1] = e;
-      run_info[2] = b * B;
-      run_info[3] = lead ? (last - b) * B : 0;
+      if (lane == 0) {
+        run_info[0] = lead;
+        run_info[1] = e;
+        run_info[2] = b * B;
+        run_info[3] = lead ? (last - b) * B : 0;
+      }
     }
     __syncthreads();
     if (!run_info[0]) return;
@@ -106,15 +155,13 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
     row0 = run_info[2];
     rows_total = run_info[3];
   } else {
-    rows_total = min(BM, M - (int)blockIdx.y * BM);
+    rows_total = min(BM, M - tile_m * BM);
   }
 
   const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
-  // raw buffer views: lanes whose offset lies past the end read zero, so
-  // no load needs a branch (a branch around a load makes the compiler wait
-  // for it inside the branch, serialising the loads)
+  const int nsteps6 = (nsteps + 5) / 6 * 6;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
@@ -124,55 +171,46 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
     const int rows = min(BM, rows_total - pass0);
     // ---- row tables for this pass
     for (int r = tid; r < BM; r += NT) {
-      int xr = -1, yr = -1;
+      int xr_ = -1, yr = -1;
       if (r < rows) {
         if constexpr (MOE) {
           const int f = sorted_ids[row0 + pass0 + r];
-          if (f < n_pairs) { xr = f / x_row_div; yr = f; }
+          if (f < n_pairs) { xr_ = f / x_row_div; yr = f; }
         } else {
-          const int m = blockIdx.y * BM + pass0 + r;
-          xr = m; yr = m;
+          const int m = tile_m * BM + pass0 + r;
+          xr_ = m; yr = m;
         }
       }
-      xrow[r] = xr;
+      xrow[r] = xr_;
       orow[r] = yr;
     }
     __syncthreads();
     const int ms_valid = (rows + 31) >> 5;
 
-    f32x16 acc[MS][NS];
+    // Direct-to-LDS activation loads.  Instruction i of this wave fills
+    // tile rows 8 (wave*XPW + i) .. +7; lane l writes the 16 bytes at
+    // slot l, i.e. row r = 8 I + l / 8, stored piece l % 8, which holds
+    // global piece (l % 8) ^ ((r / 2) % 8) of that row.
+    uint32_t xoff[XPW];        // byte offset of this lane's piece at step 0 (or OOB)
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
+    for (int i = 0; i < XPW; ++i) {
+      const int r = 8 * (wave * XPW + i) + (lane >> 3);
+      const int pg = (lane & 7) ^ ((r >> 1) & 7);
+      const int xr_ = xrow[r];
+      xoff[i] = xr_ >= 0 ? ((uint32_t)xr_ * (uint32_t)K + 8u * (uint32_t)pg) * 2u : kOOB;
+    }
+    auto load_x = [&](int step, uint16_t* st) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
-
-    // ---- staging helpers
-    u32x4 xstage[PIECES];
-    auto load_x = [&](int step) {
-#pragma unroll
-      for (int p = 0; p < PIECES; ++p) {
-        const int piece = tid + p * NT;
-        const int r = piece >> 3;
-        const int col = (piece & 7) * 8 + step * kStepK;
-        const int xr_ = xrow[r];
-        const uint32_t off =
-            (xr_ >= 0 && col < K) ? ((uint32_t)xr_ * (uint32_t)K + (uint32_t)col) * 2u : kOOB;
-        xstage[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+      for (int i = 0; i < XPW; ++i) {
+        const int col = step * kStepK + 8 * ((lane & 7) ^ (((8 * (wave * XPW + i) + (lane >> 3)) >> 1) & 7));
+        const uint32_t off = (xoff[i] != kOOB && col < K) ? xoff[i] + (uint32_t)step * (kStepK * 2) : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void*)(st + (wave * XPW + i) * 512), 16, off, 0,
+            0, 0);
       }
     };
-    auto store_x = [&](int buf) {
-#pragma unroll
-      for (int p = 0; p < PIECES; ++p) {
-        const int piece = tid + p * NT;
-        const int r = piece >> 3;
-        *(u32x4*)&xs[buf][r][(piece & 7) * 8] = xstage[p];
-      }
-    };
-    u32x4 wreg[NS];
-    uint32_t sreg[NS];             // bf16 scale of this lane's group (low half)
-    auto load_w = [&](int step) {
+    // codes + scales of one step into a register set
+    auto load_w = [&](int step, u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) {
       const int g = 2 * step + h;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
@@ -185,49 +223,87 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
       }
     };
 
-    load_x(0);
-    load_w(0);
-    store_x(0);
-    __syncthreads();
+    f32x16 acc[MS][NS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
 
-    for (int step = 0; step < nsteps; ++step) {
-      const int buf = step & 1;
-      // dequantize this step's weights into B operands
-      u32x4 bop[NS][4];
+    // one step: wait for this step's activations, make them visible, start
+    // the stage two ahead, dequantize, multiply, start the codes two ahead.
+    // Loads issued after this step's activations and before this wait:
+    // this step's codes (2 NS), the next step's activations (XPW) and codes.
+    // one step: wait for this step's activations, make them visible, start
+    // the stage two ahead, dequantize, multiply, start the codes two ahead.
+    // MSE activation tiles are multiplied (rows past the pass read zero).
+    // Per 16-wide K slice j all operand reads are issued first and the
+    // MSE x NS MFMAs that follow are independent (no accumulator chain).
+    auto step_body = [&](auto mse, int step, const uint16_t* st, uint16_t* st_next2,
+                         u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) {
+      constexpr int MSE = decltype(mse)::value;
+      // loads issued after this step's activations: its codes and scales
+      // (2 NS), the next step's activations (XPW) and codes (2 NS)
+      static_assert(XPW + 4 * NS <= 63, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPW + 4 * NS) : "memory");
+      __syncthreads();
+      load_x(step + 2, st_next2);
+      if (step < nsteps) {
+        u32x4 bop[NS][4];
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        const float s = bf16_lo(sreg[ns]);
-        const float m8s = -8.0f * s;
-        bop[ns][0] = dequant8(wreg[ns].x, s, m8s);
-        bop[ns][1] = dequant8(wreg[ns].y, s, m8s);
-        bop[ns][2] = dequant8(wreg[ns].z, s, m8s);
-        bop[ns][3] = dequant8(wreg[ns].w, s, m8s);
-      }
-      const bool more = step + 1 < nsteps;
-      if (more) {
-        load_x(step + 1);
-        load_w(step + 1);
-      }
+        for (int ns = 0; ns < NS; ++ns) {
+          const float sc = bf16_lo(sreg[ns]);
+          const float m8s = -8.0f * sc;
+          bop[ns][0] = dequant8(wreg[ns].x, sc, m8s);
+          bop[ns][1] = dequant8(wreg[ns].y, sc, m8s);
+          bop[ns][2] = dequant8(wreg[ns].z, sc, m8s);
+          bop[ns][3] = dequant8(wreg[ns].w, sc, m8s);
+        }
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        if (ms < ms_valid) {
-          const uint16_t* xp = &xs[buf][ms * 32 + l32][32 * h];
-          const u32x4 a0 = *(const u32x4*)(xp + 0);
-          const u32x4 a1 = *(const u32x4*)(xp + 8);
-          const u32x4 a2 = *(const u32x4*)(xp + 16);
-          const u32x4 a3 = *(const u32x4*)(xp + 24);
+        for (int j = 0; j < 4; ++j) {
+          u32x4 a[MSE];
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) {
-            acc[ms][ns] = mfma32(a0, bop[ns][0], acc[ms][ns]);
-            acc[ms][ns] = mfma32(a1, bop[ns][1], acc[ms][ns]);
-            acc[ms][ns] = mfma32(a2, bop[ns][2], acc[ms][ns]);
-            acc[ms][ns] = mfma32(a3, bop[ns][3], acc[ms][ns]);
+          for (int ms = 0; ms < MSE; ++ms) {
+            const int R = ms * 32 + l32;
+            a[ms] = *(const u32x4*)(st + R * kStepK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
           }
+#pragma unroll
+          for (int ms = 0; ms < MSE; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns][j], acc[ms][ns]);
         }
       }
-      if (more) store_x(buf ^ 1);
-      __syncthreads();
+      load_w(step + 2, wreg, sreg);
+    };
+
+    u32x4 wa[NS], wb[NS];
+    uint32_t sa[NS], sb[NS];
+    load_x(0, xs0);
+    load_w(0, wa, sa);
+    load_x(1, xs1);
+    load_w(1, wb, sb);
+    auto run_steps = [&](auto mse) {
+      for (int step = 0; step < nsteps6; step += 6) {
+        step_body(mse, step + 0, xs0, xs2, wa, sa);
+        step_body(mse, step + 1, xs1, xs0, wb, sb);
+        step_body(mse, step + 2, xs2, xs1, wa, sa);
+        step_body(mse, step + 3, xs0, xs2, wb, sb);
+        step_body(mse, step + 4, xs1, xs0, wa, sa);
+        step_body(mse, step + 5, xs2, xs1, wb, sb);
+      }
+    };
+    if constexpr (MOE) {
+      // expert runs are often one activation tile (<= 32 rows)
+      if (ms_valid == 1)
+        run_steps(std::integral_constant<int, 1>{});
+      else
+        run_steps(std::integral_constant<int, MS>{});
+    } else {
+      run_steps(std::integral_constant<int, MS>{});
     }
+    // drain the loads of the padding steps before LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: lane holds D[8*(v/4) + 4*h + v%4][l32] of each tile
 #pragma unroll
@@ -254,20 +330,22 @@ __global__ __launch_bounds__(NW * 64, 2) void k_gemm(
         }
       }
     }
-    __syncthreads();   // row tables are rewritten by the next pass
+    __syncthreads();   // row tables and LDS stages are rewritten by the next pass
   }
 }
 
 namespace {
-constexpr int kBM = 128;
 constexpr int kWN = 64;
 constexpr int kNW = 4;
+constexpr int kBMDense = 128;   // dense prefill tile rows (two workgroups per CU)
+constexpr int kBMMoe = 128;     // expert blocks are 16..64 rows: a smaller tile pads less
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((k_gemm<kBM, kWN, kNW, false>), grid, dim3(kNW * 64), 0, st, X,
+  const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
+  const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
+  hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false>), grid, dim3(kNW * 64), 0, st, X,
                      (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr,
                      nullptr, 0, 1, 1, 0);
   return hipGetLastError();
@@ -281,7 +359,7 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
   const int64_t n_pairs = T * k;
   const int64_t cap = ((n_pairs + (int64_t)E * (B - 1) + B - 1) / B) * B;
   const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)), (unsigned)(cap / B));
-  hipLaunchKernelGGL((k_gemm<kBM, kWN, kNW, true>), grid, dim3(kNW * 64), 0, st, X,
+  hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true>), grid, dim3(kNW * 64), 0, st, X,
                      (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
                      topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
