@@ -38,36 +38,43 @@ __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uin
 
 // ------------------------------------------------------------- dequant ----
 
-// Byte b of a 32-bit word as fp32 (v_cvt_f32_ubyteN).  Pure VALU op; the
-// asm keeps the compiler from re-deriving each byte with a bitfield extract.
-#define W4_CVT_UBYTE(N)                                                      \
-  __device__ __forceinline__ float ubyte##N(uint32_t x) {                    \
-    float r;                                                                 \
-    asm("v_cvt_f32_ubyte" #N " %0, %1" : "=v"(r) : "v"(x));                  \
-    return r;                                                                \
-  }
-W4_CVT_UBYTE(0)
-W4_CVT_UBYTE(1)
-W4_CVT_UBYTE(2)
-W4_CVT_UBYTE(3)
-#undef W4_CVT_UBYTE
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Per-group constants of dequant8: s, s / 16, -1032 s and -72 s.  Both
+// products are exact in fp32 (an 8-bit-mantissa scale times a constant
+// whose set bits span at most 8 places).
+struct DeqScale {
+  float s, s16, c0, c1;
+};
+__device__ __forceinline__ DeqScale deq_scale(float s) {
+  return {s, s * 0.0625f, -1032.0f * s, -72.0f * s};
+}
 
 // Eight INT4 codes of one packed word -> eight bf16 w' = bf16_rne(q * s),
 // in k order (element j of the word -> bf16 j of the result: word x holds
 // j = 0, 1, word y holds 2, 3, ...).
-//   off = w ^ 0x88888888 turns each two's-complement nibble q into q + 8;
-//   (q + 8) as fp32 comes from a byte convert; fma(q + 8, s, -8 s) = q * s
-//   exactly (a 4-bit integer times an 8-bit-mantissa scale fits in fp32),
-//   so the only rounding is the final bf16 one.
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float m8s) {
-  const uint32_t off = w ^ 0x88888888u;
-  const uint32_t lo = off & 0x0F0F0F0Fu;          // j = 0, 2, 4, 6
-  const uint32_t hi = (off >> 4) & 0x0F0F0F0Fu;   // j = 1, 3, 5, 7
+//   A nibble t (two's complement, q = t < 8 ? t : t - 16) sits in the low
+//   mantissa bits of an fp16 whose other bits are those of 1024.0: one
+//   v_bitop3 computes (w & mask) ^ magic for two nibbles at once, the XOR
+//   flipping the nibble's top bit, so the fp16 values are 1024 + (q + 8)
+//   (nibbles at bits 0..3 of a half) or 1024 + 16 (q + 8) (bits 4..7).
+//   v_fma_mix_f32 widens that fp16 exactly and computes
+//   (1024 + q + 8) s - 1032 s, resp. (1024 + 16 (q + 8)) s/16 - 72 s, i.e.
+//   q * s; it is exact (a 4-bit integer times an 8-bit-mantissa scale fits
+//   in fp32), so the only rounding is the final bf16 one.
+// 17 VALU ops for 8 weights: one shift, four bitop3, eight fma_mix, four
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, const DeqScale& d) {
+  const uint32_t w8 = w >> 8;
+  const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) ^ 0x64086408u);   // j = 0, 4
+  const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) ^ 0x64806480u);   // j = 1, 5
+  const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) ^ 0x64086408u);  // j = 2, 6
+  const f16x2 e = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) ^ 0x64806480u);  // j = 3, 7
   u32x4 r;
-  r.x = pk_bf16(__builtin_fmaf(ubyte0(lo), s, m8s), __builtin_fmaf(ubyte0(hi), s, m8s));
-  r.y = pk_bf16(__builtin_fmaf(ubyte1(lo), s, m8s), __builtin_fmaf(ubyte1(hi), s, m8s));
-  r.z = pk_bf16(__builtin_fmaf(ubyte2(lo), s, m8s), __builtin_fmaf(ubyte2(hi), s, m8s));
-  r.w = pk_bf16(__builtin_fmaf(ubyte3(lo), s, m8s), __builtin_fmaf(ubyte3(hi), s, m8s));
+  r.x = pk_bf16(__builtin_fmaf((float)a.x, d.s, d.c0), __builtin_fmaf((float)b.x, d.s16, d.c1));
+  r.y = pk_bf16(__builtin_fmaf((float)c.x, d.s, d.c0), __builtin_fmaf((float)e.x, d.s16, d.c1));
+  r.z = pk_bf16(__builtin_fmaf((float)a.y, d.s, d.c0), __builtin_fmaf((float)b.y, d.s16, d.c1));
+  r.w = pk_bf16(__builtin_fmaf((float)c.y, d.s, d.c0), __builtin_fmaf((float)e.y, d.s16, d.c1));
   return r;
 }
 

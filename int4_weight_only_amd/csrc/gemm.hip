@@ -11,7 +11,7 @@
 // NW*WN weight rows.  Each wave owns WN weight rows and all BM activation
 // rows, so every weight is loaded from HBM and dequantized exactly once
 // per workgroup, straight into the MFMA B operand (no LDS round trip),
-// and the VALU cost of dequantization (about 3 ops per weight) is spread
+// and the VALU cost of dequantization (17 ops per 8 weights) is spread
 // over BM rows of MFMA work.  K advances 64 per step: lane (n = l % 32,
 // h = l / 32) loads the whole 32-element group 2c + h of weight row n (16
 // bytes, one scale) and word j of it feeds MFMA j
@@ -20,13 +20,14 @@
 //
 // Pipeline: activations go straight from HBM into LDS (16-byte
 // buffer_load ... lds, three stages, no staging registers); codes and
-// scales go to registers two steps ahead (two register sets, the K loop
-// unrolled by two).  In LDS a 64-element activation row is 128 bytes; its
-// eight 16-byte pieces are stored XOR-swizzled by (row / 2) % 8 so that
-// the MFMA operand reads of 32 consecutive rows spread over the banks.
-// Every load is a raw buffer load whose out-of-range lanes read zero
-// (rows past the end, K past the end, the padding step of an odd step
-// count), so no load is conditional.
+// scales go to registers two steps ahead (two register sets).  The K loop
+// is unrolled by six so that each step names its LDS stages statically.
+// In LDS a 64-element activation row is 128 bytes; its eight 16-byte
+// pieces are stored XOR-swizzled by (row / 2) % 8 so that the MFMA
+// operand reads of 32 consecutive rows spread over the banks.  Every load
+// is a raw buffer load whose out-of-range lanes read zero (rows past the
+// end, K past the end, the padding steps of the unrolled loop), so no
+// load is conditional.
 #include <type_traits>
 
 #include "common.h"
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   constexpr int XI = BM / 8;           // 1 KB direct-to-LDS loads per activation stage
   constexpr int XPW = XI / NW;         // ... issued by each wave
   constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage (three stages)
-  static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0, "tile shape");
+  static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
   // three separately declared stages: each DMA target and each operand
   // read names one object, so the compiler can tell that reading stage s
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   __shared__ int xrow[BM];     // activation row of each tile row (-1: none)
   __shared__ int orow[BM];     // output row of each tile row (-1: none)
   __shared__ int run_info[4];
+  __shared__ int wave_end[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,23 +171,41 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 
   for (int pass0 = 0; pass0 < rows_total; pass0 += BM) {
     const int rows = min(BM, rows_total - pass0);
-    // ---- row tables for this pass
-    for (int r = tid; r < BM; r += NT) {
+    // ---- row tables for this pass (thread r < BM fills row r)
+    {
       int xr_ = -1, yr = -1;
-      if (r < rows) {
+      if (tid < rows) {
         if constexpr (MOE) {
-          const int f = sorted_ids[row0 + pass0 + r];
+          const int f = sorted_ids[row0 + pass0 + tid];
           if (f < n_pairs) { xr_ = f / x_row_div; yr = f; }
         } else {
-          const int m = tile_m * BM + pass0 + r;
+          const int m = tile_m * BM + pass0 + tid;
           xr_ = m; yr = m;
         }
       }
-      xrow[r] = xr_;
-      orow[r] = yr;
+      if (tid < BM) {
+        xrow[tid] = xr_;
+        orow[tid] = yr;
+      }
+      if constexpr (MOE) {
+        // one past the last valid row of each wave's 64 rows: padding
+        // slots (sentinel ids) at the end of a run need no MFMA tile
+        const uint64_t v = __ballot(xr_ >= 0);
+        if (lane == 0) wave_end[wave] = v ? wave * 64 + 64 - (int)__clzll(v) : 0;
+      }
     }
     __syncthreads();
-    const int ms_valid = (rows + 31) >> 5;
+    int ms_valid = (rows + 31) >> 5;
+    if constexpr (MOE) {
+      int end = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) end = max(end, wave_end[w]);
+      ms_valid = (end + 31) >> 5;
+      if (ms_valid == 0) {   // a pass of padding only (blocks larger than the tile)
+        __syncthreads();     // wave_end is rewritten by the next pass
+        continue;
+      }
+    }
 
     // Direct-to-LDS activation loads.  Instruction i of this wave fills
     // tile rows 8 (wave*XPW + i) .. +7; lane l writes the 16 bytes at
@@ -199,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       const int xr_ = xrow[r];
       xoff[i] = xr_ >= 0 ? ((uint32_t)xr_ * (uint32_t)K + 8u * (uint32_t)pg) * 2u : kOOB;
     }
-    auto load_x = [&](int step, uint16_t* st) {
+    auto load_x = [&](int step, uint16_t* st) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const int col = step * kStepK + 8 * ((lane & 7) ^ (((8 * (wave * XPW + i) + (lane >> 3)) >> 1) & 7));
@@ -210,7 +230,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       }
     };
     // codes + scales of one step into a register set
-    auto load_w = [&](int step, u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) {
+    auto load_w = [&](int step, u32x4 (&wreg)[NS], uint32_t (&sreg)[NS])
+        __attribute__((always_inline)) {
       const int g = 2 * step + h;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
@@ -233,15 +254,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 
     // one step: wait for this step's activations, make them visible, start
     // the stage two ahead, dequantize, multiply, start the codes two ahead.
-    // Loads issued after this step's activations and before this wait:
-    // this step's codes (2 NS), the next step's activations (XPW) and codes.
-    // one step: wait for this step's activations, make them visible, start
-    // the stage two ahead, dequantize, multiply, start the codes two ahead.
     // MSE activation tiles are multiplied (rows past the pass read zero).
     // Per 16-wide K slice j all operand reads are issued first and the
     // MSE x NS MFMAs that follow are independent (no accumulator chain).
     auto step_body = [&](auto mse, int step, const uint16_t* st, uint16_t* st_next2,
-                         u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) {
+                         u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) __attribute__((always_inline)) {
       constexpr int MSE = decltype(mse)::value;
       // loads issued after this step's activations: its codes and scales
       // (2 NS), the next step's activations (XPW) and codes (2 NS)
@@ -253,12 +270,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         u32x4 bop[NS][4];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          const float sc = bf16_lo(sreg[ns]);
-          const float m8s = -8.0f * sc;
-          bop[ns][0] = dequant8(wreg[ns].x, sc, m8s);
-          bop[ns][1] = dequant8(wreg[ns].y, sc, m8s);
-          bop[ns][2] = dequant8(wreg[ns].z, sc, m8s);
-          bop[ns][3] = dequant8(wreg[ns].w, sc, m8s);
+          const DeqScale d = deq_scale(bf16_lo(sreg[ns]));
+          bop[ns][0] = dequant8(wreg[ns].x, d);
+          bop[ns][1] = dequant8(wreg[ns].y, d);
+          bop[ns][2] = dequant8(wreg[ns].z, d);
+          bop[ns][3] = dequant8(wreg[ns].w, d);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     load_w(0, wa, sa);
     load_x(1, xs1);
     load_w(1, wb, sb);
-    auto run_steps = [&](auto mse) {
+    auto run_steps = [&](auto mse) __attribute__((always_inline)) {
       for (int step = 0; step < nsteps6; step += 6) {
         step_body(mse, step + 0, xs0, xs2, wa, sa);
         step_body(mse, step + 1, xs1, xs0, wb, sb);
@@ -294,11 +310,17 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       }
     };
     if constexpr (MOE) {
-      // expert runs are often one activation tile (<= 32 rows)
+      // MFMA row tiles that hold valid rows (a run of one expert is often
+      // a single 32-row tile; a run of 85 rows padded to 128 needs three)
+      static_assert(MS == 4, "one instantiation per row-tile count");
       if (ms_valid == 1)
         run_steps(std::integral_constant<int, 1>{});
+      else if (ms_valid == 2)
+        run_steps(std::integral_constant<int, 2>{});
+      else if (ms_valid == 3)
+        run_steps(std::integral_constant<int, 3>{});
       else
-        run_steps(std::integral_constant<int, MS>{});
+        run_steps(std::integral_constant<int, 4>{});
     } else {
       run_steps(std::integral_constant<int, MS>{});
     }
