@@ -10,6 +10,9 @@ each on its own copy of the weights (24 copies rotate, 680 MB in all, so
 the 256 MB last-level cache never holds the step's weights).  ``value`` is
 the algorithmic HBM traffic of the step (packed codes + scales + X + Y)
 over the step time, HIP events on the launch stream around exactly K steps.
+Before each timed region the same work runs untimed for SETTLE_MS (after
+the W warm-up steps): from idle the GPU takes a few tens of milliseconds
+of sustained load to reach its steady clocks.
 
 The other workloads of the path are timed in the same run and reported
 under "detail": the prefill product (M = 4096, N = 14336, K = 4096,
@@ -38,6 +41,7 @@ PEAK_BF16_TFLOPS = 2500.0
 
 DECODE_N, DECODE_K, DECODE_MS = 12288, 4096, (1, 8, 16, 32)
 ROTATE = 24
+SETTLE_MS = 150.0     # sustained untimed load before each timed region
 
 
 def decode_bytes(M, N=DECODE_N, K=DECODE_K):
@@ -77,6 +81,16 @@ class Timer:
         b.record(st)
         torch.cuda.synchronize()
         return a.elapsed_time(b)          # ms for all iterations
+
+    def settle(self, fn, min_ms=SETTLE_MS):
+        """Untimed: repeat fn until min_ms of sustained work has run.  From
+        idle the GPU needs a few tens of milliseconds of load to reach its
+        steady clocks; numbers taken earlier describe the ramp, not the
+        kernel."""
+        done, n = 0.0, 1
+        while done < min_ms:
+            done += self.run(fn, n)
+            n = min(2 * n, 1024)
 
 
 def source_hash():
@@ -121,6 +135,7 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
             w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
 
     timer.run(step, warmup)
+    timer.settle(step)
     ms = timer.run(step, steps)
     step_bytes = sum(decode_bytes(M) for M in DECODE_MS)
     per_m = {}
@@ -129,6 +144,7 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
             r = i % ROTATE
             w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
         timer.run(one, warmup)
+        timer.settle(one, SETTLE_MS / 3)
         t = timer.run(one, steps) / steps
         per_m[str(M)] = {"us": round(t * 1e3, 3),
                          "GB/s": round(decode_bytes(M) / (t * 1e-3) / 1e9, 1),
@@ -147,7 +163,7 @@ def bench_prefill(w4, synth, torch, iters, timer):
     Wq, S = w4.w4_quantize_pack(W)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     f = lambda i: w4.w4a16_gemm(X, Wq, S, out=Y)
-    timer.run(f, 2)
+    timer.settle(f)
     t = timer.run(f, iters) / iters
     tf = gemm_flops(M, N, K) / (t * 1e-3) / 1e12
     return {"M": M, "N": N, "K": K, "us": round(t * 1e3, 1), "TFLOP/s": round(tf, 1),
@@ -167,7 +183,7 @@ def bench_quant(w4, synth, torch, iters, timer):
     fq_bytes = 4 * N * K
     for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
                              ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes)):
-        timer.run(fn, 3)
+        timer.settle(fn, SETTLE_MS / 3)
         t = timer.run(fn, iters) / iters
         gbs = nbytes / (t * 1e-3) / 1e9
         out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "bytes": nbytes,
@@ -219,7 +235,7 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
         for fn in stages.values():
             fn()
 
-    timer.run(layer, 2)
+    timer.settle(layer)
     t_layer = timer.run(layer, iters) / iters
     per = {}
     for sname, fn in stages.items():
@@ -331,7 +347,7 @@ def main():
         cpu = cpu_baseline()
 
     line = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+            "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "decode W4A16 GEMV sweep: packed int4 W[12288x4096] group 32 "
                                    "bf16 scales, X[M,4096] bf16, M in {1,8,16,32}",

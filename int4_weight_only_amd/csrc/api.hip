@@ -3,7 +3,7 @@
 // Every entry point validates all of its arguments before enqueueing any
 // work, so a nonzero status leaves the outputs untouched.  Nothing here
 // allocates, synchronizes or reads device memory.
-#include "../../include/w4a16.h"
+#include "w4a16.h"
 
 #include "common.h"
 

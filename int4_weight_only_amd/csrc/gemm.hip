@@ -50,7 +50,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // MOE = true: the workgroup leads a run of alignment blocks of one expert;
 // row r of the run is pair f = sorted_ids[row0 + r] (valid if f < n_pairs),
 // activation row f / x_row_div, output row f.
-template <int BM, int WN, int NW, bool MOE>
+// SA: K is a multiple of 256, so a row's scales start 16-byte aligned and
+// eight of them are one 16-byte load.
+template <int BM, int WN, int NW, bool MOE, bool SA>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
@@ -80,15 +82,27 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  // Tile of this workgroup.  MoE: (blockIdx.x = weight-row tile,
-  // blockIdx.y = alignment block).  Dense: a 1-D grid; workgroups are
+  // Tile of this workgroup.  MoE: a slot of at most BM rows (an alignment
+  // block, or one BM-row part of a block larger than BM) and a weight-row
+  // tile; the workgroup leads a run of consecutive slots of one expert,
+  // at most BM rows.  Dense: a 1-D grid; workgroups are
   // dispatched round-robin over the 8 XCDs (each with its own L2), so XCD x
   // takes the contiguous tile range [x * per, (x + 1) * per), walked in
   // groups of GM activation row-blocks: the workgroups running together on
   // one XCD share activation rows and weight rows in that XCD's L2.
   int tile_n, tile_m;
+  int slot = 0;
+  const int bpw = BM >= B ? BM / B : 1;               // MoE: blocks per run (at most)
+  const int ppb = B > BM ? (B + BM - 1) / BM : 1;      // MoE: slots per block
   if constexpr (MOE) {
-    tile_n = blockIdx.x;
+    // XCD-aware: groups of bpw slots (one run's worth) go round-robin over
+    // the XCDs; all N-tiles of a group on one XCD, which share its rows
+    const int ntn = gridDim.x;                       // N-tiles
+    const int pid = blockIdx.x + ntn * blockIdx.y;   // dispatch order
+    const int xcd = pid & 7, j = pid >> 3;
+    tile_n = j % ntn;
+    const int q = j / ntn;
+    slot = (xcd + 8 * (q / bpw)) * bpw + q % bpw;
     tile_m = 0;
   } else {
     constexpr int kXcds = 8, GM = 8;
@@ -109,8 +123,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   const int G = K >> 5;
   const int kw = K >> 3;
 
-  int rows_total;              // rows handled by this workgroup (all passes)
-  int row0 = 0;                // MoE: first sorted slot of the run
+  int rows;                    // rows of this workgroup's tile (<= BM)
+  int row0 = 0;                // MoE: first sorted position of the run
   int expert = 0;
   if constexpr (MOE) {
     // Find this block's run of one expert with wave 0: expert_ids[0, nblk)
@@ -119,12 +133,12 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     // parallel loads; ballots give the distance to the run's first block
     // (a longer run walks back 64 blocks at a time) and its end.
     if (wave == 0) {
-      const int b = blockIdx.y;
+      const int b = slot / ppb;
+      const int part = slot - b * ppb;
       const int nblk = ntpp[0] / B;
       int lead = 0, e = -1, last = 0;
       if (b < nblk) {
         e = expert_ids[b];
-        const int bpw = BM >= B ? BM / B : 1;
         // backwards: first block of the run
         int first = b;
         for (int base = b;; base -= 64) {
@@ -147,39 +161,38 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       if (lane == 0) {
         run_info[0] = lead;
         run_info[1] = e;
-        run_info[2] = b * B;
-        run_info[3] = lead ? (last - b) * B : 0;
+        run_info[2] = b * B + part * BM;
+        run_info[3] = lead ? min(BM, (last - b) * B - part * BM) : 0;
       }
     }
     __syncthreads();
     if (!run_info[0]) return;
     expert = run_info[1];
     row0 = run_info[2];
-    rows_total = run_info[3];
+    rows = run_info[3];
   } else {
-    rows_total = min(BM, M - tile_m * BM);
+    rows = min(BM, M - tile_m * BM);
   }
 
   const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
-  const int nsteps6 = (nsteps + 5) / 6 * 6;  // padded to the unroll; pad steps load zeros, skip MFMAs
+  const int nsteps3 = (nsteps + 2) / 3 * 3;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
   const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
 
-  for (int pass0 = 0; pass0 < rows_total; pass0 += BM) {
-    const int rows = min(BM, rows_total - pass0);
-    // ---- row tables for this pass (thread r < BM fills row r)
+  {
+    // ---- row tables (thread r < BM fills row r)
     {
       int xr_ = -1, yr = -1;
       if (tid < rows) {
         if constexpr (MOE) {
-          const int f = sorted_ids[row0 + pass0 + tid];
+          const int f = sorted_ids[row0 + tid];
           if (f < n_pairs) { xr_ = f / x_row_div; yr = f; }
         } else {
-          const int m = tile_m * BM + pass0 + tid;
+          const int m = tile_m * BM + tid;
           xr_ = m; yr = m;
         }
       }
@@ -201,10 +214,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 #pragma unroll
       for (int w = 0; w < NW; ++w) end = max(end, wave_end[w]);
       ms_valid = (end + 31) >> 5;
-      if (ms_valid == 0) {   // a pass of padding only (blocks larger than the tile)
-        __syncthreads();     // wave_end is rewritten by the next pass
-        continue;
-      }
+      if (ms_valid == 0) return;   // a slot of padding only (blocks larger than the tile)
     }
 
     // Direct-to-LDS activation loads.  Instruction i of this wave fills
@@ -229,9 +239,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
             0, 0);
       }
     };
-    // codes + scales of one step into a register set
-    auto load_w = [&](int step, u32x4 (&wreg)[NS], uint32_t (&sreg)[NS])
-        __attribute__((always_inline)) {
+    // codes of one step into a register set
+    auto load_w = [&](int step, u32x4 (&wreg)[NS]) __attribute__((always_inline)) {
       const int g = 2 * step + h;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
@@ -239,45 +248,96 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         // rows past N lie past the buffer's end; a group past K reads zero
         const uint32_t woff = (g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
         wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
-        const uint32_t soff = (g < G) ? (n * (uint32_t)G + (uint32_t)g) * 2u : kOOB;
-        sreg[ns] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+      }
+    };
+    // Scales come in windows of 8 steps (16 groups): lane (n, h) loads the
+    // 8 scales of groups 16 u + 8 h .. + 7 of its row, so a scale row is
+    // read in 32-byte pieces, each once (scattered 2-byte loads per step
+    // would need each 128-byte scale line to stay in L2 for 32 steps).
+    auto load_s = [&](int u, u32x4 (&raw)[NS]) __attribute__((always_inline)) {
+      const int g0 = 16 * u + 8 * h;
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
+        if constexpr (SA) {
+          const uint32_t soff = (g0 < G) ? (n * (uint32_t)G + (uint32_t)g0) * 2u : kOOB;
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, soff, 0, 0);
+        } else {
+          uint32_t hw[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int g = g0 + j;
+            const uint32_t soff = (g < G) ? (n * (uint32_t)G + (uint32_t)g) * 2u : kOOB;
+            hw[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+          }
+          raw[ns] = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
+                          hw[6] | (hw[7] << 16)};
+        }
+      }
+    };
+    // Step t of the window uses group 2 t + h.  v_permlane32_swap hands each
+    // lane its partner's (other h) raw dwords; v_perm keeps half h of both:
+    // scw[ns][k] = (scale of step k, scale of step k + 4) as a bf16 pair.
+    const uint32_t half_sel = h ? 0x07060302u : 0x05040100u;
+    auto unpack_s = [&](const u32x4 (&raw)[NS], uint32_t (&scw)[NS][4])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const uint32_t r[4] = {raw[ns].x, raw[ns].y, raw[ns].z, raw[ns].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const auto pr = __builtin_amdgcn_permlane32_swap(r[k], r[k], false, false);
+          // pr[0]: the h = 0 lane's dword (groups 2k, 2k + 1 of the window)
+          // pr[1]: the h = 1 lane's dword (groups 8 + 2k, 8 + 2k + 1)
+          scw[ns][k] = __builtin_amdgcn_perm(pr[1], pr[0], half_sel);
+        }
       }
     };
 
-    f32x16 acc[MS][NS];
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
-
-    // one step: wait for this step's activations, make them visible, start
-    // the stage two ahead, dequantize, multiply, start the codes two ahead.
-    // MSE activation tiles are multiplied (rows past the pass read zero).
-    // Per 16-wide K slice j all operand reads are issued first and the
-    // MSE x NS MFMAs that follow are independent (no accumulator chain).
+    // One step: wait for this step's activations and make them visible,
+    // start the stage two ahead, dequantize, multiply, start the codes three
+    // ahead.  MSE activation tiles are multiplied (rows past the tile read
+    // zero).  Per 16-wide K slice j all operand reads are issued first and
+    // the MSE x NS MFMAs that follow are independent (no accumulator chain).
+    u32x4 sraw[NS];            // scale window in flight
+    uint32_t scw[NS][4];       // scale window in use
     auto step_body = [&](auto mse, int step, const uint16_t* st, uint16_t* st_next2,
-                         u32x4 (&wreg)[NS], uint32_t (&sreg)[NS]) __attribute__((always_inline)) {
+                         u32x4 (&wreg)[NS], f32x16 (&acc)[decltype(mse)::value][NS])
+        __attribute__((always_inline)) {
       constexpr int MSE = decltype(mse)::value;
-      // loads issued after this step's activations: its codes and scales
-      // (2 NS), the next step's activations (XPW) and codes (2 NS)
-      static_assert(XPW + 4 * NS <= 63, "vmcnt range");
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPW + 4 * NS) : "memory");
-      __syncthreads();
+      // Loads issued after this step's activations: the codes of step + 1
+      // (NS), the activations of step + 1 (XPW) and the codes of step + 2
+      // (NS), plus at times a scale window (waiting for fewer outstanding
+      // loads than were issued is only stricter).  Then a bare s_barrier:
+      // __syncthreads' release fence would also wait for the next stage's
+      // activation DMA, which nothing reads yet.  The empty asm statements
+      // keep LDS accesses on their side of the barrier.
+      static_assert(XPW + 2 * NS <= 63, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(XPW + 2 * NS) : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       load_x(step + 2, st_next2);
+      if ((step & 7) == 0) {   // a new scale window: unpack it, fetch the next
+        unpack_s(sraw, scw);
+        load_s((step >> 3) + 1, sraw);
+      }
       if (step < nsteps) {
-        u32x4 bop[NS][4];
+        const int t = step & 7;
+        DeqScale d[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          const DeqScale d = deq_scale(bf16_lo(sreg[ns]));
-          bop[ns][0] = dequant8(wreg[ns].x, d);
-          bop[ns][1] = dequant8(wreg[ns].y, d);
-          bop[ns][2] = dequant8(wreg[ns].z, d);
-          bop[ns][3] = dequant8(wreg[ns].w, d);
+          const uint32_t x = scw[ns][t & 3];
+          d[ns] = deq_scale((t & 4) ? bf16_hi(x) : bf16_lo(x));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // word j of each code register feeds MFMA slice j
+          u32x4 bop[NS];
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+            bop[ns] = dequant8(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
+                                                                                : wreg[ns].w,
+                               d[ns]);
           u32x4 a[MSE];
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms) {
@@ -287,50 +347,41 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms)
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns][j], acc[ms][ns]);
+            for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
         }
       }
-      load_w(step + 2, wreg, sreg);
+      load_w(step + 3, wreg);
     };
 
-    u32x4 wa[NS], wb[NS];
-    uint32_t sa[NS], sb[NS];
+    u32x4 wa[NS], wb[NS], wc[NS];
     load_x(0, xs0);
-    load_w(0, wa, sa);
+    load_w(0, wa);
+    load_s(0, sraw);
     load_x(1, xs1);
-    load_w(1, wb, sb);
-    auto run_steps = [&](auto mse) __attribute__((always_inline)) {
-      for (int step = 0; step < nsteps6; step += 6) {
-        step_body(mse, step + 0, xs0, xs2, wa, sa);
-        step_body(mse, step + 1, xs1, xs0, wb, sb);
-        step_body(mse, step + 2, xs2, xs1, wa, sa);
-        step_body(mse, step + 3, xs0, xs2, wb, sb);
-        step_body(mse, step + 4, xs1, xs0, wa, sa);
-        step_body(mse, step + 5, xs2, xs1, wb, sb);
-      }
-    };
-    if constexpr (MOE) {
-      // MFMA row tiles that hold valid rows (a run of one expert is often
-      // a single 32-row tile; a run of 85 rows padded to 128 needs three)
-      static_assert(MS == 4, "one instantiation per row-tile count");
-      if (ms_valid == 1)
-        run_steps(std::integral_constant<int, 1>{});
-      else if (ms_valid == 2)
-        run_steps(std::integral_constant<int, 2>{});
-      else if (ms_valid == 3)
-        run_steps(std::integral_constant<int, 3>{});
-      else
-        run_steps(std::integral_constant<int, 4>{});
-    } else {
-      run_steps(std::integral_constant<int, MS>{});
-    }
-    // drain the loads of the padding steps before LDS is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // ---- epilogue: lane holds D[8*(v/4) + 4*h + v%4][l32] of each tile
+    load_w(1, wb);
+    load_w(2, wc);
+    // The steps and the epilogue, for MSE valid 32-row tiles
+    // (accumulators of tiles that hold no valid row are never allocated).
+    auto run_tile = [&](auto mse) __attribute__((always_inline)) {
+      constexpr int MSE = decltype(mse)::value;
+      f32x16 acc[MSE][NS];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      if (ms < ms_valid) {
+      for (int ms = 0; ms < MSE; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
+      for (int step = 0; step < nsteps3; step += 3) {
+        step_body(mse, step + 0, xs0, xs2, wa, acc);
+        step_body(mse, step + 1, xs1, xs0, wb, acc);
+        step_body(mse, step + 2, xs2, xs1, wc, acc);
+      }
+      // drain the loads of the padding steps before LDS is reused
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+      // ---- epilogue: lane holds D[8*(v/4) + 4*h + v%4][l32] of each tile
+#pragma unroll
+      for (int ms = 0; ms < MSE; ++ms) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -351,8 +402,22 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
           }
         }
       }
+    };
+    if constexpr (MOE) {
+      // MFMA row tiles that hold valid rows (a run of one expert is often
+      // a single 32-row tile; a run of 85 rows padded to 128 needs three)
+      static_assert(MS == 4, "one instantiation per row-tile count");
+      if (ms_valid == 1)
+        run_tile(std::integral_constant<int, 1>{});
+      else if (ms_valid == 2)
+        run_tile(std::integral_constant<int, 2>{});
+      else if (ms_valid == 3)
+        run_tile(std::integral_constant<int, 3>{});
+      else
+        run_tile(std::integral_constant<int, 4>{});
+    } else {
+      run_tile(std::integral_constant<int, MS>{});
     }
-    __syncthreads();   // row tables and LDS stages are rewritten by the next pass
   }
 }
 
@@ -367,9 +432,14 @@ hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
   const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
-  hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false>), grid, dim3(kNW * 64), 0, st, X,
-                     (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr,
-                     nullptr, 0, 1, 1, 0);
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       nullptr, nullptr, 0, 1, 1, 0);
+  else
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false>), grid, dim3(kNW * 64), 0, st,
+                       X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       nullptr, nullptr, 0, 1, 1, 0);
   return hipGetLastError();
 }
 
@@ -380,10 +450,19 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            int32_t x_row_div, hipStream_t st) {
   const int64_t n_pairs = T * k;
   const int64_t cap = ((n_pairs + (int64_t)E * (B - 1) + B - 1) / B) * B;
-  const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)), (unsigned)(cap / B));
-  hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true>), grid, dim3(kNW * 64), 0, st, X,
-                     (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
-                     topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
+  const int64_t bpw = kBMMoe >= B ? kBMMoe / B : 1;
+  const int64_t ppb = B > kBMMoe ? (B + kBMMoe - 1) / kBMMoe : 1;   // slots per block
+  const int64_t slots = (cap / B) * ppb;
+  const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)),
+                  (unsigned)((slots + 8 * bpw - 1) / (8 * bpw) * (8 * bpw)));
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
+                       topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
+  else
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
+                       topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
 }
 
