@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode1(const uint16_t* __restr
       for (int cc = 0; cc < kCPW; ++cc) {
         const int g = 4 * (c0 + cc) + kq;
         const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, kNonTemporal);
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
@@ -436,43 +436,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode1(const uint16_t* __restr
 #pragma unroll
     for (int t = 0; t < T; ++t) *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc[t];
 
-    // ---- sum over waves in a fixed order (deterministic), rows m < M only.
-    // Few outputs (small M): four lanes share one, lane q adding waves
-    // 4q .. 4q+3, then two quad exchanges.  Otherwise one thread per output.
+    // ---- sum over waves in a fixed order (deterministic): one thread per
+    // output, rows m < M only
     __syncthreads();
     const int mrows = min(M, 16);
     const int nout = ntiles * mrows * 16;
-    auto emit = [&](int o, float sum) {
+    for (int o = tid; o < nout; o += kWaves * 64) {
       const int t = o / (mrows * 16);
       const int m = (o >> 4) % mrows;
       const int n = o & 15;
+      const int e = n * PSTR + m;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += part[t][w][e];
       const int row = t * 16 + n;
       if (npass > 1) {
         sum += (pass == 0) ? 0.0f : ybuf[t][m * 16 + n];
         ybuf[t][m * 16 + n] = sum;
       }
       if (pass == npass - 1 && row < rows) Y[(size_t)m * N + n0 + row] = to_bf16(sum);
-    };
-    auto elem = [&](int o) { return ((o & 15) * PSTR) + (o >> 4) % mrows; };
-    if (nout * 4 <= kWaves * 64) {
-      const int o = min(tid >> 2, nout - 1);
-      const int q = tid & 3;
-      const int t = o / (mrows * 16);
-      const int e = elem(o);
-      float sum = part[t][4 * q][e] + part[t][4 * q + 1][e] + part[t][4 * q + 2][e] +
-                  part[t][4 * q + 3][e];
-      sum += __uint_as_float(quad_xor1(__float_as_uint(sum)));
-      sum += __uint_as_float(quad_xor2(__float_as_uint(sum)));
-      if (q == 0 && (tid >> 2) < nout) emit(o, sum);
-    } else {
-      for (int o = tid; o < nout; o += kWaves * 64) {
-        const int t = o / (mrows * 16);
-        const int e = elem(o);
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += part[t][w][e];
-        emit(o, sum);
-      }
     }
     if (npass > 1) __syncthreads();   // part is rewritten by the next pass
   }
