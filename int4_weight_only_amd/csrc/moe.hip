@@ -19,14 +19,19 @@ namespace w4 {
 // ------------------------------------------------------------------ align --
 //
 // One workgroup of 1024 threads (the alignment touches T*k ids, a few
-// thousand to a few tens of thousands, and must be stable and exact).
-//  1. histogram of experts (LDS atomics: the counts do not depend on order);
-//  2. exclusive scan of the padded counts -> segment starts;
-//  3. stable placement, 1024 pairs per round: inside a wave the lanes with
-//     the same expert are found with ten ballots (one per bit of the id),
-//     giving each lane its rank among equal lanes before it; a per-expert
-//     prefix over the 16 waves (in wave order, in LDS) and a running count
-//     per expert place the round after all earlier rounds;
+// thousand to a few tens of thousands, and must be stable and exact).  Wave
+// w owns the contiguous pair range [w*P/16, (w+1)*P/16).
+//  1. per-wave histograms of experts in LDS (atomics on the wave's own
+//     counters: counts do not depend on order);
+//  2. exclusive scan of the padded counts -> segment starts; then, per
+//     expert, a scan over the waves in wave order turns the wave's count
+//     into the position where its first pair of that expert goes;
+//  3. every wave walks its range in order, 64 pairs per round: the lanes
+//     with the same expert are found with ten ballots (one per bit of the
+//     id), giving each lane its rank among equal lanes before it; the
+//     round's first lane of each expert then advances the wave's position
+//     for that expert.  No barrier between rounds: positions are private to
+//     the wave, read and advanced in program order;
 //  4. padding slots, the tail and the block -> expert map are written by
 //     disjoint threads, so no location is written twice.
 constexpr int kAlignThreads = 1024;
@@ -40,35 +45,51 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
                                                          int32_t* __restrict__ sorted_ids,
                                                          int32_t* __restrict__ expert_ids,
                                                          int32_t* __restrict__ ntpp) {
-  __shared__ int count[kMaxExperts];
+  __shared__ int pos[kAlignWaves][kMaxExperts];   // counts, then positions
   __shared__ int start[kMaxExperts];
-  __shared__ int running[kMaxExperts];
-  __shared__ int wave_base[kAlignWaves][kMaxExperts];
+  __shared__ int count[kMaxExperts];
   __shared__ int wave_tot[kAlignWaves];
   __shared__ int total_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int chunk = (P + kAlignWaves - 1) / kAlignWaves;
+  const int f_lo = min(P, wave * chunk);
+  const int f_hi = min(P, f_lo + chunk);
 
-  for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
-    count[e] = 0;
-    running[e] = 0;
-  }
-  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads)
-    (&wave_base[0][0])[i] = 0;
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&pos[0][0])[i] = 0;
   __syncthreads();
 
-  // 1. histogram
-  for (int f = tid; f < P; f += kAlignThreads) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&count[e], 1);
+  // ids of kBatch rounds are loaded together (the rounds would otherwise
+  // wait on one load each)
+  constexpr int kBatch = 8;
+  auto load_batch = [&](int base, int (&v)[kBatch]) {
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int f = base + 64 * r + lane;
+      v[r] = (f < f_hi) ? ids[f] : -1;
+    }
+  };
+
+  // 1. per-wave histograms
+  for (int base = f_lo; base < f_hi; base += 64 * kBatch) {
+    int v[kBatch];
+    load_batch(base, v);
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r)
+      if (v[r] >= 0 && v[r] < E) atomicAdd(&pos[wave][v[r]], 1);
   }
   __syncthreads();
 
-  // 2. exclusive scan of padded counts (thread e owns expert e)
-  int padded = 0;
-  if (tid < E) padded = ((count[tid] + B - 1) / B) * B;
+  // 2. segment starts (thread e owns expert e), then per-wave positions
+  int c = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) c += pos[w][tid];
+    count[tid] = c;
+  }
+  const int padded = (tid < E) ? ((c + B - 1) / B) * B : 0;
   int incl = padded;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -79,60 +100,57 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   __syncthreads();
   int wprefix = 0;
   for (int w = 0; w < wave; ++w) wprefix += wave_tot[w];
-  if (tid < E) start[tid] = wprefix + incl - padded;
+  if (tid < E) {
+    const int s0 = wprefix + incl - padded;
+    start[tid] = s0;
+    int run = s0;
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int n = pos[w][tid];
+      pos[w][tid] = run;
+      run += n;
+    }
+  }
   if (tid == kAlignThreads - 1) total_sh = wprefix + incl;
   __syncthreads();
   const int total = total_sh;
 
-  // 3. stable placement
+  // 3. stable placement, each wave through its own range
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < P; base += kAlignThreads) {
-    const int f = base + tid;
-    int e = -1;
-    if (f < P) {
-      const int v = ids[f];
-      if (v >= 0 && v < E) e = v;
-    }
-    const bool valid = e >= 0;
-    uint64_t match = ballot64(valid);
+  for (int base0 = f_lo; base0 < f_hi; base0 += 64 * kBatch) {
+    int v[kBatch];
+    load_batch(base0, v);
 #pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const bool b = valid && ((e >> bit) & 1);
-      const uint64_t ones = ballot64(b);
-      match &= ((e >> bit) & 1) ? ones : ~ones;
-    }
-    const int rank = __popcll(match & lt_mask);
-    const bool leader = valid && rank == 0;
-    if (leader) wave_base[wave][e] = __popcll(match);
-    __syncthreads();
-    if (tid < E) {
-      int run = running[tid];
+    for (int r = 0; r < kBatch; ++r) {
+      const int f = base0 + 64 * r + lane;
+      const int e = (v[r] >= 0 && v[r] < E) ? v[r] : -1;
+      const bool valid = e >= 0;
+      uint64_t match = ballot64(valid);
 #pragma unroll
-      for (int w = 0; w < kAlignWaves; ++w) {
-        // only entries some lane of wave w leads are rewritten (and that
-        // leader clears them after placement); absent experts stay 0
-        const int c = wave_base[w][tid];
-        if (c != 0) wave_base[w][tid] = run;
-        run += c;
+      for (int bit = 0; bit < 10; ++bit) {
+        const bool b = valid && ((e >> bit) & 1);
+        const uint64_t ones = ballot64(b);
+        match &= ((e >> bit) & 1) ? ones : ~ones;
       }
-      running[tid] = run;
+      const int rank = __popcll(match & lt_mask);
+      int p = 0;
+      if (valid) p = pos[wave][e] + rank;
+      // every lane has read its position (same wave, program order) before
+      // the expert's first lane advances it
+      if (valid && rank == 0) pos[wave][e] += __popcll(match);
+      if (valid) sorted_ids[p] = f;
     }
-    __syncthreads();
-    if (valid) sorted_ids[start[e] + wave_base[wave][e] + rank] = f;
-    // same wave, program order: every lane has read its base before the
-    // leader clears the entry for the next round
-    if (leader) wave_base[wave][e] = 0;
   }
 
   // 4. padding slots inside segments, the tail, and the block map
   if (tid < E) {
     const int s0 = start[tid];
-    const int c = count[tid];
-    const int pe = ((c + B - 1) / B) * B;
-    for (int p = s0 + c; p < s0 + pe; ++p) sorted_ids[p] = P;
+    const int cnt = count[tid];
+    const int pe = ((cnt + B - 1) / B) * B;
+    for (int q = s0 + cnt; q < s0 + pe; ++q) sorted_ids[q] = P;
     for (int b = s0 / B; b < (s0 + pe) / B; ++b) expert_ids[b] = tid;
   }
-  for (int p = total + tid; p < cap; p += kAlignThreads) sorted_ids[p] = P;
+  for (int q = total + tid; q < cap; q += kAlignThreads) sorted_ids[q] = P;
   for (int b = total / B + tid; b < cap / B; b += kAlignThreads) expert_ids[b] = -1;
   if (tid == 0) ntpp[0] = total;
 }
