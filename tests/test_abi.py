@@ -204,3 +204,12 @@ def test_elementwise_validation(lib):
     assert lib.w4_moe_route(None, 4, 64, 8, A4, A4, None) == NULL
     assert lib.w4_moe_route(A2, 4, 64, 8, A4, A4, None) == MISALIGNED
     assert lib.w4_moe_route(None, 0, 64, 8, None, None, None) == OK
+
+
+def test_qat_op_refuses_cpu_tensors():
+    """The QAT op has no CPU path: a CPU weight is rejected before any call."""
+    import torch
+    from int4_weight_only_amd.qat import fake_quant_ste
+    W = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fake_quant_ste(W)

@@ -1,0 +1,60 @@
+"""GPU: the QAT op (fake quant forward, straight-through backward).
+
+Forward: bit-exact against the oracle's fake quant.  Backward: the
+straight-through estimator passes the upstream gradient unchanged to the
+bf16 master weight (grad_W == grad_out bit for bit), also through a small
+linear layer whose loss depends on the fake-quantized weight.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import dev, down_bits, say, up_bits
+from int4_weight_only_amd.qat import fake_quant_ste
+from oracle import quant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,K,seed", [(512, 512, 0), (96, 160, 7), (1, 32, 3)])
+def test_forward_matches_oracle(N, K, seed):
+    say(f"qat forward N={N} K={K}")
+    Wb = synth.bits(synth.weights(N, K, seed))
+    W = up_bits(Wb).requires_grad_(True)
+    Y = fake_quant_ste(W)
+    np.testing.assert_array_equal(down_bits(Y.detach()), quant.fake_quant(Wb))
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (64, 96)])
+def test_backward_is_identity(N, K):
+    say(f"qat backward N={N} K={K}")
+    W = synth.weights(N, K, 11).to(dev()).requires_grad_(True)
+    G = synth.activations(N, K, 12).to(dev())
+    Y = fake_quant_ste(W)
+    Y.backward(G)
+    torch.cuda.synchronize()
+    assert W.grad is not None and W.grad.dtype == torch.bfloat16
+    np.testing.assert_array_equal(synth.bits(W.grad), synth.bits(G))
+
+
+def test_gradient_through_a_linear_layer():
+    """loss = sum(X @ fq(W)^T * R): dloss/dW = R^T @ X exactly as for an
+    unquantized weight (the estimator hides the rounding)."""
+    say("qat linear layer")
+    M, N, K = 8, 64, 128
+    W = synth.weights(N, K, 21).to(dev()).float().requires_grad_(True)
+    X = synth.activations(M, K, 22).to(dev()).float()
+    R = synth.activations(M, N, 23).to(dev()).float()
+    Wq = fake_quant_ste(W.to(torch.bfloat16)).float()
+    loss = ((X @ Wq.t()) * R).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    # the gradient reaches W through one bf16 cast; the two fp32 products may
+    # round differently, so allow one bf16 step
+    expect = (R.t().cpu().double() @ X.cpu().double()).numpy()
+    np.testing.assert_allclose(W.grad.cpu().numpy(), expect, rtol=2 ** -7, atol=1e-3)
+    # and the forward used the quantization grid
+    ref = quant.fake_quant(synth.bits(W.detach().to(torch.bfloat16).cpu()))
+    np.testing.assert_array_equal(synth.bits(Wq.detach().to(torch.bfloat16)), ref)
