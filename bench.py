@@ -216,7 +216,7 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     logits = synth.router_logits(T, E, seed, wl["skew"], device=dev)
     B = w4.w4_pick_block_size(T, k, E)
     ids, tw = w4.w4_moe_route(logits, k)
-    buf = wmoe.alloc_buffers(T, k, E, H, I, B, dev)
+    buf = wmoe.alloc_buffers(T, k, E, H, I, B, dev, fused=False)
     tw_flat = tw.reshape(-1)
 
     stages = {
@@ -226,14 +226,21 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
         "gate_up": lambda: w4.w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, buf.sorted_token_ids,
                                              buf.expert_ids, buf.ntpp, T, k, B, k, out=buf.H1),
         "silu_mul": lambda: w4.w4_silu_mul(buf.H1, out=buf.A),
+        "gate_up_swiglu": lambda: w4.w4a16_moe_gemm_swiglu(X, gate_up.Wq, gate_up.S,
+                                                           buf.sorted_token_ids, buf.expert_ids,
+                                                           buf.ntpp, T, k, B, k, out=buf.A),
         "down": lambda: w4.w4a16_moe_gemm(buf.A, down.Wq, down.S, buf.sorted_token_ids,
                                           buf.expert_ids, buf.ntpp, T, k, B, 1, out=buf.H2),
         "combine": lambda: w4.w4_moe_sum(buf.H2, tw, T, k, out=buf.out),
     }
 
+    # the layer runs the fused gate_up + SwiGLU; the unfused pair is timed
+    # per stage for reference
+    layer_stages = ("route", "align", "gate_up_swiglu", "down", "combine")
+
     def layer(i):
-        for fn in stages.values():
-            fn()
+        for sname in layer_stages:
+            stages[sname]()
 
     timer.settle(layer)
     t_layer = timer.run(layer, iters) / iters

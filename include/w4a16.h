@@ -165,6 +165,26 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                    int32_t x_row_div, void* stream);
 
 /*
+ * w4a16_moe_gemm_swiglu -- the gate_up projection with the SwiGLU of
+ * w4_silu_mul fused into its epilogue (NEXT step of [RL] §4's "MoE operator
+ * fusion"; the activation is a reading, as for w4_silu_mul).  Wq / S hold
+ * 2I weight rows per expert: rows [0, I) gate, [I, 2I) up.  For every
+ * valid slot (as in w4a16_moe_gemm, topk weights not applied):
+ *   g = bf16_rne(X[f / x_row_div, :] * dequant(W_e[0:I])^T)
+ *   u = bf16_rne(X[f / x_row_div, :] * dequant(W_e[I:2I])^T)
+ *   A[f, i] = bf16_rne( silu(g[i]) * u[i] )
+ * so A equals w4_silu_mul(w4a16_moe_gemm(...)) bit for bit, without the
+ * [T*k, 2I] intermediate.  X, Wq, S, the alignment arrays, B and x_row_div
+ * as for w4a16_moe_gemm with N = 2I; A bf16 [T*k, I], 4-byte aligned;
+ * I >= 1.  Rows of A not named by a valid slot are not written.
+ */
+int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                          const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
+                          int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
+                          int32_t x_row_div, void* stream);
+
+/*
  * w4_silu_mul -- SwiGLU between the expert projections (a reading: the
  * pages name the gate_up / down pair but not the activation):
  *   A[r, i] = bf16_rne( silu(H1[r, i]) * H1[r, I + i] ),  silu(v) = v/(1+e^-v)

@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4a16_gemm", "w4_pick_block_size",
-    "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm",
+    "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
 ]
 
@@ -180,6 +180,45 @@ def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padde
         _ptr(X), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, k, E, N, K, B,
         x_row_div, _stream(X)))
+    return out
+
+
+def w4a16_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                          T, k, B, x_row_div, out=None):
+    """gate_up projection with the SwiGLU fused into its epilogue.
+
+    Wq [E, 2I, K/8] / S [E, 2I, K/32] hold gate rows [0, I) and up rows
+    [I, 2I).  Row f of ``out`` [T*k, I] = bf16(silu(g) * u) with g, u the
+    bf16 gate and up products of X[f // x_row_div], i.e. exactly
+    w4_silu_mul(w4a16_moe_gemm(...)).  Other rows are not written.
+    """
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wq, "Wq", torch.int32, 3)
+    _need(S, "S", torch.bfloat16, 3)
+    E, N, kw = Wq.shape
+    K = kw * 8
+    if N % 2:
+        raise ValueError("Wq must hold 2I rows per expert")
+    I = N // 2
+    if X.shape[1] != K or tuple(S.shape) != (E, N, K // 32):
+        raise ValueError("shape mismatch between X, Wq and S")
+    if X.shape[0] != (T * k) // x_row_div:
+        raise ValueError("X must have T*k / x_row_div rows")
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, n, torch.int32)
+    cap = w4_moe_align_capacity(T, k, E, B)
+    if sorted_token_ids.numel() < cap or expert_ids.numel() < cap // B:
+        raise ValueError("alignment buffers are smaller than the capacity")
+    if out is None:
+        out = torch.empty((T * k, I), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * k * I:
+        raise ValueError("out must be [T*k, I]")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm_swiglu", lib.w4a16_moe_gemm_swiglu(
+        _ptr(X), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
     return out
 
 

@@ -26,6 +26,8 @@ SIGNATURES = {
     "moe_align_block_size": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
     "w4a16_moe_gemm": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32,
                                       _i64, _i64, _i32, _i32, _p]),
+    "w4a16_moe_gemm_swiglu": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32,
+                                             _i64, _i64, _i32, _i32, _p]),
     "w4_silu_mul": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
     "w4_moe_sum": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i64, _p]),
     "w4_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),

@@ -136,11 +136,35 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
       !aligned(num_tokens_post_padded, 4) || !aligned(topk_weights, 4))
     return W4_ERR_MISALIGNED;
-  const int64_t blocks = w4_moe_align_capacity(T, k, E, B) / B;
-  if (blocks > 65535) return W4_ERR_UNSUPPORTED;
+  if (w4::moe_gemm_slots(T, k, E, B) > 65535) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids,
                                         num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B,
                                         x_row_div, as_stream(stream)));
+}
+
+int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                          const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
+                          int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
+                          int32_t x_row_div, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || I < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
+  if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
+  if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
+  const int64_t N = 2 * I;
+  if (T * k + (int64_t)E * B >= kMaxI32 || N > kMaxI32 || K > kMaxI32 ||
+      (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (T == 0) return W4_OK;
+  if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !A)
+    return W4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2) || !aligned(A, 4) ||
+      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4))
+    return W4_ERR_MISALIGNED;
+  if (w4::moe_gemm_slots(T, k, E, B) > 65535) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids,
+                                               num_tokens_post_padded, A, T, k, E, I, K, B,
+                                               x_row_div, as_stream(stream)));
 }
 
 int w4_silu_mul(const uint16_t* H1, uint16_t* A, int64_t R, int64_t I, void* stream) {

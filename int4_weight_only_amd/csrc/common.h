@@ -98,6 +98,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 // ----------------------------------------------------------------- DPP ----
 
+// SwiGLU of one element, fp32: silu(g) * u = g / (1 + e^-g) * u.  One
+// definition for the standalone kernel and the fused GEMM epilogue, so both
+// round identically.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // Value from lane (l ^ 1) / (l ^ 2) inside each group of four lanes.
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
@@ -122,6 +129,13 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                            int32_t x_row_div, hipStream_t st);
+hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                                  const int32_t* sorted_ids, const int32_t* expert_ids,
+                                  const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
+                                  int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
+                                  hipStream_t st);
+// Workgroup slots along the grouped GEMM's second grid dimension.
+int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B);
 hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t B,
                         int64_t cap, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
                         hipStream_t st);

@@ -52,7 +52,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // activation row f / x_row_div, output row f.
 // SA: K is a multiple of 256, so a row's scales start 16-byte aligned and
 // eight of them are one 16-byte load.
-template <int BM, int WN, int NW, bool MOE, bool SA>
+// SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
+// take gate rows [c, c + 128) and waves 2, 3 the matching up rows, and the
+// epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
+template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
@@ -119,7 +122,9 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     tile_m = first_m + in_group % gm;
     tile_n = in_group / gm;
   }
-  const int n_base = tile_n * (NW * WN) + wave * WN;
+  static_assert(!SWI || (MOE && NW == 4), "fused SwiGLU: grouped product, four waves");
+  const int n_base = SWI ? (wave >> 1) * (N >> 1) + tile_n * (2 * WN) + (wave & 1) * WN
+                         : tile_n * (NW * WN) + wave * WN;
   const int G = K >> 5;
   const int kw = K >> 3;
 
@@ -380,24 +385,68 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
       // ---- epilogue: lane holds D[8*(v/4) + 4*h + v%4][l32] of each tile
+      if constexpr (SWI) {
+        // the up waves park bf16(up) in the activation stages (rows 0..63
+        // in stage 0, 64..127 in stage 1, 128 columns each); the gate waves
+        // combine it with their own bf16(gate)
+        const int I = N >> 1;
+        __syncthreads();   // every wave is done reading the activation stages
+        if (wave >= 2) {
 #pragma unroll
-      for (int ms = 0; ms < MSE; ++ms) {
+          for (int ms = 0; ms < MSE; ++ms) {
+            uint16_t* buf = ms < 2 ? xs0 : xs1;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int yr = orow[r];
-          if (yr < 0) continue;
-          float wgt = 1.0f;
-          if constexpr (MOE) {
-            if (topk_w != nullptr) wgt = topk_w[yr];
+            for (int v = 0; v < 16; ++v) {
+              const int r = (ms & 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns)
+                buf[r * (2 * WN) + (wave & 1) * WN + ns * 32 + l32] = to_bf16(acc[ms][ns][v]);
+            }
           }
+        }
+        __syncthreads();
+        if (wave < 2) {
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) {
-            const int n = n_base + ns * 32 + l32;
-            if (n < N) {
-              float y = acc[ms][ns][v];
-              if constexpr (MOE) y *= wgt;
-              Y[(int64_t)yr * N + n] = to_bf16(y);
+          for (int ms = 0; ms < MSE; ++ms) {
+            const uint16_t* buf = ms < 2 ? xs0 : xs1;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = (ms & 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+              const int yr = orow[ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+              if (yr < 0) continue;
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) {
+                const int c = wave * WN + ns * 32 + l32;
+                const int col = tile_n * (2 * WN) + c;
+                if (col < I) {
+                  const float g = bf16f(to_bf16(acc[ms][ns][v]));
+                  const float u = bf16f(buf[r * (2 * WN) + c]);
+                  Y[(int64_t)yr * I + col] = to_bf16(silu_mul(g, u));
+                }
+              }
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ms = 0; ms < MSE; ++ms) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int yr = orow[r];
+            if (yr < 0) continue;
+            float wgt = 1.0f;
+            if constexpr (MOE) {
+              if (topk_w != nullptr) wgt = topk_w[yr];
+            }
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+              const int n = n_base + ns * 32 + l32;
+              if (n < N) {
+                float y = acc[ms][ns][v];
+                if constexpr (MOE) y *= wgt;
+                Y[(int64_t)yr * N + n] = to_bf16(y);
+              }
             }
           }
         }
@@ -433,37 +482,65 @@ hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
   const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
   const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true>), grid, dim3(kNW * 64), 0, st, X,
-                       (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false>), grid, dim3(kNW * 64), 0,
+                       st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
   else
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false>), grid, dim3(kNW * 64), 0, st,
-                       X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false>), grid, dim3(kNW * 64), 0,
+                       st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
   return hipGetLastError();
 }
+
+// Slots (at most BM rows each: an alignment block, or one BM-row part of a
+// larger block), padded to whole rounds of one run's worth over the 8 XCDs.
+int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B) {
+  const int64_t cap = ((T * k + (int64_t)E * (B - 1) + B - 1) / B) * B;
+  const int64_t bpw = kBMMoe >= B ? kBMMoe / B : 1;
+  const int64_t ppb = B > kBMMoe ? (B + kBMMoe - 1) / kBMMoe : 1;   // slots per block
+  const int64_t slots = (cap / B) * ppb;
+  return (slots + 8 * bpw - 1) / (8 * bpw) * (8 * bpw);
+}
+
+namespace {
+template <bool SWI>
+hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
+                          int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
+                          int32_t x_row_div, hipStream_t st) {
+  // a fused SwiGLU workgroup covers 128 gate rows and the matching up rows
+  const int64_t ntn = SWI ? (N / 2 + 2 * kWN - 1) / (2 * kWN) : (N + kNW * kWN - 1) / (kNW * kWN);
+  const dim3 grid((unsigned)ntn, (unsigned)moe_gemm_slots(T, k, E, B));
+  const int n_pairs = (int)(T * k);
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st,
+                       X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
+                       ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+  else
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st,
+                       X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
+                       ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                            const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                            int32_t x_row_div, hipStream_t st) {
-  const int64_t n_pairs = T * k;
-  const int64_t cap = ((n_pairs + (int64_t)E * (B - 1) + B - 1) / B) * B;
-  const int64_t bpw = kBMMoe >= B ? kBMMoe / B : 1;
-  const int64_t ppb = B > kBMMoe ? (B + kBMMoe - 1) / kBMMoe : 1;   // slots per block
-  const int64_t slots = (cap / B) * ppb;
-  const dim3 grid((unsigned)((N + kNW * kWN - 1) / (kNW * kWN)),
-                  (unsigned)((slots + 8 * bpw - 1) / (8 * bpw) * (8 * bpw)));
-  if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true>), grid, dim3(kNW * 64), 0, st, X,
-                       (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
-                       topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
-  else
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false>), grid, dim3(kNW * 64), 0, st, X,
-                       (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids, ntpp,
-                       topk_w, (int)n_pairs, (int)B, (int)x_row_div, (int)E);
-  return hipGetLastError();
+  return launch_grouped<false>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N, K,
+                               B, x_row_div, st);
+}
+
+hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                                  const int32_t* sorted_ids, const int32_t* expert_ids,
+                                  const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
+                                  int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
+                                  hipStream_t st) {
+  return launch_grouped<true>(X, Wq, S, sorted_ids, expert_ids, ntpp, nullptr, A, T, k, E, 2 * I,
+                              K, B, x_row_div, st);
 }
 
 }  // namespace w4

@@ -244,8 +244,8 @@ __global__ __launch_bounds__(256) void k_silu_mul(const uint32_t* __restrict__ H
     const uint32_t g = H1[r * 2 * I2 + c];
     const uint32_t u = H1[r * 2 * I2 + I2 + c];
     const float g0 = bf16_lo(g), g1 = bf16_hi(g);
-    const float a0 = g0 / (1.0f + expf(-g0)) * bf16_lo(u);
-    const float a1 = g1 / (1.0f + expf(-g1)) * bf16_hi(u);
+    const float a0 = silu_mul(g0, bf16_lo(u));
+    const float a1 = silu_mul(g1, bf16_hi(u));
     A[i] = pk_bf16(a0, a1);
   }
 }

@@ -6,8 +6,8 @@ moe_align_block_size, the fused expert GEMMs):
 
     logits --w4_moe_route--> ids, weights
     ids --moe_align_block_size--> sorted_token_ids, expert_ids, ntpp
-    X --w4a16_moe_gemm (gate_up, x_row_div = k)--> H1 [T*k, 2I]
-    H1 --w4_silu_mul--> A [T*k, I]
+    X --w4a16_moe_gemm_swiglu (gate_up + SwiGLU, x_row_div = k)--> A [T*k, I]
+      (unfused: w4a16_moe_gemm --> H1 [T*k, 2I], then w4_silu_mul --> A)
     A --w4a16_moe_gemm (down, x_row_div = 1)--> H2 [T*k, H]
     H2, weights --w4_moe_sum--> Out [T, H]
 
@@ -21,7 +21,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
-               w4_pick_block_size, w4_quantize_pack, w4_silu_mul, w4a16_moe_gemm)
+               w4_pick_block_size, w4_quantize_pack, w4_silu_mul, w4a16_moe_gemm,
+               w4a16_moe_gemm_swiglu)
 
 
 @dataclass
@@ -66,28 +67,30 @@ class MoEBuffers:
     sorted_token_ids: torch.Tensor
     expert_ids: torch.Tensor
     ntpp: torch.Tensor
-    H1: torch.Tensor
+    H1: torch.Tensor            # None when the SwiGLU is fused into gate_up
     A: torch.Tensor
     H2: torch.Tensor
     out: torch.Tensor
 
 
-def alloc_buffers(T, k, E, H, I, B, device):
+def alloc_buffers(T, k, E, H, I, B, device, fused=True):
     cap = w4_moe_align_capacity(T, k, E, B)
     i32 = dict(dtype=torch.int32, device=device)
     bf = dict(dtype=torch.bfloat16, device=device)
+    H1 = None if fused else torch.empty((T * k, 2 * I), **bf)
     return MoEBuffers(torch.empty(cap, **i32), torch.empty(cap // B, **i32),
-                      torch.empty(1, **i32), torch.empty((T * k, 2 * I), **bf),
+                      torch.empty(1, **i32), H1,
                       torch.empty((T * k, I), **bf), torch.empty((T * k, H), **bf),
                       torch.empty((T, H), **bf))
 
 
-def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None):
+def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None, fused=True):
     """Expert part of the layer for routed tokens.
 
     X bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
     gate_up: E experts of [2I, H]; down: E experts of [H, I].  B defaults to
-    ``w4_pick_block_size``.  Returns (Out bf16 [T, H], buffers).
+    ``w4_pick_block_size``.  ``fused``: SwiGLU in the gate_up epilogue (the
+    result is the same bit for bit).  Returns (Out bf16 [T, H], buffers).
     """
     T, H = X.shape
     k = topk_ids.shape[1]
@@ -97,19 +100,25 @@ def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None):
         raise ValueError("expert weight shapes do not match X")
     if B is None:
         B = w4_pick_block_size(T, k, E)
-    b = buffers or alloc_buffers(T, k, E, H, I, B, X.device)
+    b = buffers or alloc_buffers(T, k, E, H, I, B, X.device, fused)
     moe_align_block_size(topk_ids, E, B, b.sorted_token_ids, b.expert_ids, b.ntpp)
-    w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
-                   T, k, B, k, out=b.H1)
-    w4_silu_mul(b.H1, out=b.A)
+    if fused:
+        w4a16_moe_gemm_swiglu(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids,
+                              b.ntpp, T, k, B, k, out=b.A)
+    else:
+        if b.H1 is None:
+            raise ValueError("the unfused path needs buffers with H1 (fused=False)")
+        w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
+                       T, k, B, k, out=b.H1)
+        w4_silu_mul(b.H1, out=b.A)
     w4a16_moe_gemm(b.A, down.Wq, down.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
                    T, k, B, 1, out=b.H2)
     w4_moe_sum(b.H2, topk_weights, T, k, out=b.out)
     return b.out, b
 
 
-def moe_layer(X, logits, k, gate_up, down, B=None, buffers=None):
+def moe_layer(X, logits, k, gate_up, down, B=None, buffers=None, fused=True):
     """Routing plus ``moe_forward``: logits fp32 [T, E] -> Out bf16 [T, H]."""
     ids, w = w4_moe_route(logits, k)
-    out, b = moe_forward(X, ids, w, gate_up, down, B, buffers)
+    out, b = moe_forward(X, ids, w, gate_up, down, B, buffers, fused)
     return out, ids, w, b

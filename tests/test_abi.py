@@ -189,6 +189,23 @@ def test_moe_gemm_validation(lib):
     assert f(*bad_tw, 4, 2, 8, 64, 64, 16, 1, None) == MISALIGNED
 
 
+def test_moe_gemm_swiglu_validation(lib):
+    f = lib.w4a16_moe_gemm_swiglu
+    good = [A16, A16, A2, A4, A4, A4, A4]
+    assert f(*good, 4, 2, 8, 32, 48, 16, 1, None) == SHAPE        # K % 32
+    assert f(*good, 4, 2, 8, 32, 64, 16, 3, None) == SHAPE        # x_row_div
+    assert f(*good, 4, 2, 8, 0, 64, 16, 1, None) == SHAPE         # I
+    assert f(*good, 4, 2, 8, 32, 64, 0, 1, None) == SHAPE         # B
+    assert f(*good, 4, 2, 2000, 32, 64, 16, 1, None) == UNSUPPORTED
+    assert f(*good, 0, 2, 8, 32, 64, 16, 1, None) == OK           # T == 0: no-op
+    bad_null = list(good)
+    bad_null[6] = None
+    assert f(*bad_null, 4, 2, 8, 32, 64, 16, 1, None) == NULL
+    bad_al = list(good)
+    bad_al[6] = A2
+    assert f(*bad_al, 4, 2, 8, 32, 64, 16, 1, None) == MISALIGNED
+
+
 def test_elementwise_validation(lib):
     assert lib.w4_silu_mul(A4, A4, 4, 3, None) == SHAPE
     assert lib.w4_silu_mul(None, A4, 4, 4, None) == NULL

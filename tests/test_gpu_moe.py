@@ -185,6 +185,37 @@ def test_moe_gemm_small(B, x_row_div_is_k, weighted):
     assert np.all(y[untouched] == CANARY)
 
 
+@pytest.mark.parametrize("I,K", [(48, 160), (200, 256), (128, 512)])
+@pytest.mark.parametrize("B", [4, 64, 200])
+@pytest.mark.parametrize("x_row_div_is_k", [True, False])
+def test_moe_gemm_swiglu_small(I, K, B, x_row_div_is_k):
+    """gate_up with the SwiGLU fused: equal bit for bit to the unfused pair
+    of calls, untouched rows unwritten, and within tolerance of the oracle."""
+    E, T, k = 5, 37, 3
+    say(f"moe_gemm_swiglu I={I} K={K} B={B} div_k={x_row_div_is_k}")
+    rng = np.random.default_rng(100 + B + I)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[1, 1] = -3                      # skipped pair
+    Wq, S, ref_w = small_experts(E, 2 * I, K, 41)
+    div = k if x_row_div_is_k else 1
+    Xb = synth.bits(synth.activations(T * k // div, K, 42))
+    X = up_bits(Xb)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    H1 = w4.w4a16_moe_gemm(X, Wq, S, s, e, n, T, k, B, div)
+    A_unfused = down_bits(w4.w4_silu_mul(H1))
+    A = canary_bf16((T * k, I))
+    w4.w4a16_moe_gemm_swiglu(X, Wq, S, s, e, n, T, k, B, div, out=A)
+    a = down_bits(A)
+    valid = [f for f in range(T * k) if 0 <= ids.flat[f] < E]
+    np.testing.assert_array_equal(a[valid], A_unfused[valid])
+    untouched = [f for f in range(T * k) if f not in valid]
+    assert np.all(a[untouched] == CANARY)
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    h = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, div, T * k)
+    ref = {f: omoe.silu(r[:I]) * r[I:] for f, r in h.items()}
+    assert_rows_close(a, ref, "moe swiglu small")
+
+
 def test_moe_gemm_one_expert_is_dense():
     """E = 1, k = 1: the grouped product is the dense product of all rows."""
     T, N, K = 300, 100, 544
@@ -247,7 +278,7 @@ def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
     for B in B_list:
         say(f"moe layer {name}: B={B}")
         s_ref, e_ref, n_ref = omoe.align(ids, E, B)
-        out, buf = wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B)
+        out, buf = wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B, fused=False)
         np.testing.assert_array_equal(down(buf.sorted_token_ids), s_ref)
         np.testing.assert_array_equal(down(buf.expert_ids), e_ref)
         assert int(down(buf.ntpp)[0]) == n_ref
@@ -255,6 +286,13 @@ def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
         ref = omoe.grouped_gemm(Xb, lambda e: ex.ref("gate_up", e), s_ref, e_ref, n_ref, B, k,
                                 T * k, experts=gu_experts)
         assert_rows_close(h1, ref, f"{name} gate_up B={B}")
+        # the fused gate_up + SwiGLU gives the unfused A bit for bit
+        a_unfused = down_bits(buf.A)
+        del buf
+        A = w4.w4a16_moe_gemm_swiglu(X, ex.gate_up.Wq, ex.gate_up.S, *map(
+            up, (s_ref, e_ref, np.array([n_ref], np.int32))), T, k, B, k)
+        np.testing.assert_array_equal(down_bits(A), a_unfused)
+        del A
     # down projection on its own, on seeded activations
     say(f"moe layer {name}: down projection")
     B = B_list[0]
