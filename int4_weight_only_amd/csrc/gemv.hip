@@ -143,7 +143,21 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
-    // ---- activations (issued first: the first wait is for them alone)
+    // ---- codes of every tile first, so the HBM stream starts at once (rows
+    // past the end read zero); a row's two chunks are adjacent requests (one
+    // 128-byte line)
+    u32x4 wv[T][kCPW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint32_t nl = (uint32_t)(t * 16 + n16);
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const int g = 4 * (c0 + cc) + kq;
+        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+      }
+    }
+    // ---- activations (L2 hits after the first CU's request)
     u32x4 xop[kCPW][4];
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc)
@@ -175,19 +189,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
         }
         sraw = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                      h[6] | (h[7] << 16)};
-      }
-    }
-    // ---- codes of every tile (rows past the end read zero); a row's two
-    // chunks are adjacent requests (one 128-byte line)
-    u32x4 wv[T][kCPW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint32_t nl = (uint32_t)(t * 16 + n16);
-#pragma unroll
-      for (int cc = 0; cc < kCPW; ++cc) {
-        const int g = 4 * (c0 + cc) + kq;
-        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
