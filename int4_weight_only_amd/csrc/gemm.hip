@@ -19,10 +19,10 @@
 // same K permutation, which leaves the sum unchanged.
 //
 // Pipeline: activations go straight from HBM into LDS (16-byte
-// buffer_load ... lds, STG stages, no staging registers); codes go to
-// registers STG steps ahead (STG register sets), scales in 8-step windows.
-// The K loop is unrolled by STG so that each step names its LDS stages
-// statically.
+// buffer_load ... lds, four stages: three steps ahead, no staging
+// registers); codes go to registers two steps ahead (two register sets),
+// scales in 8-step windows.  The K loop is unrolled by four so that each
+// step names its LDS stage and register set statically.
 // In LDS a 64-element activation row is 128 bytes; its eight 16-byte
 // pieces are stored XOR-swizzled by (row / 2) % 8 so that the MFMA
 // operand reads of 32 consecutive rows spread over the banks.  Every load
@@ -38,6 +38,8 @@ namespace w4 {
 namespace {
 
 constexpr int kStepK = 64;            // K per pipeline step (two groups)
+constexpr int kXS = 4;                // LDS activation stages (three steps ahead)
+constexpr int kWS = 2;                // code register sets (two steps ahead)
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past any buffer: reads 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -56,9 +58,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
 // take gate rows [c, c + 128) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
-// STG: LDS activation stages = code register sets (3 or 4); activations run
-// STG - 1 steps ahead, codes STG steps ahead.
-template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, int STG>
+template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   __shared__ __attribute__((aligned(16))) uint16_t xs0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t xs3[STG == 4 ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs3[STAGE];
   __shared__ int xrow[BM];     // activation row of each tile row (-1: none)
   __shared__ int orow[BM];     // output row of each tile row (-1: none)
   __shared__ int run_info[4];
@@ -186,8 +186,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
-  static_assert(STG == 3 || STG == 4, "stages");
-  const int nstepsp = (nsteps + STG - 1) / STG * STG;  // padded to the unroll; pad steps load zeros, skip MFMAs
+  const int nstepsp = (nsteps + kXS - 1) / kXS * kXS;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
@@ -305,8 +304,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     };
 
     // One step: wait for this step's activations and make them visible,
-    // start the stage STG - 1 ahead, dequantize, multiply, start the codes
-    // STG ahead.  MSE activation tiles are multiplied (rows past the tile read
+    // start the stage three ahead, dequantize, multiply, start the codes two
+    // ahead.  MSE activation tiles are multiplied (rows past the tile read
     // zero).  Per 16-wide K slice j all operand reads are issued first and
     // the MSE x NS MFMAs that follow are independent (no accumulator chain).
     u32x4 sraw[NS];            // scale window in flight
@@ -315,20 +314,23 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
                          u32x4 (&wreg)[NS], f32x16 (&acc)[decltype(mse)::value][NS])
         __attribute__((always_inline)) {
       constexpr int MSE = decltype(mse)::value;
-      // Loads issued after this step's activations: the codes of steps
-      // step + 1 .. step + STG - 1 (NS each) and the activations of steps
-      // step + 1 .. step + STG - 2 (XPW each), plus at times a scale window
-      // (waiting for fewer outstanding loads than were issued is only
-      // stricter).  Then a bare s_barrier:
-      // __syncthreads' release fence would also wait for the next stage's
-      // activation DMA, which nothing reads yet.  The empty asm statements
-      // keep LDS accesses on their side of the barrier.
-      constexpr int kAfter = (STG - 2) * XPW + (STG - 1) * NS;
+      // Wait until this wave's activations of this step have landed.  They
+      // were issued three steps ago; after them came, in steady state, the
+      // codes of steps step - 1 .. step + 1 (NS loads each) and the
+      // activations of steps step + 1, step + 2 (XPW each), in the first
+      // three steps one code set fewer.  Allowing 2 XPW + 2 NS loads in
+      // flight is therefore exact at the start and in steady state only
+      // also waits for the codes of step - 1, which that step consumed.
+      // Scale windows add loads, which only makes the wait stricter.  Then
+      // a bare s_barrier: __syncthreads' release fence would also wait for
+      // the later stages' DMA, which nothing reads yet.  The empty asm
+      // statements keep LDS accesses on their side of the barrier.
+      constexpr int kAfter = (kXS - 2) * XPW + kWS * NS;
       static_assert(kAfter <= 63, "vmcnt range");
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kAfter) : "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      load_x(step + STG - 1, st_next);
+      load_x(step + kXS - 1, st_next);
       if ((step & 7) == 0) {   // a new scale window: unpack it, fetch the next
         unpack_s(sraw, scw);
         load_s((step >> 3) + 1, sraw);
@@ -362,20 +364,16 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
             for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
         }
       }
-      load_w(step + STG, wreg);
+      load_w(step + kWS, wreg);
     };
 
-    u32x4 wa[NS], wb[NS], wc[NS], wd[STG == 4 ? NS : 1];
+    u32x4 wa[NS], wb[NS];
     load_x(0, xs0);
     load_w(0, wa);
     load_s(0, sraw);
     load_x(1, xs1);
     load_w(1, wb);
-    load_w(2, wc);
-    if constexpr (STG == 4) {
-      load_x(2, xs2);
-      load_w(3, wd);
-    }
+    load_x(2, xs2);
     // The steps and the epilogue, for MSE valid 32-row tiles
     // (accumulators of tiles that hold no valid row are never allocated).
     auto run_tile = [&](auto mse) __attribute__((always_inline)) {
@@ -387,19 +385,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
-      if constexpr (STG == 4) {
-        for (int step = 0; step < nstepsp; step += 4) {
-          step_body(mse, step + 0, xs0, xs3, wa, acc);
-          step_body(mse, step + 1, xs1, xs0, wb, acc);
-          step_body(mse, step + 2, xs2, xs1, wc, acc);
-          step_body(mse, step + 3, xs3, xs2, wd, acc);
-        }
-      } else {
-        for (int step = 0; step < nstepsp; step += 3) {
-          step_body(mse, step + 0, xs0, xs2, wa, acc);
-          step_body(mse, step + 1, xs1, xs0, wb, acc);
-          step_body(mse, step + 2, xs2, xs1, wc, acc);
-        }
+      for (int step = 0; step < nstepsp; step += 4) {
+        step_body(mse, step + 0, xs0, xs3, wa, acc);
+        step_body(mse, step + 1, xs1, xs0, wb, acc);
+        step_body(mse, step + 2, xs2, xs1, wa, acc);
+        step_body(mse, step + 3, xs3, xs2, wb, acc);
       }
       // drain the loads of the padding steps before LDS is reused
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -502,11 +492,11 @@ hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
   const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
   const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false, 4>), grid, dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false>), grid, dim3(kNW * 64), 0,
                        st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
   else
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false, 4>), grid, dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false>), grid, dim3(kNW * 64), 0,
                        st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
   return hipGetLastError();
@@ -534,11 +524,11 @@ hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* 
   const dim3 grid((unsigned)ntn, (unsigned)moe_gemm_slots(T, k, E, B));
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true, SWI, 3>), grid, dim3(kNW * 64), 0, st,
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st,
                        X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
                        ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   else
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false, SWI, 3>), grid, dim3(kNW * 64), 0, st,
+    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st,
                        X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
                        ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
