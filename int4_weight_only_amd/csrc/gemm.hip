@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     // the MSE x NS MFMAs that follow are independent (no accumulator chain).
     u32x4 sraw[NS];            // scale window in flight
     uint32_t scw[NS][4];       // scale window in use
-    auto step_body = [&](auto mse, int step, const uint16_t* st, uint16_t* st_next,
+    auto step_body = [&](auto mse, auto pos, int step, const uint16_t* st, uint16_t* st_next,
                          u32x4 (&wreg)[NS], f32x16 (&acc)[decltype(mse)::value][NS])
         __attribute__((always_inline)) {
       constexpr int MSE = decltype(mse)::value;
@@ -331,17 +331,20 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       load_x(step + kXS - 1, st_next);
-      if ((step & 7) == 0) {   // a new scale window: unpack it, fetch the next
+      // pos = step % 4 (static); the 8-step scale window's half is (step >> 2) & 1
+      constexpr int P = decltype(pos)::value;
+      if (P == 0 && (step & 4) == 0) {   // a new scale window: unpack it, fetch the next
         unpack_s(sraw, scw);
         load_s((step >> 3) + 1, sraw);
       }
       if (step < nsteps) {
-        const int t = step & 7;
+        // step t of the window uses the bf16 in half (t >= 4) of dword t % 4:
+        // one v_perm with a uniform selector moves it into the top half
+        const uint32_t hsel = (step & 4) ? 0x03020C0Cu : 0x01000C0Cu;
         DeqScale d[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          const uint32_t x = scw[ns][t & 3];
-          d[ns] = deq_scale((t & 4) ? bf16_hi(x) : bf16_lo(x));
+          d[ns] = deq_scale(__uint_as_float(__builtin_amdgcn_perm(0u, scw[ns][P], hsel)));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -386,10 +389,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
       for (int step = 0; step < nstepsp; step += 4) {
-        step_body(mse, step + 0, xs0, xs3, wa, acc);
-        step_body(mse, step + 1, xs1, xs0, wb, acc);
-        step_body(mse, step + 2, xs2, xs1, wa, acc);
-        step_body(mse, step + 3, xs3, xs2, wb, acc);
+        step_body(mse, std::integral_constant<int, 0>{}, step + 0, xs0, xs3, wa, acc);
+        step_body(mse, std::integral_constant<int, 1>{}, step + 1, xs1, xs0, wb, acc);
+        step_body(mse, std::integral_constant<int, 2>{}, step + 2, xs2, xs1, wa, acc);
+        step_body(mse, std::integral_constant<int, 3>{}, step + 3, xs3, xs2, wb, acc);
       }
       // drain the loads of the padding steps before LDS is reused
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
