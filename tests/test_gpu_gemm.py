@@ -75,6 +75,31 @@ def test_integer_exact(M):
     np.testing.assert_array_equal(y, gemm.to_bf16(exact))
 
 
+@pytest.mark.parametrize("M", [1, 8, 16, 17, 32, 33, 130])
+@pytest.mark.parametrize("K", [4640, 8192])
+def test_long_k(M, K):
+    """K above one 4096-wide decode pass (the pass partials carry in LDS);
+    4640 also leaves K / 32 off a multiple of 8 (unaligned scale rows)."""
+    run_case(M, 200, K, 7 * M + K, "long K")
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_integer_exact_two_passes(M):
+    """As test_integer_exact, with K = 8192: two decode K passes."""
+    N, K = 64, 8192
+    say(f"gemm integer-exact two passes M={M}")
+    rng = np.random.default_rng(1000 + M)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.float32)
+    q.reshape(N, K // 32, 32)[:, :, 5] = -7.0
+    Xi = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wb, Xb = bf16.rne(q), bf16.rne(Xi)
+    Wq, S, _, S_ref = quantized_pair(Wb)
+    assert np.all(bf16.to_f32(S_ref) == 1.0)
+    y = down_bits(w4.w4a16_gemm(up_bits(Xb), Wq, S))
+    exact = Xi.astype(np.float64) @ q.astype(np.float64).T
+    np.testing.assert_array_equal(y, gemm.to_bf16(exact))
+
+
 @pytest.mark.parametrize("M", [1, 8, 16, 32])
 def test_decode_full(M):
     wl = synth.WORKLOADS["decode"]
