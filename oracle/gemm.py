@@ -15,7 +15,7 @@ are compared to this within the stated tolerance.
 
 import numpy as np
 
-from . import bf16, quant
+from . import bf16, quant, quant_asym
 
 
 def dequant_f64(Wq, S):
@@ -32,6 +32,19 @@ def w4a16_gemm(X, Wq, S):
     """
     x = bf16.to_f32(X).astype(np.float64)
     w = dequant_f64(Wq, S)
+    return x @ w.T
+
+
+def w4a16_gemm_asym(X, Wq, S, Z):
+    """fp64 reference Y = X * w'^T with asymmetric weights
+    w' = bf16((q - z) * s) ("Quantization basics" §2.1 inverse map).
+
+    ``Wq`` int32 [N, K/8] unsigned codes; ``S`` bf16 bits [N, K/32];
+    ``Z`` uint8 [N, K/32].  Returns the unrounded float64 product.
+    """
+    x = bf16.to_f32(X).astype(np.float64)
+    q = quant_asym.unpack_unsigned(Wq)
+    w = bf16.to_f32(quant_asym.dequant_asym(q, S, Z)).astype(np.float64)
     return x @ w.T
 
 
