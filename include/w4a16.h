@@ -93,6 +93,34 @@ int w4_fake_quant(const uint16_t* W, int64_t N, int64_t K,
                   uint16_t* W_fq, void* stream);
 
 /*
+ * w4_quantize_pack_asym -- asymmetric (zero-point) group-wise INT4
+ * quantization + packing ([QB] §2.1 affine map, §2.3 asymmetric scale and
+ * zero point; [TAG] [11] 1 x 32 groups).  Unsigned grid [0, 15]; the range
+ * is widened to contain 0 (the zero-point bullet of [QB] §2.1: 0 is on
+ * the grid).  For each row n and group g:
+ *   lo = min(0, min w), hi = max(0, max w)                    (exact)
+ *   S[n, g] = bf16_rne( fp32(hi - lo) / 15 )                  (fp32 sub, IEEE div)
+ *   Z[n, g] = S == 0 ? 0 : clamp( rint_half_even(0 - lo / S), 0, 15 )
+ *   q = S == 0 ? 0 : clamp( rint_half_even(w / S) + Z, 0, 15 )
+ *   Wq packs the unsigned q along k (nibble j of word w holds k = 8w + j).
+ * W bf16 [N, K], 16-byte aligned, finite, with every group's hi - lo
+ * finite in fp32 (otherwise the codes are undefined).  Wq int32 [N, K/8],
+ * 16-byte aligned.  S bf16 [N, K/32], 2-byte aligned.  Z uint8 [N, K/32].
+ * K % 32 == 0.  Bit-exact with the definition above.
+ */
+int w4_quantize_pack_asym(const uint16_t* W, int64_t N, int64_t K,
+                          int32_t* Wq, uint16_t* S, uint8_t* Z, void* stream);
+
+/*
+ * w4_fake_quant_asym -- QAT forward with the asymmetric grid:
+ *   W_fq[n, k] = bf16_rne( (q[n, k] - Z[n, k/32]) * S[n, k/32] )
+ * with q, S, Z as w4_quantize_pack_asym computes them (the fp32 product is
+ * exact).  Layout, alignment and in-place rules as w4_fake_quant.
+ */
+int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K,
+                       uint16_t* W_fq, void* stream);
+
+/*
  * w4a16_gemm -- Y = X * dequant(Wq, S)^T ([RL] §4: INT4 weights, BF16
  * activations, dequantized in registers, BF16 matrix cores, fp32
  * accumulation).

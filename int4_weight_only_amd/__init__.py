@@ -19,7 +19,8 @@ import torch
 from . import _lib
 
 __all__ = [
-    "w4_quantize_pack", "w4_fake_quant", "w4a16_gemm", "w4_pick_block_size",
+    "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
+    "w4a16_gemm", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
 ]
@@ -83,6 +84,42 @@ def w4_fake_quant(W, out=None):
         raise ValueError("out size does not match W")
     lib = _lib.load()
     _lib.check("w4_fake_quant", lib.w4_fake_quant(_ptr(W), N, K, _ptr(out), _stream(W)))
+    return out
+
+
+def w4_quantize_pack_asym(W, Wq=None, S=None, Z=None):
+    """bf16 W [N, K] -> (Wq int32 [N, K/8] unsigned codes, S bf16 [N, K/32],
+    Z uint8 [N, K/32] zero points): asymmetric INT4 on the grid [0, 15]."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    if S is None:
+        S = torch.empty((N, K // 32), dtype=torch.bfloat16, device=W.device)
+    if Z is None:
+        Z = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
+    _need(Wq, "Wq", torch.int32)
+    _need(S, "S", torch.bfloat16)
+    _need(Z, "Z", torch.uint8)
+    if Wq.numel() != N * (K // 8) or S.numel() != N * (K // 32) or Z.numel() != N * (K // 32):
+        raise ValueError("output sizes do not match W")
+    lib = _lib.load()
+    _lib.check("w4_quantize_pack_asym", lib.w4_quantize_pack_asym(
+        _ptr(W), N, K, _ptr(Wq), _ptr(S), _ptr(Z), _stream(W)))
+    return Wq, S, Z
+
+
+def w4_fake_quant_asym(W, out=None):
+    """bf16 W [N, K] -> bf16 (q - z) * s on the asymmetric grid.  ``out`` may be W."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != W.numel():
+        raise ValueError("out size does not match W")
+    lib = _lib.load()
+    _lib.check("w4_fake_quant_asym", lib.w4_fake_quant_asym(_ptr(W), N, K, _ptr(out), _stream(W)))
     return out
 
 

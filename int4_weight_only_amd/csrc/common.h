@@ -119,7 +119,7 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
 // Implemented in the .hip files; called by api.hip after validation.
 namespace w4 {
 hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16_t* S,
-                           uint16_t* Wfq, bool fake, hipStream_t st);
+                           uint8_t* Z, uint16_t* Wfq, bool fake, bool asym, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,

@@ -1,4 +1,5 @@
-// Symmetric group-wise INT4 quantization, packing and fake quantization.
+// Group-wise INT4 quantization (symmetric, and asymmetric with a zero
+// point), packing and fake quantization.
 //
 // Method: "Quantization basics: from FP32 to INT4", §2.2 (z = 0,
 // s = max|w| / q_max, q = clamp(round(w / s))) and §5 (round half to even,
@@ -17,10 +18,16 @@
 
 namespace w4 {
 
-template <bool FAKE>
+// ASYM: "Quantization basics" §2.3 with the readings of the asymmetric
+// oracle: unsigned grid [0, 15], range widened to contain 0,
+// s = bf16(fp32(x_max - x_min) / 15), z = clamp(rint(-x_min / s), 0, 15),
+// q = clamp(rint(w / s) + z, 0, 15), dequant bf16((q - z) s); z is one byte
+// per group.  Every division is IEEE fp32, every rint half to even.
+template <bool FAKE, bool ASYM>
 __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, int64_t words,
                                                   uint32_t* __restrict__ Wq,
-                                                  uint16_t* __restrict__ S, u32x4* Wfq) {
+                                                  uint16_t* __restrict__ S,
+                                                  uint8_t* __restrict__ Z, u32x4* Wfq) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   // words % 4 == 0 and blocks start on multiples of 4, so a quad is either
   // entirely inside or entirely past the end: no DPP reads an exited lane.
@@ -28,31 +35,57 @@ __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, i
   const u32x4 v = W[i];
   const float w[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-  // For finite bf16, |w| orders like its 15-bit magnitude field.
-  uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-  a = max(a, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
-  a = max(a, quad_xor1(a));
-  a = max(a, quad_xor2(a));
-  const float amax = __uint_as_float(a << 16);
-  const uint16_t sb = to_bf16(amax / 7.0f);   // IEEE fp32 division, then RNE
-  const float s = bf16f(sb);
+  float s, zf = 0.0f;
+  uint16_t sb;
+  if constexpr (!ASYM) {
+    // For finite bf16, |w| orders like its 15-bit magnitude field.
+    uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+    a = max(a, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+    a = max(a, quad_xor1(a));
+    a = max(a, quad_xor2(a));
+    const float amax = __uint_as_float(a << 16);
+    sb = to_bf16(amax / 7.0f);                 // IEEE fp32 division, then RNE
+    s = bf16f(sb);
+  } else {
+    float lo = w[0], hi = w[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      lo = fminf(lo, w[j]);
+      hi = fmaxf(hi, w[j]);
+    }
+    lo = fminf(lo, __uint_as_float(quad_xor1(__float_as_uint(lo))));
+    hi = fmaxf(hi, __uint_as_float(quad_xor1(__float_as_uint(hi))));
+    lo = fminf(lo, __uint_as_float(quad_xor2(__float_as_uint(lo))));
+    hi = fmaxf(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
+    lo = fminf(lo, 0.0f);                      // the grid always holds 0
+    hi = fmaxf(hi, 0.0f);
+    sb = to_bf16((hi - lo) / 15.0f);           // fp32 subtraction, IEEE division, RNE
+    s = bf16f(sb);
+    zf = (s == 0.0f) ? 0.0f : fminf(fmaxf(rintf(0.0f - lo / s), 0.0f), 15.0f);
+  }
   float q[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float r = rintf(w[j] / s);         // IEEE division, half to even
-    q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r, -8.0f), 7.0f);
+    if constexpr (!ASYM)
+      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r, -8.0f), 7.0f);
+    else
+      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r + zf, 0.0f), 15.0f);
   }
   if constexpr (!FAKE) {
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) word |= ((uint32_t)(int)q[j] & 0xFu) << (4 * j);
     Wq[i] = word;
-    if ((i & 3) == 0) S[i >> 2] = sb;
+    if ((i & 3) == 0) {
+      S[i >> 2] = sb;
+      if constexpr (ASYM) Z[i >> 2] = (uint8_t)(int)zf;
+    }
   } else {
-    // q * s is exact in fp32; one rounding to bf16.  Adding +0 turns the
-    // -0 that rintf gives for small negative w into the code 0's +0.
+    // (q - z) * s is exact in fp32; one rounding to bf16.  Adding +0 turns
+    // the -0 that rintf gives for small negative w into the code's +0.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = q[j] + 0.0f;
+    for (int j = 0; j < 8; ++j) q[j] = (q[j] - zf) + 0.0f;
     u32x4 o;
     o.x = pk_bf16(q[0] * s, q[1] * s);
     o.y = pk_bf16(q[2] * s, q[3] * s);
@@ -63,14 +96,22 @@ __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, i
 }
 
 hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16_t* S,
-                           uint16_t* Wfq, bool fake, hipStream_t st) {
+                           uint8_t* Z, uint16_t* Wfq, bool fake, bool asym, hipStream_t st) {
   const int64_t blocks = (words + 255) / 256;
-  if (fake)
-    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const u32x4*)W, words, nullptr, nullptr, (u32x4*)Wfq);
+  const dim3 g((unsigned)blocks), b(256);
+  const u32x4* w = (const u32x4*)W;
+  if (fake && asym)
+    hipLaunchKernelGGL((k_quantize<true, true>), g, b, 0, st, w, words, nullptr, nullptr, nullptr,
+                       (u32x4*)Wfq);
+  else if (fake)
+    hipLaunchKernelGGL((k_quantize<true, false>), g, b, 0, st, w, words, nullptr, nullptr,
+                       nullptr, (u32x4*)Wfq);
+  else if (asym)
+    hipLaunchKernelGGL((k_quantize<false, true>), g, b, 0, st, w, words, (uint32_t*)Wq, S, Z,
+                       nullptr);
   else
-    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const u32x4*)W, words, (uint32_t*)Wq, S, nullptr);
+    hipLaunchKernelGGL((k_quantize<false, false>), g, b, 0, st, w, words, (uint32_t*)Wq, S,
+                       nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -125,6 +125,24 @@ def test_quantize_pack_validation(lib):
     assert f(A16, 4, 32, A16, A1, None) == MISALIGNED
 
 
+def test_quantize_pack_asym_validation(lib):
+    f = lib.w4_quantize_pack_asym
+    assert f(A16, 4, 33, A16, A2, A1, None) == SHAPE
+    assert f(None, 0, 32, None, None, None, None) == OK      # empty: no-op
+    assert f(A16, 4, 32, A16, A2, None, None) == NULL
+    assert f(A16, 4, 32, None, A2, A1, None) == NULL
+    assert f(A4, 4, 32, A16, A2, A1, None) == MISALIGNED
+    assert f(A16, 4, 32, A16, A1, A1, None) == MISALIGNED
+
+
+def test_fake_quant_asym_validation(lib):
+    f = lib.w4_fake_quant_asym
+    assert f(A16, 4, 48, A16, None) == SHAPE
+    assert f(None, 4, 32, A16, None) == NULL
+    assert f(A4, 4, 32, ctypes.c_void_p(0x20000), None) == MISALIGNED
+    assert f(ctypes.c_void_p(0x10000), 4, 32, ctypes.c_void_p(0x10010), None) == UNSUPPORTED
+
+
 def test_fake_quant_validation(lib):
     f = lib.w4_fake_quant
     assert f(A16, 4, 48, A16, None) == SHAPE
