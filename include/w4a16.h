@@ -129,10 +129,28 @@ int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K,
  * X  bf16 [M, K], 16-byte aligned.   Wq int32 [N, K/8], 16-byte aligned.
  * S  bf16 [N, K/32].                 Y  bf16 [M, N] output, 4-byte aligned.
  * K % 32 == 0; M, N >= 0 (M*N == 0 is a no-op); K == 0 writes zeros.
- * Small M (<= 32) runs the decode kernel, larger M the tiled MFMA kernel.
+ * Small M (<= 32, K <= 2^24) runs the decode kernel, larger M the tiled
+ * MFMA kernel, which needs X and Wq each below 2 GiB (32-bit buffer
+ * offsets): W4_ERR_UNSUPPORTED otherwise.
  */
 int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * w4a16_gemm_asym -- the same product with zero-point weights ([QB] §2.1
+ * inverse map x_hat = (q - z) s, §2.3 asymmetric quantization; [RL] §4
+ * for the mixed-precision product):
+ *   Y[m, n] = bf16_rne( sum_k X[m, k] * w'[n, k] )
+ *   w'[n, k] = bf16_rne( (q[n, k] - Z[n, k/32]) * S[n, k/32] )   (exact product)
+ * with q the unsigned nibbles of Wq, as w4_quantize_pack_asym writes them.
+ * Z uint8 [N, K/32], values in [0, 15] (other values: results undefined).
+ * Layout, alignment, size limits, dispatch and accumulation as w4a16_gemm.
+ * The decode kernel scales the exact integer sum of x (q - z) per group
+ * instead of rounding w' to bf16: within fp32 accumulation tolerance.
+ */
+int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                    const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                    void* stream);
 
 /*
  * w4_pick_block_size -- alignment block size from the token count and the
@@ -183,7 +201,8 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t T, int32_t k,
  * moe_align_block_size with the same T, k, E, B (device memory; the count
  * is read on the device, never by the host).
  * topk_weights float32 [T*k] or NULL.  K % 32 == 0, N >= 1, B in [1, 1024],
- * x_row_div in {1, k}.
+ * x_row_div in {1, k}.  X and one expert's Wq each below 2 GiB (32-bit
+ * buffer offsets), else W4_ERR_UNSUPPORTED.
  */
 int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,

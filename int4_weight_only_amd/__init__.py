@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
-    "w4a16_gemm", "w4_pick_block_size",
+    "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
 ]
@@ -141,6 +141,29 @@ def w4a16_gemm(X, Wq, S, out=None):
     lib = _lib.load()
     _lib.check("w4a16_gemm", lib.w4a16_gemm(_ptr(X), _ptr(Wq), _ptr(S), _ptr(out),
                                             M, N, K, _stream(X)))
+    return out
+
+
+def w4a16_gemm_asym(X, Wq, S, Z, out=None):
+    """Zero-point weights: Y [M, N] = X [M, K] * dequant_asym(Wq, S, Z)^T with
+    w' = bf16((q - z) s), q the unsigned codes of Wq and Z uint8 [N, K/32]."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wq, "Wq", torch.int32, 2)
+    _need(S, "S", torch.bfloat16, 2)
+    _need(Z, "Z", torch.uint8, 2)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] * 8 != K or tuple(S.shape) != (N, K // 32) or tuple(Z.shape) != (N, K // 32):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} Wq {tuple(Wq.shape)} "
+                         f"S {tuple(S.shape)} Z {tuple(Z.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out size does not match [M, N]")
+    lib = _lib.load()
+    _lib.check("w4a16_gemm_asym", lib.w4a16_gemm_asym(_ptr(X), _ptr(Wq), _ptr(S), _ptr(Z),
+                                                      _ptr(out), M, N, K, _stream(X)))
     return out
 
 

@@ -23,6 +23,21 @@ inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 constexpr int64_t kMaxI32 = 2147483647;
 
+// The kernels address operands with 32-bit raw-buffer offsets and use
+// offset 2^31 as "past the end" (reads zero): every buffer a kernel spans
+// must stay below 2^31 bytes.
+inline bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31); }
+
+// Decode path (M <= 32): per-workgroup weight buffers, X below 2^30 bytes.
+inline bool use_decode(int64_t M, int64_t K) { return M <= 32 && K <= ((int64_t)1 << 24); }
+
+// Tiled path: X [M, K] and the whole of Wq [N, K/8] in one buffer each,
+// and a 1-D grid of tiles.
+inline bool gemm_fits(int64_t M, int64_t N, int64_t K) {
+  return fits_buffer(M * K * 2) && fits_buffer(N * (K / 2)) &&
+         ((M + 127) / 128) * ((N + 255) / 256) < ((int64_t)1 << 31) - 8;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,11 +121,28 @@ int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t
   if (K == 0) return hip_status(w4::launch_zero_bf16(Y, M * N, as_stream(stream)));
   if (!X || !Wq || !S) return W4_ERR_NULL;
   if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
-  // decode kernel: 32-bit buffer offsets cover M * K * 2 <= 2^31 bytes of X
-  if (M <= 32 && K <= ((int64_t)1 << 24))
+  if (use_decode(M, K))
     return hip_status(w4::launch_gemv(X, Wq, S, Y, M, N, K, as_stream(stream)));
-  if (((M + 127) / 128) * ((N + 255) / 256) >= ((int64_t)1 << 31) - 8) return W4_ERR_UNSUPPORTED;
+  if (!gemm_fits(M, N, K)) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_gemm(X, Wq, S, Y, M, N, K, as_stream(stream)));
+}
+
+int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                    uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!Y) return W4_ERR_NULL;
+  if (!aligned(Y, 4)) return W4_ERR_MISALIGNED;
+  if (M > kMaxI32 || N > kMaxI32 || K > kMaxI32 || M * N > ((int64_t)1 << 40) ||
+      N * (K / 8) > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (!use_decode(M, K) && !gemm_fits(M, N, K)) return W4_ERR_UNSUPPORTED;
+  if (K == 0) return hip_status(w4::launch_zero_bf16(Y, M * N, as_stream(stream)));
+  if (!X || !Wq || !S || !Z) return W4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
+  if (use_decode(M, K))
+    return hip_status(w4::launch_gemv_zp(X, Wq, S, Z, Y, M, N, K, as_stream(stream)));
+  return hip_status(w4::launch_gemm_zp(X, Wq, S, Z, Y, M, N, K, as_stream(stream)));
 }
 
 int32_t w4_pick_block_size(int64_t T, int32_t k, int32_t E) {
@@ -156,6 +188,9 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
   if (T * k + (int64_t)E * B >= kMaxI32 || N > kMaxI32 || K > kMaxI32 ||
       (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
     return W4_ERR_UNSUPPORTED;
+  // one buffer spans X's rows, one an expert's Wq
+  if (!fits_buffer((T * k / x_row_div) * K * 2) || !fits_buffer(N * (K / 2)))
+    return W4_ERR_UNSUPPORTED;
   if (T == 0) return W4_OK;
   if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y)
     return W4_ERR_NULL;
@@ -180,6 +215,9 @@ int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* 
   const int64_t N = 2 * I;
   if (T * k + (int64_t)E * B >= kMaxI32 || N > kMaxI32 || K > kMaxI32 ||
       (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  // one buffer spans X's rows, one an expert's Wq
+  if (!fits_buffer((T * k / x_row_div) * K * 2) || !fits_buffer(N * (K / 2)))
     return W4_ERR_UNSUPPORTED;
   if (T == 0) return W4_OK;
   if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !A)

@@ -50,6 +50,13 @@ __device__ __forceinline__ DeqScale deq_scale(float s) {
   return {s, s * 0.0625f, -1032.0f * s, -72.0f * s};
 }
 
+// Zero-point codes (unsigned q in [0, 15], w' = bf16((q - z) s)): the same
+// operation without the nibble flip, with c0 = -(1024 + z) s and
+// c1 = -(64 + z) s (exact: at most 11 and 7 significant bits times s).
+__device__ __forceinline__ DeqScale deq_scale_zp(float s, float z) {
+  return {s, s * 0.0625f, -(1024.0f + z) * s, -(64.0f + z) * s};
+}
+
 // Eight INT4 codes of one packed word -> eight bf16 w' = bf16_rne(q * s),
 // in k order (element j of the word -> bf16 j of the result: word x holds
 // j = 0, 1, word y holds 2, 3, ...).
@@ -63,13 +70,17 @@ __device__ __forceinline__ DeqScale deq_scale(float s) {
 //   q * s; it is exact (a 4-bit integer times an 8-bit-mantissa scale fits
 //   in fp32), so the only rounding is the final bf16 one.
 // 17 VALU ops for 8 weights: one shift, four bitop3, eight fma_mix, four
-// v_cvt_pk_bf16_f32.
+// v_cvt_pk_bf16_f32.  UNSIGNED: zero-point codes, no flip (magic 1024 only)
+// and the constants of deq_scale_zp.
+template <bool UNSIGNED = false>
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, const DeqScale& d) {
+  constexpr uint32_t kLo = UNSIGNED ? 0x64006400u : 0x64086408u;   // 1024 (+ 8: flip)
+  constexpr uint32_t kHi = UNSIGNED ? 0x64006400u : 0x64806480u;   // 1024 (+ 128: flip)
   const uint32_t w8 = w >> 8;
-  const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) ^ 0x64086408u);   // j = 0, 4
-  const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) ^ 0x64806480u);   // j = 1, 5
-  const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) ^ 0x64086408u);  // j = 2, 6
-  const f16x2 e = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) ^ 0x64806480u);  // j = 3, 7
+  const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) ^ kLo);    // j = 0, 4
+  const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) ^ kHi);    // j = 1, 5
+  const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) ^ kLo);   // j = 2, 6
+  const f16x2 e = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) ^ kHi);   // j = 3, 7
   u32x4 r;
   r.x = pk_bf16(__builtin_fmaf((float)a.x, d.s, d.c0), __builtin_fmaf((float)b.x, d.s16, d.c1));
   r.y = pk_bf16(__builtin_fmaf((float)c.x, d.s, d.c0), __builtin_fmaf((float)e.x, d.s16, d.c1));
@@ -124,6 +135,13 @@ hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+// zero-point weights (unsigned codes, Z uint8 [N, K/32])
+hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st);
+hipError_t launch_gemv_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st);
 hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                            const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,

@@ -58,10 +58,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
 // take gate rows [c, c + 128) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
-template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI>
+// ZP (dense only): zero-point weights, unsigned codes and one zero point
+// byte per group in Z [N, K/32]; w' = bf16((q - z) s).
+template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
-    uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
     const float* __restrict__ topk_w, int n_pairs, int B, int x_row_div, int E) {
   constexpr int NT = NW * 64;
@@ -127,6 +129,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     tile_n = in_group / gm;
   }
   static_assert(!SWI || (MOE && NW == 4), "fused SwiGLU: grouped product, four waves");
+  static_assert(!ZP || !MOE, "zero points: dense product");
   const int n_base = SWI ? (wave >> 1) * (N >> 1) + tile_n * (2 * WN) + (wave & 1) * WN
                          : tile_n * (NW * WN) + wave * WN;
   const int G = K >> 5;
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
   const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
+  const __amdgpu_buffer_rsrc_t zr = rsrc(Z, ZP ? (uint32_t)N * (uint32_t)G : 0u);
 
   {
     // ---- row tables (thread r < BM fills row r)
@@ -284,6 +288,30 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         }
       }
     };
+    // Zero points in the same windows: lane (n, h) loads the 8 bytes of
+    // groups 16 u + 8 h .. + 7 (one 8-byte load when rows are 8-byte
+    // aligned, K % 256 == 0).
+    auto load_z = [&](int u, u32x2 (&raw)[NS]) __attribute__((always_inline)) {
+      const int g0 = 16 * u + 8 * h;
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
+        if constexpr (SA) {
+          const uint32_t zoff = (g0 < G) ? n * (uint32_t)G + (uint32_t)g0 : kOOB;
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, zoff, 0, 0);
+        } else {
+          uint32_t b[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int g = g0 + j;
+            const uint32_t zoff = (g < G) ? n * (uint32_t)G + (uint32_t)g : kOOB;
+            b[j] = __builtin_amdgcn_raw_buffer_load_b8(zr, zoff, 0, 0);
+          }
+          raw[ns] = u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                          b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+        }
+      }
+    };
     // Step t of the window uses group 2 t + h.  v_permlane32_swap hands each
     // lane its partner's (other h) raw dwords; v_perm keeps half h of both:
     // scw[ns][k] = (scale of step k, scale of step k + 4) as a bf16 pair.
@@ -302,6 +330,20 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         }
       }
     };
+    // zero points: steps 0..3 take bytes h, 2 + h, 4 + h, 6 + h of the
+    // h = 0 lane's 8 bytes, steps 4..7 the same bytes of the h = 1 lane's:
+    // zw[ns][t / 4] byte t % 4 = zero point of step t
+    const uint32_t byte_sel = h ? 0x07050301u : 0x06040200u;
+    auto unpack_z = [&](const u32x2 (&raw)[NS], uint32_t (&zw)[NS][2])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const auto p0 = __builtin_amdgcn_permlane32_swap(raw[ns].x, raw[ns].x, false, false);
+        const auto p1 = __builtin_amdgcn_permlane32_swap(raw[ns].y, raw[ns].y, false, false);
+        zw[ns][0] = __builtin_amdgcn_perm(p1[0], p0[0], byte_sel);
+        zw[ns][1] = __builtin_amdgcn_perm(p1[1], p0[1], byte_sel);
+      }
+    };
 
     // One step: wait for this step's activations and make them visible,
     // start the stage three ahead, dequantize, multiply, start the codes two
@@ -310,6 +352,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     // the MSE x NS MFMAs that follow are independent (no accumulator chain).
     u32x4 sraw[NS];            // scale window in flight
     uint32_t scw[NS][4];       // scale window in use
+    u32x2 zraw[NS];            // zero-point window in flight (ZP)
+    uint32_t zw[NS][2];        // zero-point window in use (ZP)
     auto step_body = [&](auto mse, auto pos, int step, const uint16_t* st, uint16_t* st_next,
                          u32x4 (&wreg)[NS], f32x16 (&acc)[decltype(mse)::value][NS])
         __attribute__((always_inline)) {
@@ -336,6 +380,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       if (P == 0 && (step & 4) == 0) {   // a new scale window: unpack it, fetch the next
         unpack_s(sraw, scw);
         load_s((step >> 3) + 1, sraw);
+        if constexpr (ZP) {
+          unpack_z(zraw, zw);
+          load_z((step >> 3) + 1, zraw);
+        }
       }
       if (step < nsteps) {
         // step t of the window uses the bf16 in half (t >= 4) of dword t % 4:
@@ -344,7 +392,13 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         DeqScale d[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          d[ns] = deq_scale(__uint_as_float(__builtin_amdgcn_perm(0u, scw[ns][P], hsel)));
+          const float sc = __uint_as_float(__builtin_amdgcn_perm(0u, scw[ns][P], hsel));
+          if constexpr (ZP) {
+            const uint32_t zd = (step & 4) ? zw[ns][1] : zw[ns][0];
+            d[ns] = deq_scale_zp(sc, (float)((zd >> (8 * P)) & 0xFFu));
+          } else {
+            d[ns] = deq_scale(sc);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -352,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
           u32x4 bop[NS];
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns)
-            bop[ns] = dequant8(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
+            bop[ns] = dequant8<ZP>(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
                                                                                 : wreg[ns].w,
                                d[ns]);
           u32x4 a[MSE];
@@ -374,6 +428,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     load_x(0, xs0);
     load_w(0, wa);
     load_s(0, sraw);
+    if constexpr (ZP) load_z(0, zraw);
     load_x(1, xs1);
     load_w(1, wb);
     load_x(2, xs2);
@@ -496,12 +551,28 @@ hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, 
   const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
   if (K % 256 == 0)
     hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false>), grid, dim3(kNW * 64), 0,
-                       st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       st, X, (const uint32_t*)Wq, S, nullptr, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
   else
     hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false>), grid, dim3(kNW * 64), 0,
-                       st, X, (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       st, X, (const uint32_t*)Wq, S, nullptr, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
                        nullptr, nullptr, 0, 1, 1, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st) {
+  const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
+  const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false, true>), grid,
+                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
+  else
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false, true>), grid,
+                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
   return hipGetLastError();
 }
 
@@ -528,11 +599,11 @@ hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* 
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
     hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st,
-                       X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
+                       X, (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
                        ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   else
     hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st,
-                       X, (const uint32_t*)Wq, S, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
+                       X, (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
                        ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
 }

@@ -35,6 +35,13 @@
 // group shared by the T tile MFMAs.  Per-wave partials meet in LDS (fixed
 // wave order, deterministic) once per K pass; each output is owned by one
 // thread.
+//
+// Zero-point weights (ZP; "Quantization basics: from FP32 to INT4" §2.1 and
+// §2.3, w' = (q - z) s with unsigned q): the code operand is 128 + q (no
+// flip), and the C operand of tile t's MFMA is X against the constant
+// column -(128 + z) of each weight row (bf16 0xC300 | z, exact), one MFMA
+// per tile and group, so the MFMA returns sum_k x_k (q_k - z) and the scale
+// step is unchanged.
 #include "common.h"
 
 namespace w4 {
@@ -74,8 +81,43 @@ __device__ __forceinline__ u32x4 x_slots(u32x4 d) {
 __device__ __forceinline__ uint32_t code_pair(uint32_t x) {
   return __builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x43084308u, 0x6A);
 }
+// unsigned codes: 128 + q, no flip (one v_and_or_b32)
+__device__ __forceinline__ uint32_t code_pair_u(uint32_t x) {
+  return (x & 0x000F000Fu) | 0x43004300u;
+}
+template <bool ZP>
 __device__ __forceinline__ u32x4 code_slots(uint32_t w) {
-  return u32x4{code_pair(w), code_pair(w >> 4), code_pair(w >> 8), code_pair(w >> 12)};
+  if constexpr (ZP)
+    return u32x4{code_pair_u(w), code_pair_u(w >> 4), code_pair_u(w >> 8), code_pair_u(w >> 12)};
+  else
+    return u32x4{code_pair(w), code_pair(w >> 4), code_pair(w >> 8), code_pair(w >> 12)};
+}
+
+// bf16 pair (-(128 + z), -(128 + z)) from byte J of a word of zero points
+template <int J>
+__device__ __forceinline__ uint32_t zp_offset_pair(uint32_t zw) {
+  constexpr uint32_t sel = 0x0C000C00u | ((uint32_t)J << 16) | (uint32_t)J;   // 0x0C: zero byte
+  return __builtin_amdgcn_perm(0u, zw, sel) | 0xC300C300u;
+}
+
+// This lane row's 8 zero points of weight row srow, groups g0 .. g0 + 7
+// (two dwords); the SALIGNED block is clamped into the row like the scales.
+template <bool SALIGNED>
+__device__ __forceinline__ u32x2 load_zp8(__amdgpu_buffer_rsrc_t zr, uint32_t srow, int g0, int G) {
+  if constexpr (SALIGNED) {
+    const uint32_t gb = (uint32_t)min(g0, G - 8);
+    return __builtin_amdgcn_raw_buffer_load_b64(zr, srow * (uint32_t)G + gb, 0, 0);
+  } else {
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int gj = g0 + j;
+      const uint32_t zoff = (gj < G) ? srow * (uint32_t)G + (uint32_t)gj : kOOB;
+      b[j] = __builtin_amdgcn_raw_buffer_load_b8(zr, zoff, 0, 0);
+    }
+    return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                 b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  }
 }
 
 // 4 x 4 transpose across the four 16-lane rows: on entry lane row r holds
@@ -112,10 +154,11 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
 // one row are one 16-byte load).  T: tiles of 16 weight rows per workgroup.
 // RM: rows of each lane's D fragment that are accumulated (for M = 1 only
 // row 0 of lane row 0 exists; the other rows are skipped).
-template <bool SALIGNED, int T, int RM>
+template <bool SALIGNED, int T, int RM, bool ZP>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
+                                                          const uint8_t* __restrict__ Z,
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 4 && (RM == 1 || RM == 4), "decode shape");
@@ -138,6 +181,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
   const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
+  const __amdgpu_buffer_rsrc_t zr =
+      rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
   const u32x4 neg136 = u32x4{kNeg136, kNeg136, kNeg136, kNeg136};
 
@@ -191,6 +236,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
                      h[6] | (h[7] << 16)};
       }
     }
+    u32x2 zraw = u32x2{0u, 0u};
+    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
 #pragma unroll
@@ -217,13 +264,30 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
       u32x4 u[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) u[t] = transpose_rows(wv[t][cc]);
+      uint32_t zc[T];                    // ZP: tile t's zero points of this chunk's groups
+      if constexpr (ZP) {
+        uint32_t b[4];
+        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[t] = b[t];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 cst = mfma16(xop[cc][j], neg136, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 cst = zero4;
+        if constexpr (!ZP) cst = mfma16(xop[cc][j], neg136, zero4);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const uint32_t word = j == 0 ? u[t].x : j == 1 ? u[t].y : j == 2 ? u[t].z : u[t].w;
-          const f32x4 d = mfma16(xop[cc][j], code_slots(word), cst);
+          f32x4 ct = cst;
+          if constexpr (ZP) {
+            const uint32_t zz = j == 0   ? zp_offset_pair<0>(zc[t])
+                                : j == 1 ? zp_offset_pair<1>(zc[t])
+                                : j == 2 ? zp_offset_pair<2>(zc[t])
+                                         : zp_offset_pair<3>(zc[t]);
+            ct = mfma16(xop[cc][j], u32x4{zz, zz, zz, zz}, zero4);
+          }
+          const f32x4 d = mfma16(xop[cc][j], code_slots<ZP>(word), ct);
           const uint32_t sp = sct[t][2 * cc + (j >> 1)];
           const float sc = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
 #pragma unroll
@@ -264,10 +328,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 // wave's LDS region (direct-to-LDS loads issued with the others) and is read
 // per group where it is used.  Each converted code word feeds the MFMAs of
 // both halves.  The region then takes the wave's partial sums.
-template <bool SALIGNED, int T>
+template <bool SALIGNED, int T, bool ZP>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
+                                                          const uint8_t* __restrict__ Z,
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 3, "decode shape");
@@ -292,6 +357,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
   const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
+  const __amdgpu_buffer_rsrc_t zr =
+      rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
   const u32x4 neg136 = u32x4{kNeg136, kNeg136, kNeg136, kNeg136};
 
@@ -333,6 +400,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
                      hw[6] | (hw[7] << 16)};
       }
     }
+    u32x2 zraw = u32x2{0u, 0u};
+    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
     // ---- codes of every tile (rows past the end read zero)
     u32x4 wv[T][kCPW];
 #pragma unroll
@@ -381,17 +450,38 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       u32x4 u[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) u[t] = transpose_rows(wv[t][cc]);
+      uint32_t zc[T];                    // ZP: tile t's zero points of this chunk's groups
+      if constexpr (ZP) {
+        uint32_t b[4];
+        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[t] = b[t];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 x1 = x_slots(*(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane]);
-        const f32x4 cst0 = mfma16(xop[cc][j], neg136, f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 cst1 = mfma16(x1, neg136, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 cst0 = zero4, cst1 = zero4;
+        if constexpr (!ZP) {
+          cst0 = mfma16(xop[cc][j], neg136, zero4);
+          cst1 = mfma16(x1, neg136, zero4);
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const uint32_t word = j == 0 ? u[t].x : j == 1 ? u[t].y : j == 2 ? u[t].z : u[t].w;
-          const u32x4 cs = code_slots(word);
-          const f32x4 d0 = mfma16(xop[cc][j], cs, cst0);
-          const f32x4 d1 = mfma16(x1, cs, cst1);
+          const u32x4 cs = code_slots<ZP>(word);
+          f32x4 ct0 = cst0, ct1 = cst1;
+          if constexpr (ZP) {
+            const uint32_t zz = j == 0   ? zp_offset_pair<0>(zc[t])
+                                : j == 1 ? zp_offset_pair<1>(zc[t])
+                                : j == 2 ? zp_offset_pair<2>(zc[t])
+                                         : zp_offset_pair<3>(zc[t]);
+            const u32x4 zop = u32x4{zz, zz, zz, zz};
+            ct0 = mfma16(xop[cc][j], zop, zero4);
+            ct1 = mfma16(x1, zop, zero4);
+          }
+          const f32x4 d0 = mfma16(xop[cc][j], cs, ct0);
+          const f32x4 d1 = mfma16(x1, cs, ct1);
           const uint32_t sp = sct[t][2 * cc + (j >> 1)];
           const float sc = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
 #pragma unroll
@@ -450,60 +540,75 @@ int cu_count() {
   return cus[dev];
 }
 
-template <bool SA, int T, int RM>
-hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                         int64_t M, int64_t N, int64_t K, hipStream_t st) {
+template <bool SA, int T, int RM, bool ZP>
+hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<SA, T, RM>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, X,
-                     (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_decode16<SA, T, RM, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                     st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, int RM>
-hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+template <bool SA, int RM, bool ZP>
+hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                        uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode16_t<SA, 1, RM>(X, Wq, S, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<SA, 2, RM>(X, Wq, S, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<SA, 3, RM>(X, Wq, S, Y, M, N, K, st);
-  return run_decode16_t<SA, 4, RM>(X, Wq, S, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode16_t<SA, 1, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<SA, 2, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<SA, 3, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<SA, 4, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-template <bool SA, int T>
-hipError_t run_decode32_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                         int64_t M, int64_t N, int64_t K, hipStream_t st) {
+template <bool SA, int T, bool ZP>
+hipError_t run_decode32_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode32<SA, T>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, X,
-                     (const uint32_t*)Wq, S, Y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_decode32<SA, T, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
+                     X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA>
-hipError_t run_decode32(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+template <bool SA, bool ZP>
+hipError_t run_decode32(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                        uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode32_t<SA, 1>(X, Wq, S, Y, M, N, K, st);
-  if (tpw == 2) return run_decode32_t<SA, 2>(X, Wq, S, Y, M, N, K, st);
-  return run_decode32_t<SA, 3>(X, Wq, S, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode32_t<SA, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode32_t<SA, 2, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode32_t<SA, 3, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+}
+
+template <bool ZP>
+hipError_t launch_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                         const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                         hipStream_t st) {
+  const bool sa = ((K >> 5) & 7) == 0;
+  if (M == 1)
+    return sa ? run_decode16<true, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st)
+              : run_decode16<false, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (M <= 16)
+    return sa ? run_decode16<true, 4, ZP>(X, Wq, S, Z, Y, M, N, K, st)
+              : run_decode16<false, 4, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  return sa ? run_decode32<true, ZP>(X, Wq, S, Z, Y, M, N, K, st)
+            : run_decode32<false, ZP>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const bool sa = ((K >> 5) & 7) == 0;
-  if (M == 1)
-    return sa ? run_decode16<true, 1>(X, Wq, S, Y, M, N, K, st)
-              : run_decode16<false, 1>(X, Wq, S, Y, M, N, K, st);
-  if (M <= 16)
-    return sa ? run_decode16<true, 4>(X, Wq, S, Y, M, N, K, st)
-              : run_decode16<false, 4>(X, Wq, S, Y, M, N, K, st);
-  return sa ? run_decode32<true>(X, Wq, S, Y, M, N, K, st)
-            : run_decode32<false>(X, Wq, S, Y, M, N, K, st);
+  return launch_decode<false>(X, Wq, S, nullptr, Y, M, N, K, st);
+}
+
+hipError_t launch_gemv_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st) {
+  return launch_decode<true>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 }  // namespace w4

@@ -167,6 +167,30 @@ def test_gemm_validation(lib):
     assert f(A16, A4, A2, A4, 4, 8, 32, None) == MISALIGNED
     assert f(A16, A16, A2, A2, 4, 8, 32, None) == MISALIGNED
     assert f(A16, A16, A2, A4, 1 << 40, 8, 32, None) == UNSUPPORTED
+    # the tiled kernel's 32-bit buffer offsets: X and Wq below 2 GiB each
+    assert f(A16, A16, A2, A4, 64, 8, 1 << 24, None) == UNSUPPORTED      # X = 2 GiB
+    assert f(A16, A16, A2, A4, 33, 8, 1 << 25, None) == UNSUPPORTED      # K above decode
+    assert f(A16, A16, A2, A4, 64, 1 << 20, 4096, None) == UNSUPPORTED   # Wq = 2 GiB
+
+
+def test_gemm_asym_validation(lib):
+    f = lib.w4a16_gemm_asym
+    assert f(A16, A16, A2, A1, A4, 4, 8, 40, None) == SHAPE
+    assert f(A16, A16, A2, A1, A4, 4, -1, 32, None) == SHAPE
+    assert f(None, None, None, None, None, 0, 8, 32, None) == OK    # M == 0
+    assert f(None, None, None, None, None, 4, 0, 32, None) == OK    # N == 0
+    assert f(None, A16, A2, A1, A4, 4, 8, 32, None) == NULL
+    assert f(A16, None, A2, A1, A4, 4, 8, 32, None) == NULL
+    assert f(A16, A16, None, A1, A4, 4, 8, 32, None) == NULL
+    assert f(A16, A16, A2, None, A4, 4, 8, 32, None) == NULL        # Z
+    assert f(A16, A16, A2, A1, None, 4, 8, 32, None) == NULL
+    assert f(A4, A16, A2, A1, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A4, A2, A1, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A1, A1, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A2, A1, A2, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A2, A1, A4, 1 << 40, 8, 32, None) == UNSUPPORTED
+    assert f(A16, A16, A2, A1, A4, 64, 8, 1 << 24, None) == UNSUPPORTED
+    assert f(A16, A16, A2, A1, A4, 64, 1 << 20, 4096, None) == UNSUPPORTED
 
 
 def test_align_validation(lib):
@@ -195,6 +219,9 @@ def test_moe_gemm_validation(lib):
     assert f(*good, 4, 0, 8, 64, 64, 16, 1, None) == SHAPE        # k
     assert f(*good, 4, 2, 8, 64, 64, 0, 1, None) == SHAPE         # B
     assert f(*good, 4, 2, 2000, 64, 64, 16, 1, None) == UNSUPPORTED
+    # X = 2^19 pair rows x 2048 = 2 GiB, within the grid's slot limit
+    assert f(*good, 1 << 16, 8, 8, 64, 2048, 1024, 1, None) == UNSUPPORTED
+    assert f(*good, 4, 2, 8, 1 << 20, 4096, 16, 1, None) == UNSUPPORTED   # an expert = 2 GiB
     assert f(*good, 0, 2, 8, 64, 64, 16, 1, None) == OK           # T == 0: no-op
     bad_null = list(good)
     bad_null[3] = None
@@ -215,6 +242,8 @@ def test_moe_gemm_swiglu_validation(lib):
     assert f(*good, 4, 2, 8, 0, 64, 16, 1, None) == SHAPE         # I
     assert f(*good, 4, 2, 8, 32, 64, 0, 1, None) == SHAPE         # B
     assert f(*good, 4, 2, 2000, 32, 64, 16, 1, None) == UNSUPPORTED
+    assert f(*good, 1 << 16, 8, 8, 32, 2048, 1024, 1, None) == UNSUPPORTED  # X = 2 GiB
+    assert f(*good, 4, 2, 8, 1 << 19, 4096, 16, 1, None) == UNSUPPORTED   # 2I rows = 2 GiB
     assert f(*good, 0, 2, 8, 32, 64, 16, 1, None) == OK           # T == 0: no-op
     bad_null = list(good)
     bad_null[6] = None
