@@ -19,7 +19,10 @@ under "detail": the prefill product (M = 4096, N = 14336, K = 4096,
 TFLOP/s), quantize + pack and fake quant of that weight (GB/s), and the two
 routed MoE layers (128 experts / top-8 / hidden 4096 / intermediate 1536 at
 256 tokens; 384 experts / top-8 / hidden 7168 / intermediate 2048 at 4096
-tokens with skewed routing), per stage and whole layer.
+tokens with skewed routing), per stage and whole layer; and under
+"asym" the zero-point variants: the decode sweep and the prefill product
+with zero-point weights (one uint8 zero point per group on top of the
+scale), asymmetric quantize + pack and fake quant.
 
 The CPU oracle is timed on this host on one full decode step (the same
 four products over the same weight shape), as a reported baseline.
@@ -44,9 +47,11 @@ ROTATE = 24
 SETTLE_MS = 150.0     # sustained untimed load before each timed region
 
 
-def decode_bytes(M, N=DECODE_N, K=DECODE_K):
-    """Algorithmic bytes of one decode product: codes + scales + X + Y."""
-    return N * K // 2 + 2 * N * (K // 32) + 2 * M * K + 2 * M * N
+def decode_bytes(M, N=DECODE_N, K=DECODE_K, zero_points=False):
+    """Algorithmic bytes of one decode product: codes + scales (+ zero
+    points) + X + Y."""
+    zp = N * (K // 32) if zero_points else 0
+    return N * K // 2 + 2 * N * (K // 32) + zp + 2 * M * K + 2 * M * N
 
 
 def gemm_flops(M, N, K):
@@ -58,7 +63,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--sections", default="decode,prefill,quant,moe_qwen,moe_kimi")
+    p.add_argument("--sections", default="decode,prefill,quant,moe_qwen,moe_kimi,asym")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args()
 
@@ -183,6 +188,60 @@ def bench_quant(w4, synth, torch, iters, timer):
     fq_bytes = 4 * N * K
     for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
                              ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes)):
+        timer.settle(fn, SETTLE_MS / 3)
+        t = timer.run(fn, iters) / iters
+        gbs = nbytes / (t * 1e-3) / 1e9
+        out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "bytes": nbytes,
+                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def bench_asym(w4, synth, torch, steps, warmup, iters, timer):
+    """Zero-point weights: decode per M (rotating weight copies as in the
+    headline sweep), the prefill product, asymmetric quantize + pack and
+    fake quant."""
+    dev = torch.device("cuda")
+    out = {}
+    src = synth.weights(DECODE_N, DECODE_K, synth.WORKLOADS["decode"]["seed"], device=dev)
+    Wq0, S0, Z0 = w4.w4_quantize_pack_asym(src)
+    del src
+    ws = [(Wq0, S0, Z0)] + [(Wq0.clone(), S0.clone(), Z0.clone()) for _ in range(ROTATE - 1)]
+    per_m = {}
+    for M in DECODE_MS:
+        X = synth.activations(M, DECODE_K, 1, device=dev)
+        Y = torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev)
+
+        def one(i, X=X, Y=Y):
+            Wq, S, Z = ws[i % ROTATE]
+            w4.w4a16_gemm_asym(X, Wq, S, Z, out=Y)
+        timer.run(one, warmup)
+        timer.settle(one, SETTLE_MS / 3)
+        t = timer.run(one, steps) / steps
+        nb = decode_bytes(M, zero_points=True)
+        per_m[str(M)] = {"us": round(t * 1e3, 3), "GB/s": round(nb / (t * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["decode_per_M"] = per_m
+    del ws, Wq0, S0, Z0
+
+    wl = synth.WORKLOADS["prefill"]
+    M, N, K = wl["M"][0], wl["N"], wl["K"]
+    W = synth.weights(N, K, wl["seed"], device=dev)
+    X = synth.activations(M, K, wl["seed"], device=dev)
+    Wq, S, Z = w4.w4_quantize_pack_asym(W)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    f = lambda i: w4.w4a16_gemm_asym(X, Wq, S, Z, out=Y)
+    timer.settle(f)
+    t = timer.run(f, iters) / iters
+    tf = gemm_flops(M, N, K) / (t * 1e-3) / 1e12
+    out["prefill"] = {"M": M, "N": N, "K": K, "us": round(t * 1e3, 1), "TFLOP/s": round(tf, 1),
+                      "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    Wf = torch.empty_like(W)
+    qp_bytes = 2 * N * K + N * K // 2 + 3 * N * (K // 32)
+    fq_bytes = 4 * N * K
+    for name, fn, nbytes in (
+            ("quantize_pack_asym", lambda i: w4.w4_quantize_pack_asym(W, Wq, S, Z), qp_bytes),
+            ("fake_quant_asym", lambda i: w4.w4_fake_quant_asym(W, Wf), fq_bytes)):
         timer.settle(fn, SETTLE_MS / 3)
         t = timer.run(fn, iters) / iters
         gbs = nbytes / (t * 1e-3) / 1e9
@@ -347,6 +406,10 @@ def main():
         if name in sections:
             log(f"bench: {name}")
             detail[name] = bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer)
+
+    if "asym" in sections:
+        log("bench: zero-point variants")
+        detail["asym"] = bench_asym(w4, synth, torch, args.steps, args.warmup, iters, timer)
 
     cpu = None
     if not args.no_cpu_baseline:
