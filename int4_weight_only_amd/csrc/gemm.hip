@@ -20,9 +20,11 @@
 //
 // Pipeline: activations go straight from HBM into LDS (16-byte
 // buffer_load ... lds, four stages: three steps ahead, no staging
-// registers); codes go to registers two steps ahead (two register sets),
-// scales in 8-step windows.  The K loop is unrolled by four so that each
-// step names its LDS stage and register set statically.
+// registers); codes go to registers two steps ahead (two register sets;
+// four for the 32-row tile, whose few MFMAs per step leave the weight
+// stream latency-bound), scales in 8-step windows.  The K loop is unrolled
+// by four so that each step names its LDS stage and register set
+// statically.
 // In LDS a 64-element activation row is 128 bytes; its eight 16-byte
 // pieces are stored XOR-swizzled by (row / 2) % 8 so that the MFMA
 // operand reads of 32 consecutive rows spread over the banks.  Every load
@@ -39,7 +41,6 @@ namespace {
 
 constexpr int kStepK = 64;            // K per pipeline step (two groups)
 constexpr int kXS = 4;                // LDS activation stages (three steps ahead)
-constexpr int kWS = 2;                // code register sets (two steps ahead)
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past any buffer: reads 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -60,8 +61,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
 // ZP (dense only): zero-point weights, unsigned codes and one zero point
 // byte per group in Z [N, K/32]; w' = bf16((q - z) s).
+// BM = 32 (one MFMA row tile, small expert blocks): four code register sets
+// and four workgroups per CU keep more weight bytes in flight.
 template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false>
-__global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
+__global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
   constexpr int XI = BM / 8;           // 1 KB direct-to-LDS loads per activation stage
   constexpr int XPW = XI / NW;         // ... issued by each wave
   constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage
+  constexpr int kWS = BM <= 32 ? 4 : 2;   // code register sets (steps ahead)
   static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
   // separately declared stages: each DMA target and each operand read names
@@ -359,17 +363,19 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         __attribute__((always_inline)) {
       constexpr int MSE = decltype(mse)::value;
       // Wait until this wave's activations of this step have landed.  They
-      // were issued three steps ago; after them came, in steady state, the
-      // codes of steps step - 1 .. step + 1 (NS loads each) and the
-      // activations of steps step + 1, step + 2 (XPW each), in the first
-      // three steps one code set fewer.  Allowing 2 XPW + 2 NS loads in
-      // flight is therefore exact at the start and in steady state only
-      // also waits for the codes of step - 1, which that step consumed.
-      // Scale windows add loads, which only makes the wait stricter.  Then
+      // were issued three steps ago; after them came, in steady state, three
+      // code sets (NS loads each: steps step + kWS - 3 .. step + kWS - 1)
+      // and the activations of steps step + 1, step + 2 (XPW each).  With
+      // two register sets the prologue has one code set fewer in the first
+      // steps, so 2 XPW + 2 NS loads may stay in flight (in steady state
+      // this also waits for the codes of step - 1, which that step
+      // consumed); with four sets the prologue has more, and steady state
+      // allows 2 XPW + 3 NS.  Scale and zero-point windows add loads, which
+      // only makes the wait stricter.  Then
       // a bare s_barrier: __syncthreads' release fence would also wait for
       // the later stages' DMA, which nothing reads yet.  The empty asm
       // statements keep LDS accesses on their side of the barrier.
-      constexpr int kAfter = (kXS - 2) * XPW + kWS * NS;
+      constexpr int kAfter = (kXS - 2) * XPW + (kWS < 3 ? kWS : 3) * NS;
       static_assert(kAfter <= 63, "vmcnt range");
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kAfter) : "memory");
       __builtin_amdgcn_s_barrier();
@@ -424,14 +430,16 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
       load_w(step + kWS, wreg);
     };
 
-    u32x4 wa[NS], wb[NS];
+    u32x4 wset[kWS][NS];       // code register sets: step t uses set t % kWS
     load_x(0, xs0);
-    load_w(0, wa);
+    load_w(0, wset[0]);
     load_s(0, sraw);
     if constexpr (ZP) load_z(0, zraw);
     load_x(1, xs1);
-    load_w(1, wb);
+    load_w(1, wset[1]);
     load_x(2, xs2);
+#pragma unroll
+    for (int i = 2; i < kWS; ++i) load_w(i, wset[i]);
     // The steps and the epilogue, for MSE valid 32-row tiles
     // (accumulators of tiles that hold no valid row are never allocated).
     auto run_tile = [&](auto mse) __attribute__((always_inline)) {
@@ -444,31 +452,39 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
       for (int step = 0; step < nstepsp; step += 4) {
-        step_body(mse, std::integral_constant<int, 0>{}, step + 0, xs0, xs3, wa, acc);
-        step_body(mse, std::integral_constant<int, 1>{}, step + 1, xs1, xs0, wb, acc);
-        step_body(mse, std::integral_constant<int, 2>{}, step + 2, xs2, xs1, wa, acc);
-        step_body(mse, std::integral_constant<int, 3>{}, step + 3, xs3, xs2, wb, acc);
+        step_body(mse, std::integral_constant<int, 0>{}, step + 0, xs0, xs3, wset[0 % kWS], acc);
+        step_body(mse, std::integral_constant<int, 1>{}, step + 1, xs1, xs0, wset[1 % kWS], acc);
+        step_body(mse, std::integral_constant<int, 2>{}, step + 2, xs2, xs1, wset[2 % kWS], acc);
+        step_body(mse, std::integral_constant<int, 3>{}, step + 3, xs3, xs2, wset[3 % kWS], acc);
       }
       // drain the loads of the padding steps before LDS is reused
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
       // ---- epilogue: lane holds D[8*(v/4) + 4*h + v%4][l32] of each tile
       if constexpr (SWI) {
-        // the up waves park bf16(up) in the activation stages (rows 0..63
-        // in stage 0, 64..127 in stage 1, 128 columns each); the gate waves
-        // combine it with their own bf16(gate)
+        // the up waves park bf16(up) in the activation stages; the gate
+        // waves combine it with their own bf16(gate).  Up wave u's element
+        // (tile ms, row rl, column cw): for BM = 128 rows 0..63 in stage 0,
+        // 64..127 in stage 1, 128 columns each; for BM = 32 stage u holds
+        // that wave's 32 x 64 block.
         const int I = N >> 1;
+        auto park = [&](int ms, int rl, int u, int cw) __attribute__((always_inline)) {
+          if constexpr (BM == 32)
+            return (u ? xs1 : xs0) + rl * WN + cw;
+          else
+            return (ms < 2 ? xs0 : xs1) + ((ms & 1) * 32 + rl) * (2 * WN) + u * WN + cw;
+        };
+        static_assert(BM == 32 || BM == 128, "parking layout");
         __syncthreads();   // every wave is done reading the activation stages
         if (wave >= 2) {
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms) {
-            uint16_t* buf = ms < 2 ? xs0 : xs1;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int r = (ms & 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+              const int rl = 8 * (v >> 2) + 4 * h + (v & 3);
 #pragma unroll
               for (int ns = 0; ns < NS; ++ns)
-                buf[r * (2 * WN) + (wave & 1) * WN + ns * 32 + l32] = to_bf16(acc[ms][ns][v]);
+                *park(ms, rl, wave & 1, ns * 32 + l32) = to_bf16(acc[ms][ns][v]);
             }
           }
         }
@@ -476,11 +492,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
         if (wave < 2) {
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms) {
-            const uint16_t* buf = ms < 2 ? xs0 : xs1;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int r = (ms & 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-              const int yr = orow[ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+              const int rl = 8 * (v >> 2) + 4 * h + (v & 3);
+              const int yr = orow[ms * 32 + rl];
               if (yr < 0) continue;
 #pragma unroll
               for (int ns = 0; ns < NS; ++ns) {
@@ -488,7 +503,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
                 const int col = tile_n * (2 * WN) + c;
                 if (col < I) {
                   const float g = bf16f(to_bf16(acc[ms][ns][v]));
-                  const float u = bf16f(buf[r * (2 * WN) + c]);
+                  const float u = bf16f(*park(ms, rl, wave, ns * 32 + l32));
                   Y[(int64_t)yr * I + col] = to_bf16(silu_mul(g, u));
                 }
               }
@@ -523,15 +538,19 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : 2) void k_gemm(
     if constexpr (MOE) {
       // MFMA row tiles that hold valid rows (a run of one expert is often
       // a single 32-row tile; a run of 85 rows padded to 128 needs three)
-      static_assert(MS == 4, "one instantiation per row-tile count");
-      if (ms_valid == 1)
+      static_assert(MS == 1 || MS == 4, "one instantiation per row-tile count");
+      if constexpr (MS == 1) {
         run_tile(std::integral_constant<int, 1>{});
-      else if (ms_valid == 2)
-        run_tile(std::integral_constant<int, 2>{});
-      else if (ms_valid == 3)
-        run_tile(std::integral_constant<int, 3>{});
-      else
-        run_tile(std::integral_constant<int, 4>{});
+      } else {
+        if (ms_valid == 1)
+          run_tile(std::integral_constant<int, 1>{});
+        else if (ms_valid == 2)
+          run_tile(std::integral_constant<int, 2>{});
+        else if (ms_valid == 3)
+          run_tile(std::integral_constant<int, 3>{});
+        else
+          run_tile(std::integral_constant<int, 4>{});
+      }
     } else {
       run_tile(std::integral_constant<int, MS>{});
     }
@@ -542,7 +561,17 @@ namespace {
 constexpr int kWN = 64;
 constexpr int kNW = 4;
 constexpr int kBMDense = 128;   // dense prefill tile rows (two workgroups per CU)
-constexpr int kBMMoe = 128;     // expert blocks are 16..64 rows: a smaller tile pads less
+constexpr int kBMMoe = 128;     // expert blocks of 64 rows and more
+constexpr int kBMMoeSmall = 32; // expert blocks of 32 rows or fewer (few rows per expert)
+#ifndef W4_WN_SMALL
+#define W4_WN_SMALL 32
+#endif
+constexpr int kWNMoeSmall = W4_WN_SMALL;   // weight rows per wave of the 32-row tile
+
+// Tile rows of the grouped product for alignment block size B: with blocks
+// of at most 32 rows an expert holds few rows, the product streams weights,
+// and the 32-row tile keeps more of them in flight.
+int64_t moe_tile_rows(int32_t B) { return B <= kBMMoeSmall ? kBMMoeSmall : kBMMoe; }
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
@@ -579,33 +608,47 @@ hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* 
 // Slots (at most BM rows each: an alignment block, or one BM-row part of a
 // larger block), padded to whole rounds of one run's worth over the 8 XCDs.
 int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B) {
+  const int64_t bm = moe_tile_rows(B);
   const int64_t cap = ((T * k + (int64_t)E * (B - 1) + B - 1) / B) * B;
-  const int64_t bpw = kBMMoe >= B ? kBMMoe / B : 1;
-  const int64_t ppb = B > kBMMoe ? (B + kBMMoe - 1) / kBMMoe : 1;   // slots per block
+  const int64_t bpw = bm >= B ? bm / B : 1;
+  const int64_t ppb = B > bm ? (B + bm - 1) / bm : 1;   // slots per block
   const int64_t slots = (cap / B) * ppb;
   return (slots + 8 * bpw - 1) / (8 * bpw) * (8 * bpw);
 }
 
 namespace {
+template <int BM, int WN, bool SWI>
+hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
+                          int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
+                          int32_t x_row_div, hipStream_t st) {
+  // a fused SwiGLU workgroup covers 2 WN gate rows and the matching up rows
+  const int64_t ntn = SWI ? (N / 2 + 2 * WN - 1) / (2 * WN) : (N + kNW * WN - 1) / (kNW * WN);
+  const dim3 grid((unsigned)ntn, (unsigned)moe_gemm_slots(T, k, E, B));
+  const int n_pairs = (int)(T * k);
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids,
+                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+  else
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids,
+                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+  return hipGetLastError();
+}
+
 template <bool SWI>
 hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                           int32_t x_row_div, hipStream_t st) {
-  // a fused SwiGLU workgroup covers 128 gate rows and the matching up rows
-  const int64_t ntn = SWI ? (N / 2 + 2 * kWN - 1) / (2 * kWN) : (N + kNW * kWN - 1) / (kNW * kWN);
-  const dim3 grid((unsigned)ntn, (unsigned)moe_gemm_slots(T, k, E, B));
-  const int n_pairs = (int)(T * k);
-  if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st,
-                       X, (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
-                       ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
-  else
-    hipLaunchKernelGGL((k_gemm<kBMMoe, kWN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st,
-                       X, (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids, expert_ids,
-                       ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
-  return hipGetLastError();
+  if (moe_tile_rows(B) == kBMMoeSmall)
+    return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y,
+                                              T, k, E, N, K, B, x_row_div, st);
+  return launch_grouped_t<kBMMoe, kWN, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k,
+                                       E, N, K, B, x_row_div, st);
 }
 }  // namespace
 

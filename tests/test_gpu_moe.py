@@ -158,10 +158,12 @@ def small_experts(E, N, K, seed):
     return Wq, S, (lambda e: ref[e])
 
 
-@pytest.mark.parametrize("B", [1, 4, 16, 64, 200])
+@pytest.mark.parametrize("B", [1, 4, 16, 20, 32, 64, 200])
 @pytest.mark.parametrize("x_row_div_is_k", [True, False])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_moe_gemm_small(B, x_row_div_is_k, weighted):
+    """Blocks of at most 32 rows run the 32-row tile (runs of 32 / B
+    blocks), larger ones the 128-row tile (B = 200: two slots per block)."""
     E, T, k, N, K = 6, 40, 3, 96, 160
     say(f"moe_gemm small B={B} div_k={x_row_div_is_k} weighted={weighted}")
     rng = np.random.default_rng(B)
@@ -186,7 +188,7 @@ def test_moe_gemm_small(B, x_row_div_is_k, weighted):
 
 
 @pytest.mark.parametrize("I,K", [(48, 160), (200, 256), (128, 512)])
-@pytest.mark.parametrize("B", [4, 64, 200])
+@pytest.mark.parametrize("B", [4, 32, 64, 200])
 @pytest.mark.parametrize("x_row_div_is_k", [True, False])
 def test_moe_gemm_swiglu_small(I, K, B, x_row_div_is_k):
     """gate_up with the SwiGLU fused: equal bit for bit to the unfused pair
