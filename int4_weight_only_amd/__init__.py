@@ -30,7 +30,16 @@ def library_path():
     return _lib.LIB_PATH
 
 
+# The current stream's raw handle for a device index.  torch's private
+# accessor costs ~0.1 us per call where torch.cuda.current_stream(...).cuda_stream
+# costs ~3 us: at M = 1 a decode product runs ~8 us on the GPU, so the host
+# side of a call must stay well below that.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t):
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
     return ctypes_void(torch.cuda.current_stream(t.device).cuda_stream)
 
 

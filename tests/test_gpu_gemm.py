@@ -146,3 +146,22 @@ def test_k_zero_writes_zeros_and_m_zero_is_noop():
     Wq0 = torch.zeros((5, 8), dtype=torch.int32, device="cuda")
     S0 = torch.zeros((5, 2), dtype=torch.bfloat16, device="cuda")
     assert w4.w4a16_gemm(X0, Wq0, S0).shape == (0, 5)
+
+
+def test_binding_uses_the_current_stream():
+    """The binding passes the caller's current stream (the raw-handle fast
+    path agrees with torch.cuda.current_stream), and a product enqueued on a
+    side stream equals the one on the default stream."""
+    from int4_weight_only_amd import _stream
+    wl = synth.WORKLOADS["decode"]
+    X = synth.activations(4, wl["K"], 5).cuda()
+    assert _stream(X) == torch.cuda.current_stream().cuda_stream
+    Wq, S = w4.w4_quantize_pack(synth.weights(512, wl["K"], 5).cuda())
+    ref = down_bits(w4.w4a16_gemm(X, Wq, S))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert _stream(X) == side.cuda_stream != torch.cuda.default_stream().cuda_stream
+        Y = w4.w4a16_gemm(X, Wq, S)
+    side.synchronize()
+    np.testing.assert_array_equal(down_bits(Y), ref)
