@@ -131,7 +131,10 @@ int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K,
  * K % 32 == 0; M, N >= 0 (M*N == 0 is a no-op); K == 0 writes zeros.
  * Small M (<= 32, K <= 2^24) runs the decode kernel, larger M the tiled
  * MFMA kernel, which needs X and Wq each below 2 GiB (32-bit buffer
- * offsets): W4_ERR_UNSUPPORTED otherwise.
+ * offsets): W4_ERR_UNSUPPORTED otherwise.  For K <= 16384 the decode
+ * kernel multiplies the exact q * s (integer codes through the MFMA, the
+ * group scale on the fp32 partial) instead of bf16_rne(q * s): each
+ * product moves by at most 2^-9 |q s|.
  */
 int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
@@ -145,8 +148,8 @@ int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
  * with q the unsigned nibbles of Wq, as w4_quantize_pack_asym writes them.
  * Z uint8 [N, K/32], values in [0, 15] (other values: results undefined).
  * Layout, alignment, size limits, dispatch and accumulation as w4a16_gemm.
- * The decode kernel scales the exact integer sum of x (q - z) per group
- * instead of rounding w' to bf16: within fp32 accumulation tolerance.
+ * For K <= 16384 the decode kernel scales the exact integer sum of
+ * x (q - z) per group instead of rounding w' to bf16, as in w4a16_gemm.
  */
 int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                     const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,

@@ -16,8 +16,14 @@
 // The MFMA therefore sums x * (136 + q); its C operand starts at
 // -136 * sum_k x_k (itself one MFMA of X against the constant -136), so the
 // result is sum_k x_k q_k up to fp32 rounding.  Exact integer inputs stay
-// exact.  The scaled product is q * s exactly, not bf16(q * s): within the
-// fp32-accumulation tolerance of the definition.
+// exact.  The scaled product is q * s exactly, not bf16(q * s).  Per
+// product the two differ by at most 2^-9 |q s|, so over K terms the output
+// moves by ~2^-9/sqrt(3) * 0.6 * sqrt(K) |x| |w| (about 1e-3 of the
+// output's spread), while the tolerance of the definition has a fixed
+// absolute part.  Above K = 16384 (EXACT) each code is therefore
+// dequantized to w' = bf16(q s) with the 17-op fma_mix step of the tiled
+// product and the MFMA accumulates across groups: the definition's
+// weights, at about 2x the VALU per weight.
 //
 // Mapping (MI355X).  One workgroup of 16 waves per CU; wave w owns a
 // 256-element K slice (two 128-element "chunks") and keeps its slice of X
@@ -154,7 +160,7 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
 // one row are one 16-byte load).  T: tiles of 16 weight rows per workgroup.
 // RM: rows of each lane's D fragment that are accumulated (for M = 1 only
 // row 0 of lane row 0 exists; the other rows are skipped).
-template <bool SALIGNED, int T, int RM, bool ZP>
+template <bool SALIGNED, int T, int RM, bool ZP, bool EXACT>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -243,7 +249,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xop[cc][j] = x_slots(xop[cc][j]);
+      for (int j = 0; j < 4; ++j)
+        if constexpr (!EXACT) xop[cc][j] = x_slots(xop[cc][j]);
     uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
     {
       const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
@@ -273,6 +280,23 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        if constexpr (EXACT) {
+          // w' = bf16(q s) (or bf16((q - z) s)) per weight, the MFMA
+          // accumulating across groups
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint32_t word = j == 0 ? u[t].x : j == 1 ? u[t].y : j == 2 ? u[t].z : u[t].w;
+            const uint32_t sp = sct[t][2 * cc + (j >> 1)];
+            const float sc = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
+            DeqScale dq;
+            if constexpr (ZP)
+              dq = deq_scale_zp(sc, (float)((zc[t] >> (8 * j)) & 0xFFu));
+            else
+              dq = deq_scale(sc);
+            acc[t] = mfma16(xop[cc][j], dequant8<ZP>(word, dq), acc[t]);
+          }
+          continue;
+        }
         const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 cst = zero4;
         if constexpr (!ZP) cst = mfma16(xop[cc][j], neg136, zero4);
@@ -328,7 +352,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 // wave's LDS region (direct-to-LDS loads issued with the others) and is read
 // per group where it is used.  Each converted code word feeds the MFMAs of
 // both halves.  The region then takes the wave's partial sums.
-template <bool SALIGNED, int T, bool ZP>
+template <bool SALIGNED, int T, bool ZP, bool EXACT>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -426,7 +450,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xop[cc][j] = x_slots(xop[cc][j]);
+      for (int j = 0; j < 4; ++j)
+        if constexpr (!EXACT) xop[cc][j] = x_slots(xop[cc][j]);
     uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
     {
       const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
@@ -459,7 +484,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 x1 = x_slots(*(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane]);
+        u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane];
+        if constexpr (EXACT) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint32_t word = j == 0 ? u[t].x : j == 1 ? u[t].y : j == 2 ? u[t].z : u[t].w;
+            const uint32_t sp = sct[t][2 * cc + (j >> 1)];
+            const float sc = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
+            DeqScale dq;
+            if constexpr (ZP)
+              dq = deq_scale_zp(sc, (float)((zc[t] >> (8 * j)) & 0xFFu));
+            else
+              dq = deq_scale(sc);
+            const u32x4 w = dequant8<ZP>(word, dq);
+            acc0[t] = mfma16(xop[cc][j], w, acc0[t]);
+            acc1[t] = mfma16(x1, w, acc1[t]);
+          }
+          continue;
+        }
+        x1 = x_slots(x1);
         const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 cst0 = zero4, cst1 = zero4;
         if constexpr (!ZP) {
@@ -540,62 +583,75 @@ int cu_count() {
   return cus[dev];
 }
 
-template <bool SA, int T, int RM, bool ZP>
+template <bool SA, int T, int RM, bool ZP, bool EX>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<SA, T, RM, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((k_decode16<SA, T, RM, ZP, EX>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, int RM, bool ZP>
+template <bool SA, int RM, bool ZP, bool EX>
 hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode16_t<SA, 1, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<SA, 2, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<SA, 3, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode16_t<SA, 4, RM, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode16_t<SA, 1, RM, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<SA, 2, RM, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<SA, 3, RM, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<SA, 4, RM, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-template <bool SA, int T, bool ZP>
+template <bool SA, int T, bool ZP, bool EX>
 hipError_t run_decode32_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode32<SA, T, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
+  hipLaunchKernelGGL((k_decode32<SA, T, ZP, EX>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
                      X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, bool ZP>
+template <bool SA, bool ZP, bool EX>
 hipError_t run_decode32(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode32_t<SA, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode32_t<SA, 2, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode32_t<SA, 3, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode32_t<SA, 1, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode32_t<SA, 2, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode32_t<SA, 3, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
 }
+
+template <bool ZP, bool EX>
+hipError_t launch_decode_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                           hipStream_t st) {
+  const bool sa = ((K >> 5) & 7) == 0;
+  if (M == 1)
+    return sa ? run_decode16<true, 1, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st)
+              : run_decode16<false, 1, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  if (M <= 16)
+    return sa ? run_decode16<true, 4, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st)
+              : run_decode16<false, 4, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+  return sa ? run_decode32<true, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st)
+            : run_decode32<false, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
+}
+
+#ifndef W4_DECODE_EXACT_K
+#define W4_DECODE_EXACT_K 16384
+#endif
+constexpr int64_t kExactK = W4_DECODE_EXACT_K;
 
 template <bool ZP>
 hipError_t launch_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                          hipStream_t st) {
-  const bool sa = ((K >> 5) & 7) == 0;
-  if (M == 1)
-    return sa ? run_decode16<true, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st)
-              : run_decode16<false, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (M <= 16)
-    return sa ? run_decode16<true, 4, ZP>(X, Wq, S, Z, Y, M, N, K, st)
-              : run_decode16<false, 4, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return sa ? run_decode32<true, ZP>(X, Wq, S, Z, Y, M, N, K, st)
-            : run_decode32<false, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (K > kExactK) return launch_decode_t<ZP, true>(X, Wq, S, Z, Y, M, N, K, st);
+  return launch_decode_t<ZP, false>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 }  // namespace

@@ -83,11 +83,14 @@ def test_long_k(M, K):
     run_case(M, 200, K, 7 * M + K, "long K")
 
 
-@pytest.mark.parametrize("M", [1, 16, 32])
-def test_integer_exact_two_passes(M):
-    """As test_integer_exact, with K = 8192: two decode K passes."""
-    N, K = 64, 8192
-    say(f"gemm integer-exact two passes M={M}")
+@pytest.mark.parametrize("M,K", [(1, 8192), (16, 8192), (32, 8192),
+                                 (1, 16416), (16, 20480), (32, 20480), (33, 20480)])
+def test_integer_exact_two_passes(M, K):
+    """As test_integer_exact over several decode K passes: K = 8192 (two,
+    integer codes through the MFMA), K > 16384 (the decode kernels'
+    dequantizing variant; 16416 also leaves K / 32 off a multiple of 8)."""
+    N = 64
+    say(f"gemm integer-exact multi-pass M={M} K={K}")
     rng = np.random.default_rng(1000 + M)
     q = rng.integers(-7, 8, size=(N, K)).astype(np.float32)
     q.reshape(N, K // 32, 32)[:, :, 5] = -7.0
@@ -165,3 +168,13 @@ def test_binding_uses_the_current_stream():
         Y = w4.w4a16_gemm(X, Wq, S)
     side.synchronize()
     np.testing.assert_array_equal(down_bits(Y), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 48, 65536), (16, 48, 65536), (32, 48, 65536),
+                                   (33, 48, 65536), (1, 100000, 64), (20, 100000, 96),
+                                   (4096, 1, 96), (300, 3, 32)])
+def test_extreme_shapes(M, N, K):
+    """Long K (16 decode passes; 1024 pipeline steps with 128 scale
+    windows), very wide N (about 1600 decode workgroups), a single weight
+    row against 4096 activation rows, the smallest K."""
+    run_case(M, N, K, 5 * M + N + K, "extreme")

@@ -73,7 +73,7 @@ def test_long_k(M, K):
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 32, 33, 200])
-@pytest.mark.parametrize("K", [4096, 8192, 1056])
+@pytest.mark.parametrize("K", [4096, 8192, 1056, 16416, 20480])
 def test_integer_exact(M, K):
     N = 96
     say(f"gemm_asym integer-exact M={M} K={K}")
@@ -134,3 +134,9 @@ def test_k_zero_writes_zeros():
     Z = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
     w4.w4a16_gemm_asym(X, Wq, S, Z, out=Y)
     assert torch.count_nonzero(Y).item() == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 48, 65536), (32, 48, 65536), (33, 48, 65536),
+                                   (1, 100000, 64), (4096, 1, 96)])
+def test_extreme_shapes(M, N, K):
+    run_case(M, N, K, 7 * M + N + K, "extreme")
