@@ -641,10 +641,9 @@ hipError_t launch_decode_t(const uint16_t* X, const int32_t* Wq, const uint16_t*
             : run_decode32<false, ZP, EX>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-#ifndef W4_DECODE_EXACT_K
-#define W4_DECODE_EXACT_K 16384
-#endif
-constexpr int64_t kExactK = W4_DECODE_EXACT_K;
+// Above this K the decode kernels dequantize each code to bf16(q s) (the
+// definition's weights) instead of scaling exact integer-code sums.
+constexpr int64_t kExactK = 16384;
 
 template <bool ZP>
 hipError_t launch_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
