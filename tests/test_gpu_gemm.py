@@ -178,3 +178,22 @@ def test_extreme_shapes(M, N, K):
     windows), very wide N (about 1600 decode workgroups), a single weight
     row against 4096 activation rows, the smallest K."""
     run_case(M, N, K, 5 * M + N + K, "extreme")
+
+
+def random_shapes(seed, n):
+    """Seeded (M, N, K): M over the decode kernels and the tiled kernel, K
+    over aligned / unaligned scale rows, one or several decode passes and the
+    dequantizing decode variant, N ragged."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([1, 2, 7, 16, 17, 24, 32, 33, 65, 128, 200]))
+        K = 32 * int(rng.choice([1, 3, 8, 33, 128, 129, 200, 520, 700]))
+        N = int(rng.integers(1, 700))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(2024, 24))
+def test_random_shapes(M, N, K):
+    run_case(M, N, K, M * 7919 + N * 31 + K, "random")

@@ -140,3 +140,9 @@ def test_k_zero_writes_zeros():
                                    (1, 100000, 64), (4096, 1, 96)])
 def test_extreme_shapes(M, N, K):
     run_case(M, N, K, 7 * M + N + K, "extreme")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 310, 96), (5, 77, 4128), (17, 1, 20480), (32, 640, 1056),
+                                   (33, 129, 6400), (70, 250, 22400), (200, 31, 32)])
+def test_assorted_shapes(M, N, K):
+    run_case(M, N, K, M * 13 + N * 17 + K, "assorted")

@@ -187,6 +187,50 @@ def test_moe_gemm_small(B, x_row_div_is_k, weighted):
     assert np.all(y[untouched] == CANARY)
 
 
+def random_moe_cases(seed, n):
+    """Seeded grouped-product configurations: block sizes on both tiles (32 and
+    128 rows), K aligned and not (K % 256), ragged N, skewed and uniform ids,
+    dropped pairs, x_row_div of both kinds, weighted or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 300))
+        B = int(rng.choice([1, 3, 8, 16, 24, 32, 48, 64, 128]))
+        N = int(rng.integers(1, 400))
+        K = 32 * int(rng.choice([1, 5, 8, 12, 40, 72]))
+        out.append((i, E, k, T, B, N, K, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", random_moe_cases(77, 16), ids=lambda c: f"r{c[0]}")
+def test_moe_gemm_random(case):
+    i, E, k, T, B, N, K, div_k, weighted = case
+    say(f"moe_gemm random {case}")
+    rng = np.random.default_rng(1000 + i)
+    p = rng.dirichlet(np.full(E, 0.3))                     # uneven expert loads
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    ids[rng.random((T, k)) < 0.05] = -1                   # a few dropped pairs
+    Wq, S, ref_w = small_experts(E, N, K, 60 + i)
+    div = k if div_k else 1
+    Xb = synth.bits(synth.activations(T * k // div, K, 61 + i))
+    tw = rng.random((T, k)).astype(np.float32) if weighted else None
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    np.testing.assert_array_equal(down(s), s_ref)
+    Y = canary_bf16((T * k, N))
+    w4.w4a16_moe_gemm(up_bits(Xb), Wq, S, s, e, n, T, k, B, div,
+                      topk_weights=None if tw is None else up(tw), out=Y)
+    y = down_bits(Y)
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, div, T * k, tw)
+    valid = [f for f in range(T * k) if 0 <= ids.flat[f] < E]
+    assert sorted(ref) == valid
+    assert_rows_close(y, ref, "moe random")
+    untouched = [f for f in range(T * k) if f not in ref]
+    assert np.all(y[untouched] == CANARY)
+
+
 @pytest.mark.parametrize("I,K", [(48, 160), (200, 256), (128, 512)])
 @pytest.mark.parametrize("B", [4, 32, 64, 200])
 @pytest.mark.parametrize("x_row_div_is_k", [True, False])
