@@ -281,8 +281,42 @@ __global__ __launch_bounds__(256) void k_moe_sum(const uint32_t* __restrict__ H2
   }
 }
 
+// Vector path: one workgroup row per token (grid y), 8 bf16 per thread with
+// 16-byte loads and stores; the same per-element sum order as k_moe_sum.
+__global__ __launch_bounds__(256) void k_moe_sum8(const u32x4* __restrict__ H2,
+                                                  const float* __restrict__ w,
+                                                  u32x4* __restrict__ Out, int64_t T, int k,
+                                                  int64_t H8) {
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < H8;
+         c += (int64_t)gridDim.x * 256) {
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < k; ++j) {
+        const float wj = w ? w[t * k + j] : 1.0f;
+        const u32x4 hv = H2[(t * k + j) * H8 + c];
+        const uint32_t d[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s[2 * q] = __builtin_fmaf(wj, bf16_lo(d[q]), s[2 * q]);
+          s[2 * q + 1] = __builtin_fmaf(wj, bf16_hi(d[q]), s[2 * q + 1]);
+        }
+      }
+      Out[t * H8 + c] = u32x4{pk_bf16(s[0], s[1]), pk_bf16(s[2], s[3]), pk_bf16(s[4], s[5]),
+                              pk_bf16(s[6], s[7])};
+    }
+  }
+}
+
 hipError_t launch_moe_sum(const uint16_t* H2, const float* w, uint16_t* Out, int64_t T, int32_t k,
                           int64_t H, hipStream_t st) {
+  if (H % 8 == 0 && ((uintptr_t)H2 & 15) == 0 && ((uintptr_t)Out & 15) == 0) {
+    const int64_t H8 = H / 8;
+    const int64_t bx = (H8 + 255) / 256;
+    const int64_t by = T < 65535 ? T : 65535;
+    hipLaunchKernelGGL(k_moe_sum8, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, st,
+                       (const u32x4*)H2, w, (u32x4*)Out, T, (int)k, H8);
+    return hipGetLastError();
+  }
   const int64_t n = T * (H / 2);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 16384) blocks = 16384;

@@ -140,6 +140,30 @@ def test_moe_sum(weighted):
     assert np.all(np.abs(o - ref) <= 2.0 ** -8 * np.abs(ref) * 1.0001 + 1e-5 * scale)
 
 
+@pytest.mark.parametrize("T,k,H", [(23, 8, 96), (70000, 2, 16), (5, 3, 4096)])
+def test_moe_sum_vector_and_scalar_paths_agree(T, k, H):
+    """H % 8 == 0 with 16-byte aligned rows runs the 16-byte vector kernel
+    (T above the grid's y limit loops over tokens); a view 4 bytes off that
+    alignment runs the element-pair kernel.  Same sum order: equal bits."""
+    say(f"moe_sum paths T={T} k={k} H={H}")
+    n = T * k * H
+    H2b = synth.bits(synth.activations(T * k, H, 6))
+    w = np.random.default_rng(T).random((T, k)).astype(np.float32)
+    base = torch.empty(n + 8, dtype=torch.bfloat16, device="cuda")
+    out_base = torch.empty(T * H + 8, dtype=torch.bfloat16, device="cuda")
+    aligned = base[:n].view(T * k, H)
+    shifted = base[2:2 + n].view(T * k, H)              # 4-byte aligned only
+    aligned.copy_(up_bits(H2b))
+    a = down_bits(w4.w4_moe_sum(aligned, up(w), T, k, out=out_base[:T * H].view(T, H)))
+    shifted.copy_(up_bits(H2b))
+    b = down_bits(w4.w4_moe_sum(shifted, up(w), T, k, out=out_base[2:2 + T * H].view(T, H)))
+    np.testing.assert_array_equal(a, b)
+    toks = [0, T // 2, T - 1]
+    ref = omoe.moe_sum(H2b.reshape(T, k, H)[toks].reshape(-1, H), w[toks])
+    o = bf16.to_f32(a[toks]).astype(np.float64)
+    assert np.all(np.abs(o - ref) <= 2.0 ** -8 * np.abs(ref) * 1.0001 + 1e-5 * np.abs(ref).max())
+
+
 # ------------------------------------------------------------ grouped GEMM --
 
 def small_experts(E, N, K, seed):
