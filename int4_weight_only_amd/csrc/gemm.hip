@@ -76,6 +76,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   constexpr int XPW = XI / NW;         // ... issued by each wave
   constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage
   constexpr int kWS = BM <= 32 ? 4 : 2;   // code register sets (steps ahead)
+  constexpr int kU = kWS > kXS ? kWS : kXS;   // K-loop unroll: stage and set named statically
+  static_assert(kU % kXS == 0 && kU % kWS == 0, "unroll");
   static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
   // separately declared stages: each DMA target and each operand read names
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
-  const int nstepsp = (nsteps + kXS - 1) / kXS * kXS;  // padded to the unroll; pad steps load zeros, skip MFMAs
+  const int nstepsp = (nsteps + kU - 1) / kU * kU;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
@@ -381,8 +383,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       load_x(step + kXS - 1, st_next);
-      // pos = step % 4 (static); the 8-step scale window's half is (step >> 2) & 1
-      constexpr int P = decltype(pos)::value;
+      // P = step % 4 (static); the 8-step scale window's half is (step >> 2) & 1
+      constexpr int P = decltype(pos)::value % 4;
       if (P == 0 && (step & 4) == 0) {   // a new scale window: unpack it, fetch the next
         unpack_s(sraw, scw);
         load_s((step >> 3) + 1, sraw);
@@ -451,11 +453,17 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
-      for (int step = 0; step < nstepsp; step += 4) {
+      for (int step = 0; step < nstepsp; step += kU) {
         step_body(mse, std::integral_constant<int, 0>{}, step + 0, xs0, xs3, wset[0 % kWS], acc);
         step_body(mse, std::integral_constant<int, 1>{}, step + 1, xs1, xs0, wset[1 % kWS], acc);
         step_body(mse, std::integral_constant<int, 2>{}, step + 2, xs2, xs1, wset[2 % kWS], acc);
         step_body(mse, std::integral_constant<int, 3>{}, step + 3, xs3, xs2, wset[3 % kWS], acc);
+        if constexpr (kU == 8) {
+          step_body(mse, std::integral_constant<int, 4>{}, step + 4, xs0, xs3, wset[4 % kWS], acc);
+          step_body(mse, std::integral_constant<int, 5>{}, step + 5, xs1, xs0, wset[5 % kWS], acc);
+          step_body(mse, std::integral_constant<int, 6>{}, step + 6, xs2, xs1, wset[6 % kWS], acc);
+          step_body(mse, std::integral_constant<int, 7>{}, step + 7, xs3, xs2, wset[7 % kWS], acc);
+        }
       }
       // drain the loads of the padding steps before LDS is reused
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
