@@ -19,7 +19,9 @@ under "detail": the prefill product (M = 4096, N = 14336, K = 4096,
 TFLOP/s), quantize + pack and fake quant of that weight (GB/s), and the two
 routed MoE layers (128 experts / top-8 / hidden 4096 / intermediate 1536 at
 256 tokens; 384 experts / top-8 / hidden 7168 / intermediate 2048 at 4096
-tokens with skewed routing), per stage and whole layer; and under
+tokens with skewed routing), per stage and whole layer, the layer again at
+the other alignment block sizes (16 / 32 / 64 and 32 / 64), and the
+per-expert row distribution; and under
 "asym" the zero-point variants: the decode sweep and the prefill product
 with zero-point weights (one uint8 zero point per group on top of the
 scale), asymmetric quantize + pack and fake quant.
@@ -265,6 +267,9 @@ def bench_copy(torch, iters, timer):
             "GB/s": round(2 * n / (t * 1e-3) / 1e9, 1)}
 
 
+MOE_B_SWEEP = {"moe_qwen": (16, 32, 64), "moe_kimi": (32, 64)}
+
+
 def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     wl = synth.WORKLOADS[name]
     T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
@@ -314,6 +319,25 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     wbytes = gate_up.nbytes() + down.nbytes()
     counts = torch.bincount(ids.reshape(-1).long(), minlength=E)
     ntpp = int(buf.ntpp.item())
+    # the whole (fused) layer at other alignment block sizes
+    by_B = {str(B): round(t_layer * 1e3, 1)}
+    for B2 in MOE_B_SWEEP.get(name, ()):
+        if B2 == B:
+            continue
+        b2 = wmoe.alloc_buffers(T, k, E, H, I, B2, dev, fused=True)
+
+        def layer_b(i, b2=b2, B2=B2):
+            w4.w4_moe_route(logits, k, ids, tw)
+            w4.moe_align_block_size(ids, E, B2, b2.sorted_token_ids, b2.expert_ids, b2.ntpp)
+            w4.w4a16_moe_gemm_swiglu(X, gate_up.Wq, gate_up.S, b2.sorted_token_ids,
+                                     b2.expert_ids, b2.ntpp, T, k, B2, k, out=b2.A)
+            w4.w4a16_moe_gemm(b2.A, down.Wq, down.S, b2.sorted_token_ids, b2.expert_ids,
+                              b2.ntpp, T, k, B2, 1, out=b2.H2)
+            w4.w4_moe_sum(b2.H2, tw, T, k, out=b2.out)
+        timer.settle(layer_b, SETTLE_MS / 3)
+        by_B[str(B2)] = round(timer.run(layer_b, iters) / iters * 1e3, 1)
+        del b2
+    q = torch.quantile(counts.float(), torch.tensor([0.1, 0.5, 0.9], device=counts.device))
     res = {
         "T": T, "E": E, "k": k, "H": H, "I": I, "B": B,
         "layer_us": round(t_layer * 1e3, 1),
@@ -327,8 +351,10 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
                                       / 1e12 / PEAK_BF16_TFLOPS, 4),
         "frac_hbm_gemms": round(wbytes / ((per["gate_up"] + per["down"]) * 1e-6) / 1e9
                                 / PEAK_HBM_GBS, 4),
+        "layer_us_by_B": by_B,
         "rows_per_expert_max": int(counts.max().item()),
         "rows_per_expert_min": int(counts.min().item()),
+        "rows_per_expert_p10_p50_p90": [round(float(v), 1) for v in q.tolist()],
         "padding_frac": round(1.0 - pairs / ntpp, 4),
     }
     del gate_up, down, buf

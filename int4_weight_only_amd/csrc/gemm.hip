@@ -573,10 +573,15 @@ constexpr int kBMMoe = 128;     // expert blocks of 64 rows and more
 constexpr int kBMMoeSmall = 32; // expert blocks of 32 rows or fewer (few rows per expert)
 constexpr int kWNMoeSmall = 32;  // weight rows per wave of the 32-row tile (64 measured the same)
 
-// Tile rows of the grouped product for alignment block size B: with blocks
-// of at most 32 rows an expert holds few rows, the product streams weights,
-// and the 32-row tile keeps more of them in flight.
-int64_t moe_tile_rows(int32_t B) { return B <= kBMMoeSmall ? kBMMoeSmall : kBMMoe; }
+// Tile rows of the grouped product.  With at most 32 rows per expert on
+// average (and blocks of at most 32 rows) the product streams weights and
+// the 32-row tile keeps more of them in flight; with more rows per expert a
+// 32-row tile would split an expert into several runs that each re-read its
+// weights, so the 128-row tile runs.
+int64_t moe_tile_rows(int64_t T, int32_t k, int32_t E, int32_t B) {
+  const int64_t mean_rows = (T * k + E - 1) / E;
+  return (B <= kBMMoeSmall && mean_rows <= kBMMoeSmall) ? kBMMoeSmall : kBMMoe;
+}
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
@@ -613,7 +618,7 @@ hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* 
 // Slots (at most BM rows each: an alignment block, or one BM-row part of a
 // larger block), padded to whole rounds of one run's worth over the 8 XCDs.
 int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B) {
-  const int64_t bm = moe_tile_rows(B);
+  const int64_t bm = moe_tile_rows(T, k, E, B);
   const int64_t cap = ((T * k + (int64_t)E * (B - 1) + B - 1) / B) * B;
   const int64_t bpw = bm >= B ? bm / B : 1;
   const int64_t ppb = B > bm ? (B + bm - 1) / bm : 1;   // slots per block
@@ -649,7 +654,7 @@ hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* 
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                           int32_t x_row_div, hipStream_t st) {
-  if (moe_tile_rows(B) == kBMMoeSmall)
+  if (moe_tile_rows(T, k, E, B) == kBMMoeSmall)
     return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y,
                                               T, k, E, N, K, B, x_row_div, st);
   return launch_grouped_t<kBMMoe, kWN, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k,
