@@ -77,6 +77,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage
   constexpr int kWS = BM <= 32 ? 4 : 2;   // code register sets (steps ahead)
   constexpr int kU = kWS > kXS ? kWS : kXS;   // K-loop unroll: stage and set named statically
+  constexpr bool kRunSlots = MOE && BM <= 32;  // grouped product: slots index runs
   static_assert(kU % kXS == 0 && kU % kWS == 0, "unroll");
   static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
@@ -110,14 +111,17 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   const int bpw = BM >= B ? BM / B : 1;               // MoE: blocks per run (at most)
   const int ppb = B > BM ? (B + BM - 1) / BM : 1;      // MoE: slots per block
   if constexpr (MOE) {
-    // XCD-aware: groups of bpw slots (one run's worth) go round-robin over
-    // the XCDs; all N-tiles of a group on one XCD, which share its rows
+    // XCD-aware: slots go round-robin over the XCDs, all N-tiles of a slot
+    // on one XCD, which share its rows.  32-row tile: a slot is a run
+    // (below).  128-row tile: a slot is a block part, and groups of bpw
+    // slots (one run's worth of blocks) go to one XCD, which measured
+    // faster there than single slots.
     const int ntn = gridDim.x;                       // N-tiles
     const int pid = blockIdx.x + ntn * blockIdx.y;   // dispatch order
     const int xcd = pid & 7, j = pid >> 3;
     tile_n = j % ntn;
     const int q = j / ntn;
-    slot = (xcd + 8 * (q / bpw)) * bpw + q % bpw;
+    slot = kRunSlots ? xcd + 8 * q : (xcd + 8 * (q / bpw)) * bpw + q % bpw;
     tile_m = 0;
   } else {
     constexpr int kXcds = 8, GM = 8;
@@ -145,19 +149,76 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   int row0 = 0;                // MoE: first sorted position of the run
   int expert = 0;
   if constexpr (MOE) {
-    // Find this block's run of one expert with wave 0: expert_ids[0, nblk)
-    // is non-decreasing, so the blocks of expert e are contiguous.  Lanes
-    // read the 64 ids ending at b and the 64 ids starting at b in two
-    // parallel loads; ballots give the distance to the run's first block
-    // (a longer run walks back 64 blocks at a time) and its end.
+    // Find this slot's run of one expert with wave 0: expert_ids[0, nblk)
+    // is non-decreasing, so the blocks of expert e are contiguous.
     if (wave == 0) {
-      const int b = slot / ppb;
-      const int part = slot - b * ppb;
       const int nblk = ntpp[0] / B;
-      int lead = 0, e = -1, last = 0;
-      if (b < nblk) {
+      int lead = 0, e = -1, last = 0, b = 0, part = 0;
+      if (kRunSlots && bpw > 1) {
+        // Runs of up to bpw blocks start wherever an expert's blocks do, so
+        // slot r is the r-th run: count run starts over expert_ids, 64
+        // blocks per step with sixteen steps' ids loaded at once.  A ballot of
+        // expert starts (id differs from the previous block's) gives each
+        // block its expert's first block; a second ballot marks the blocks
+        // that start a run.  Indexing slots by run spreads the runs evenly
+        // over the XCDs and launches no workgroup for a run's later blocks.
+        const int r = slot;
+        int count = 0, carry_e = -3, carry_first = 0;
+        b = -1;
+        const uint64_t below = (1ull << lane) - 1ull;     // lanes < lane
+        constexpr int kScan = 16;
+        for (int cb = 0; cb < nblk && b < 0; cb += 64 * kScan) {
+          int ev[kScan];
+#pragma unroll
+          for (int u = 0; u < kScan; ++u) {
+            const int bb = cb + 64 * u + lane;
+            ev[u] = bb < nblk ? expert_ids[bb] : -2;
+          }
+#pragma unroll
+          for (int u = 0; u < kScan; ++u) {
+            const int c0 = cb + 64 * u;
+            if (c0 >= nblk || b >= 0) break;
+            const int bb = c0 + lane;
+            const bool valid = bb < nblk;
+            const int eb = ev[u];
+            int prev = __shfl_up(eb, 1);
+            if (lane == 0) prev = carry_e;
+            const uint64_t starts = __ballot(valid && eb != prev);
+            const uint64_t upto = starts & (below | (1ull << lane));
+            const int first = upto ? c0 + 63 - (int)__clzll(upto) : carry_first;
+            const bool is_lead = valid && eb >= 0 && eb < E && ((bb - first) % bpw) == 0;
+            const uint64_t leads = __ballot(is_lead);
+            const int n = __popcll(leads);
+            if (r < count + n) {
+              const uint64_t hit = __ballot(is_lead && __popcll(leads & below) == r - count);
+              const int ln = __ffsll((long long)hit) - 1;
+              b = c0 + ln;
+              e = __shfl(eb, ln);
+            } else {
+              count += n;
+              carry_e = __shfl(eb, 63);
+              carry_first = __shfl(first, 63);
+            }
+          }
+        }
+        if (b >= 0) {
+          // blocks of the run: the expert's blocks in [b, b + bpw)
+          const int fidx = b + lane;
+          const int fid = (fidx < nblk && lane < bpw) ? expert_ids[fidx] : -2;
+          lead = 1;
+          last = b + __popcll(__ballot(fid == e));
+        } else {
+          b = 0;
+        }
+      } else if ((b = slot / ppb) < nblk) {
+        // slot = block part: this block's run, led by it if it lies a
+        // multiple of bpw blocks after its expert's first block.  Lanes read
+        // the 64 ids ending at b and the 64 ids starting at b in two
+        // parallel loads; ballots give the distance to the expert's first
+        // block (a longer expert walks back 64 blocks at a time) and the
+        // run's end.
+        part = slot - b * ppb;
         e = expert_ids[b];
-        // backwards: first block of the run
         int first = b;
         for (int base = b;; base -= 64) {
           const int idx = base - lane;                       // lane 0 = base
@@ -167,7 +228,6 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
           first = base - run + 1;
           if (run < 64 || base - 64 < 0) break;
         }
-        // forwards: end of the run, capped at bpw blocks from b
         const int fidx = b + lane;
         const int fid = (fidx < nblk && lane < bpw) ? expert_ids[fidx] : -2;
         const int fwd = __popcll(__ballot(fid == e));      // blocks of the run in [b, b + bpw)
@@ -623,7 +683,9 @@ int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B) {
   const int64_t bpw = bm >= B ? bm / B : 1;
   const int64_t ppb = B > bm ? (B + bm - 1) / bm : 1;   // slots per block
   const int64_t slots = (cap / B) * ppb;
-  return (slots + 8 * bpw - 1) / (8 * bpw) * (8 * bpw);
+  // 32-row tile: slots index runs; else groups of bpw slots per XCD
+  const int64_t round = bm == kBMMoeSmall ? 8 : 8 * bpw;
+  return (slots + round - 1) / round * round;
 }
 
 namespace {

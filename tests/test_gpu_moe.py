@@ -228,6 +228,29 @@ def random_moe_cases(seed, n):
     return out
 
 
+@pytest.mark.parametrize("B", [1, 2, 16])
+def test_moe_gemm_run_search(B):
+    """Few rows per expert (the 32-row tile, whose workgroups index runs of
+    up to 32 / B blocks): with B = 1 there are over 1024 blocks (several
+    batches of the run search) and a hot expert spans several 64-block
+    chunks of it."""
+    E, T, k, N, K = 64, 600, 2, 40, 96
+    say(f"moe_gemm run search B={B}")
+    rng = np.random.default_rng(500 + B)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[:75, 0] = 7                                     # expert 7: >= 75 rows
+    ids[:75, 1] = np.where(ids[:75, 1] == 7, 8, ids[:75, 1])
+    Wq, S, ref_w = small_experts(E, N, K, 80 + B)
+    Xb = synth.bits(synth.activations(T, K, 81))
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    Y = canary_bf16((T * k, N))
+    w4.w4a16_moe_gemm(up_bits(Xb), Wq, S, s, e, n, T, k, B, k, out=Y)
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, k, T * k)
+    assert len(ref) == T * k
+    assert_rows_close(down_bits(Y), ref, f"run search B={B}")
+
+
 @pytest.mark.parametrize("case", random_moe_cases(77, 16), ids=lambda c: f"r{c[0]}")
 def test_moe_gemm_random(case):
     i, E, k, T, B, N, K, div_k, weighted = case
