@@ -23,8 +23,8 @@
 // registers); codes go to registers two steps ahead (two register sets;
 // four for the 32-row tile, whose few MFMAs per step leave the weight
 // stream latency-bound), scales in 8-step windows.  The K loop is unrolled
-// by four so that each step names its LDS stage and register set
-// statically.
+// by four (the stage rotation, or the register-set rotation if longer) so
+// that each step names its LDS stage and register set statically.
 // In LDS a 64-element activation row is 128 bytes; its eight 16-byte
 // pieces are stored XOR-swizzled by (row / 2) % 8 so that the MFMA
 // operand reads of 32 consecutive rows spread over the banks.  Every load
@@ -57,18 +57,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // SA: K is a multiple of 256, so a row's scales start 16-byte aligned and
 // eight of them are one 16-byte load.
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
-// take gate rows [c, c + 128) and waves 2, 3 the matching up rows, and the
+// take gate rows [c, c + 2 WN) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
 // ZP (dense only): zero-point weights, unsigned codes and one zero point
 // byte per group in Z [N, K/32]; w' = bf16((q - z) s).
-// BM = 32 (one MFMA row tile, small expert blocks): four code register sets
-// and four workgroups per CU keep more weight bytes in flight.
+// BM = 32 (one MFMA row tile, few rows per expert): four code register sets
+// and four to six workgroups per CU keep more weight bytes in flight, and
+// workgroups index runs rather than blocks.
 template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
-    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
-    const float* __restrict__ topk_w, int n_pairs, int B, int x_row_div, int E) {
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
+    const int32_t* __restrict__ ntpp, const float* __restrict__ topk_w, int n_pairs, int B,
+    int x_row_div, int E) {
   constexpr int NT = NW * 64;
   constexpr int MS = BM / 32;          // 32-row MFMA tiles along M
   constexpr int NS = WN / 32;          // 32-col MFMA tiles along N per wave
