@@ -198,7 +198,7 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
       !aligned(num_tokens_post_padded, 4) || !aligned(topk_weights, 4))
     return W4_ERR_MISALIGNED;
-  if (w4::moe_gemm_slots(T, k, E, B) > 65535) return W4_ERR_UNSUPPORTED;
+  if (w4::moe_gemm_workgroups(T, k, E, N, B, false) >= kMaxI32) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids,
                                         num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B,
                                         x_row_div, as_stream(stream)));
@@ -226,7 +226,7 @@ int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* 
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
       !aligned(num_tokens_post_padded, 4))
     return W4_ERR_MISALIGNED;
-  if (w4::moe_gemm_slots(T, k, E, B) > 65535) return W4_ERR_UNSUPPORTED;
+  if (w4::moe_gemm_workgroups(T, k, E, N, B, true) >= kMaxI32) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids,
                                                num_tokens_post_padded, A, T, k, E, I, K, B,
                                                x_row_div, as_stream(stream)));

@@ -152,8 +152,9 @@ hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const ui
                                   const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
                                   int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
                                   hipStream_t st);
-// Workgroup slots along the grouped GEMM's second grid dimension.
+// Slots of the grouped GEMM, and its workgroups (N-tiles x slots, a 1-D grid).
 int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B);
+int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B, bool swiglu);
 hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t B,
                         int64_t cap, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
                         hipStream_t st);

@@ -118,8 +118,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     // (below).  128-row tile: a slot is a block part, and groups of bpw
     // slots (one run's worth of blocks) go to one XCD, which measured
     // faster there than single slots.
-    const int ntn = gridDim.x;                       // N-tiles
-    const int pid = blockIdx.x + ntn * blockIdx.y;   // dispatch order
+    // N-tiles: 2 WN gate rows (+ the matching up rows) per workgroup with
+    // SWI, else NW WN weight rows; a 1-D grid of N-tiles x slots
+    const int ntn = SWI ? ((N >> 1) + 2 * WN - 1) / (2 * WN) : (N + NW * WN - 1) / (NW * WN);
+    const int pid = blockIdx.x;                      // dispatch order
     const int xcd = pid & 7, j = pid >> 3;
     tile_n = j % ntn;
     const int q = j / ntn;
@@ -214,26 +216,35 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         }
       } else if ((b = slot / ppb) < nblk) {
         // slot = block part: this block's run, led by it if it lies a
-        // multiple of bpw blocks after its expert's first block.  Lanes read
-        // the 64 ids ending at b and the 64 ids starting at b in two
-        // parallel loads; ballots give the distance to the expert's first
-        // block (a longer expert walks back 64 blocks at a time) and the
-        // run's end.
+        // multiple of bpw blocks after its expert's first block.
         part = slot - b * ppb;
         e = expert_ids[b];
-        int first = b;
-        for (int base = b;; base -= 64) {
-          const int idx = base - lane;                       // lane 0 = base
-          const int id = idx >= 0 ? expert_ids[idx] : -2;
-          const uint64_t same = __ballot(id == e);           // contiguous from lane 0
-          const int run = __popcll(same);
-          first = base - run + 1;
-          if (run < 64 || base - 64 < 0) break;
+        // The expert's first block: expert_ids is non-decreasing, so the ids
+        // below e form a prefix of [0, b]; 64 lanes sample [lo, hi] evenly and
+        // a ballot narrows it 64-fold per step (three steps for 262144 blocks).
+        int lo = 0, hi = b;
+        while (lo < hi) {
+          const int step = (hi - lo + 63) / 64;
+          const int p = lo + lane * step;
+          const int id = expert_ids[min(p, hi)];             // hi <= b < nblk: in bounds
+          const int c = __popcll(__ballot(p < hi && id < e));
+          if (c == 0) break;                                 // expert_ids[lo] == e
+          const int nhi = min(hi, lo + c * step);
+          lo = lo + (c - 1) * step + 1;
+          hi = nhi;
         }
-        const int fidx = b + lane;
-        const int fid = (fidx < nblk && lane < bpw) ? expert_ids[fidx] : -2;
-        const int fwd = __popcll(__ballot(fid == e));      // blocks of the run in [b, b + bpw)
+        const int first = lo;
         if (e >= 0 && e < E && ((b - first) % bpw) == 0) {
+          // blocks of the run: the expert's blocks in [b, b + bpw), counted
+          // 64 per ballot (bpw reaches 128 at B = 1)
+          int fwd = 0;
+          for (int off = 0; off < bpw; off += 64) {
+            const int fidx = b + off + lane;
+            const int fid = (fidx < nblk && off + lane < bpw) ? expert_ids[fidx] : -2;
+            const int cnt = __popcll(__ballot(fid == e));
+            fwd += cnt;
+            if (cnt < 64) break;
+          }
           lead = 1;
           last = b + fwd;
         }
@@ -690,6 +701,13 @@ int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B) {
   return (slots + round - 1) / round * round;
 }
 
+// Workgroups of one grouped launch: N-tiles x slots (a 1-D grid).
+int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B, bool swiglu) {
+  const int64_t wn = moe_tile_rows(T, k, E, B) == kBMMoeSmall ? kWNMoeSmall : kWN;
+  const int64_t ntn = swiglu ? (N / 2 + 2 * wn - 1) / (2 * wn) : (N + kNW * wn - 1) / (kNW * wn);
+  return ntn * moe_gemm_slots(T, k, E, B);
+}
+
 namespace {
 template <int BM, int WN, bool SWI>
 hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
@@ -699,7 +717,7 @@ hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t
                           int32_t x_row_div, hipStream_t st) {
   // a fused SwiGLU workgroup covers 2 WN gate rows and the matching up rows
   const int64_t ntn = SWI ? (N / 2 + 2 * WN - 1) / (2 * WN) : (N + kNW * WN - 1) / (kNW * WN);
-  const dim3 grid((unsigned)ntn, (unsigned)moe_gemm_slots(T, k, E, B));
+  const dim3 grid((unsigned)(ntn * moe_gemm_slots(T, k, E, B)));
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
     hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st, X,

@@ -228,6 +228,23 @@ def random_moe_cases(seed, n):
     return out
 
 
+def test_moe_gemm_many_blocks():
+    """70000 alignment blocks (B = 1): more slots than one grid dimension of
+    65535 holds, in the 1-D grid of N-tiles x slots."""
+    E, T, k, N, K, B = 4, 70000, 1, 40, 64, 1
+    say("moe_gemm 70000 blocks")
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    Wq, S, ref_w = small_experts(E, N, K, 90)
+    Xb = synth.bits(synth.activations(T, K, 91))
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    y = down_bits(w4.w4a16_moe_gemm(up_bits(Xb), Wq, S, s, e, n, T, k, B, 1))
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, 1, T * k)
+    assert len(ref) == T
+    assert_rows_close(y, ref, "70000 blocks")
+
+
 @pytest.mark.parametrize("B", [1, 2, 16])
 def test_moe_gemm_run_search(B):
     """Few rows per expert (the 32-row tile, whose workgroups index runs of
