@@ -172,7 +172,7 @@ def test_binding_uses_the_current_stream():
 
 @pytest.mark.parametrize("M,N,K", [(1, 48, 65536), (16, 48, 65536), (32, 48, 65536),
                                    (33, 48, 65536), (1, 100000, 64), (20, 100000, 96),
-                                   (4096, 1, 96), (300, 3, 32)])
+                                   (4096, 1, 96), (300, 3, 32), (40000, 64, 64)])
 def test_extreme_shapes(M, N, K):
     """Long K (16 decode passes; 1024 pipeline steps with 128 scale
     windows), very wide N (about 1600 decode workgroups), a single weight

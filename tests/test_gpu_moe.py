@@ -228,6 +228,42 @@ def random_moe_cases(seed, n):
     return out
 
 
+def extreme_moe_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 64, 300, 1024]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 3, 40, 500, 2000]))
+        B = int(rng.choice([1, 2, 128, 200, 256, 1024]))
+        N = int(rng.choice([2, 34, 130, 264]))       # I = N even (w4_silu_mul)
+        K = 32 * int(rng.choice([1, 2, 9, 64]))
+        out.append((i, E, k, T, B, N, K))
+    return out
+
+
+@pytest.mark.parametrize("case", extreme_moe_cases(4242, 14), ids=lambda c: f"x{c[0]}")
+def test_moe_gemm_extreme(case):
+    """Block sizes at the ends of the range (B = 1: runs of up to 128 blocks;
+    B = 1024: eight slot parts per block), up to 1024 experts, top-16,
+    single tokens, K = 32; the plain product and the fused SwiGLU product."""
+    i, E, k, T, B, N, K = case
+    say(f"moe_gemm extreme {case}")
+    rng = np.random.default_rng(2000 + i)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    Wq, S, ref_w = small_experts(E, 2 * N, K, 100 + i)
+    Xb = synth.bits(synth.activations(T, K, 101 + i))
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    X = up_bits(Xb)
+    H1 = w4.w4a16_moe_gemm(X, Wq, S, s, e, n, T, k, B, k)
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, k, T * k)
+    assert len(ref) == T * k
+    assert_rows_close(down_bits(H1), ref, "moe extreme")
+    A = down_bits(w4.w4a16_moe_gemm_swiglu(X, Wq, S, s, e, n, T, k, B, k))
+    np.testing.assert_array_equal(A, down_bits(w4.w4_silu_mul(H1)))
+
+
 def test_moe_gemm_many_blocks():
     """70000 alignment blocks (B = 1): more slots than one grid dimension of
     65535 holds, in the 1-D grid of N-tiles x slots."""
