@@ -65,7 +65,7 @@ int w4_quantize_pack(const uint16_t* W, int64_t N, int64_t K, int32_t* Wq, uint1
   if (!W || !Wq || !S) return W4_ERR_NULL;
   if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
   const int64_t words = N * (K / 8);
-  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  if (words / (K / 8) != N || words > ((int64_t)1 << 38)) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_quantize(W, words, Wq, S, nullptr, nullptr, false, false,
                                         as_stream(stream)));
 }
@@ -77,7 +77,7 @@ int w4_quantize_pack_asym(const uint16_t* W, int64_t N, int64_t K, int32_t* Wq, 
   if (!W || !Wq || !S || !Z) return W4_ERR_NULL;
   if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
   const int64_t words = N * (K / 8);
-  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  if (words / (K / 8) != N || words > ((int64_t)1 << 38)) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_quantize(W, words, Wq, S, Z, nullptr, false, true,
                                         as_stream(stream)));
 }
@@ -88,7 +88,7 @@ int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K, uint16_t* W_fq, 
   if (!W || !W_fq) return W4_ERR_NULL;
   if (!aligned(W, 16) || !aligned(W_fq, 16)) return W4_ERR_MISALIGNED;
   const int64_t words = N * (K / 8);
-  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  if (words / (K / 8) != N || words > ((int64_t)1 << 38)) return W4_ERR_UNSUPPORTED;
   const uintptr_t a = (uintptr_t)W, b = (uintptr_t)W_fq, len = (uintptr_t)(words * 16);
   if (a != b && a < b + len && b < a + len) return W4_ERR_UNSUPPORTED;
   return hip_status(w4::launch_quantize(W, words, nullptr, nullptr, nullptr, W_fq, true, true,
@@ -101,7 +101,7 @@ int w4_fake_quant(const uint16_t* W, int64_t N, int64_t K, uint16_t* W_fq, void*
   if (!W || !W_fq) return W4_ERR_NULL;
   if (!aligned(W, 16) || !aligned(W_fq, 16)) return W4_ERR_MISALIGNED;
   const int64_t words = N * (K / 8);
-  if (words / (K / 8) != N || words > ((int64_t)1 << 39)) return W4_ERR_UNSUPPORTED;
+  if (words / (K / 8) != N || words > ((int64_t)1 << 38)) return W4_ERR_UNSUPPORTED;
   // in place is fine; partial overlap is not
   const uintptr_t a = (uintptr_t)W, b = (uintptr_t)W_fq, len = (uintptr_t)(words * 16);
   if (a != b && a < b + len && b < a + len) return W4_ERR_UNSUPPORTED;
