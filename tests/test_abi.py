@@ -124,8 +124,8 @@ def test_quantize_pack_validation(lib):
     assert f(A16, 4, 32, A4, A2, None) == MISALIGNED
     assert f(A16, 4, 32, A16, A1, None) == MISALIGNED
     # one thread per packed word: the grid stays within 2^31 - 1 workgroups
-    assert f(A16, 1 << 30, 2048, A16, A2, None) == UNSUPPORTED     # 2^38 + 2^37 words
-    assert lib.w4_fake_quant(A16, 1 << 30, 2048, A16, None) == UNSUPPORTED
+    assert f(A16, 3 << 29, 2048, A16, A2, None) == UNSUPPORTED     # 2^38 + 2^37 words
+    assert lib.w4_fake_quant(A16, 3 << 29, 2048, A16, None) == UNSUPPORTED
 
 
 def test_quantize_pack_asym_validation(lib):
