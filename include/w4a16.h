@@ -258,7 +258,10 @@ int w4_moe_sum(const uint16_t* H2, const float* topk_weights, uint16_t* Out,
  *   expert index first), ordered by descending logit; weights are the
  *   picked p renormalised to sum to 1 (= softmax over the picked logits).
  * logits float32 [T, E]; topk_ids int32 [T, k]; topk_weights float32 [T, k].
- * 1 <= k <= min(E, 16), 1 <= E <= 1024.  fp32 arithmetic.
+ * 1 <= k <= min(E, 16), 1 <= E <= 1024, T < 2^31.  fp32 arithmetic.
+ * -inf logits (masked experts) sort last, by index, and the k ids of a
+ * token are always distinct; NaN logits are never picked (a row with fewer
+ * than k non-NaN logits gets unspecified ids).
  */
 int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
                  int32_t* topk_ids, float* topk_weights, void* stream);

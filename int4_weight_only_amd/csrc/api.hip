@@ -252,7 +252,7 @@ int w4_moe_sum(const uint16_t* H2, const float* topk_weights, uint16_t* Out, int
 int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
                  float* topk_weights, void* stream) {
   if (T < 0 || E < 1 || k < 1) return W4_ERR_SHAPE;
-  if (E > 1024 || k > 16 || k > E) return W4_ERR_UNSUPPORTED;
+  if (E > 1024 || k > 16 || k > E || T > kMaxI32) return W4_ERR_UNSUPPORTED;
   if (T == 0) return W4_OK;
   if (!logits || !topk_ids || !topk_weights) return W4_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))

@@ -208,10 +208,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     }
     picked[j] = best;
     picked_id[j] = bi;
-    // remove the pick
+    // remove the pick: NaN is never greater than nor equal to anything, so
+    // a removed expert cannot be picked again even when the rest are -inf
+    // (masked experts); those then follow in index order
 #pragma unroll
     for (int i = 0; i < kRouteMaxPerLane; ++i)
-      if (lane + 64 * i == bi) v[i] = -__builtin_inff();
+      if (lane + 64 * i == bi) v[i] = __builtin_nanf("");
   }
   if (lane == 0) {
     float sum = 0.0f;

@@ -110,6 +110,29 @@ def test_route(T, E, k, kind):
 
 # ------------------------------------------------------ element-wise steps --
 
+def test_route_masked_and_tied_logits():
+    """Rows with fewer finite logits than k (masked experts at -inf), all
+    -inf, and all equal: the ids are distinct and follow (logit desc, index
+    asc), as the oracle orders them."""
+    T, E, k = 6, 40, 8
+    lg = np.zeros((T, E), np.float32)
+    lg[0, :] = -np.inf                                  # all masked
+    lg[1, :] = -np.inf
+    lg[1, [5, 17, 30]] = [0.5, 2.0, -1.0]               # 3 finite < k
+    lg[2, :] = 1.25                                     # all tied
+    lg[3, :] = np.linspace(-1, 1, E)[::-1]
+    lg[4, ::2] = -np.inf
+    lg[5, :] = np.random.default_rng(3).normal(size=E)
+    ids_ref, w_ref = omoe.route(lg, k)
+    ids, w = w4.w4_moe_route(up(lg), k)
+    ids = down(ids)
+    np.testing.assert_array_equal(ids, ids_ref)
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == k
+    fin = np.isfinite(w_ref)
+    np.testing.assert_allclose(down(w)[fin], w_ref[fin], rtol=2e-6, atol=1e-7)
+
+
 def test_silu_mul():
     R, I = 37, 96
     say("silu_mul")
