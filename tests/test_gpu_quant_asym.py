@@ -84,3 +84,28 @@ def test_empty_is_noop():
     Wq, S, Z = w4.w4_quantize_pack_asym(W)
     assert Wq.numel() == 0 and S.numel() == 0 and Z.numel() == 0
     assert w4.w4_fake_quant_asym(W).numel() == 0
+
+
+def fuzz_bits(seed, N, K, max_exp):
+    """Random finite bf16 bit patterns (exponent field 0 .. max_exp, so
+    subnormals included), the exponent range varying per group, plus groups
+    of exact ties: (m + 1/2) * s for a random bf16 scale s."""
+    rng = np.random.default_rng(seed)
+    G = K // 32
+    lo = rng.integers(0, max_exp, size=(N, G, 1))
+    width = rng.choice([1, 4, 16, 64, 255], size=(N, G, 1))
+    exp = np.clip(lo + rng.integers(0, 256, size=(N, G, 32)) % width, 0, max_exp)
+    sign = rng.integers(0, 2, size=(N, G, 32))
+    man = rng.integers(0, 128, size=(N, G, 32))
+    W = ((sign << 15) | (exp << 7) | man).astype(np.uint16)
+    ties = rng.random((N, G)) < 0.1
+    s = bf16.to_f32(rng.integers(0x3A00, 0x4200, size=(N, G)).astype(np.uint16))
+    m = rng.integers(-7, 7, size=(N, G, 32)).astype(np.float32)
+    tie_vals = bf16.rne(((m + 0.5) * s[..., None]).astype(np.float32))
+    W = np.where(ties[..., None], tie_vals, W)
+    return W.reshape(N, K)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_bit_pattern_fuzz(seed):
+    check(fuzz_bits(seed, 256, 1024, 251), f"fuzz seed {seed}")
