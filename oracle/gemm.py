@@ -43,9 +43,23 @@ def w4a16_gemm_asym(X, Wq, S, Z):
     ``Z`` uint8 [N, K/32].  Returns the unrounded float64 product.
     """
     x = bf16.to_f32(X).astype(np.float64)
+    return x @ dequant_asym_f64(Wq, S, Z).T
+
+
+def dequant_asym_f64(Wq, S, Z):
+    """Unsigned packed codes + bf16 scales + uint8 zero points [N, K/32] ->
+    float64 w' = bf16((q - z) * s) [N, K] ("Quantization basics" §2.1)."""
     q = quant_asym.unpack_unsigned(Wq)
-    w = bf16.to_f32(quant_asym.dequant_asym(q, S, Z)).astype(np.float64)
-    return x @ w.T
+    return bf16.to_f32(quant_asym.dequant_asym(q, S, Z)).astype(np.float64)
+
+
+def dequant_weights_f64(*w):
+    """(Wq, S) -> symmetric dequant; (Wq, S, Z) -> zero-point dequant."""
+    if len(w) == 2:
+        return dequant_f64(*w)
+    if len(w) == 3:
+        return dequant_asym_f64(*w)
+    raise ValueError("weights are (Wq, S) or (Wq, S, Z)")
 
 
 def to_bf16(y):

@@ -25,6 +25,9 @@ expert activation; the readings used here are:
 * Combine: out[t] = sum over j = 0..k-1 of w[t, j] * down_out[t*k + j].
 * Storage points: the gate_up output, the activation and the down output
   are rounded to bf16, the final output too.
+* Zero-point experts ("Quantization basics: from FP32 to INT4" §2.3): an
+  expert's weights given as (Wq, S, Z) are dequantized as bf16((q - z) s);
+  everything else is unchanged.
 """
 
 import numpy as np
@@ -119,7 +122,8 @@ def grouped_gemm(X, weights, sorted_ids, expert_ids, ntpp, B, x_row_div,
     For every block b < ntpp / B with expert e = expert_ids[b], and every
     slot holding a valid pair f (f < n_pairs): row f of the result is
     X[f // x_row_div] * dequant(W_e)^T, multiplied by topk_weights.flat[f]
-    when given.  ``weights(e)`` returns (Wq int32 [N, K/8], S bf16 [N, K/32]).
+    when given.  ``weights(e)`` returns (Wq int32 [N, K/8], S bf16 [N, K/32])
+    or, for zero-point experts, (Wq, S, Z uint8 [N, K/32]).
     ``experts``, when given, restricts the product to blocks of those experts
     (a sampled check at sizes where the whole product is too slow here).
     Returns {f: float64 row} for the rows written.
@@ -134,8 +138,7 @@ def grouped_gemm(X, weights, sorted_ids, expert_ids, ntpp, B, x_row_div,
             continue
         if e not in cache:
             cache.clear()
-            Wq, S = weights(e)
-            cache[e] = gemm.dequant_f64(Wq, S)
+            cache[e] = gemm.dequant_weights_f64(*weights(e))
         w = cache[e]
         for i in range(B):
             f = int(sorted_ids[b * B + i])
@@ -187,7 +190,8 @@ def moe_layer(X, ids, topk_weights, gate_up, down, tokens=None):
       a  = bf16(silu(h1[:I]) * h1[I:])             [I]
       h2 = bf16(a * dequant(Wdn_e)^T)              [H]
     out[t] = sum_j w[t, j] * h2_j (float64, then compared to bf16 output).
-    ``gate_up(e)`` / ``down(e)`` return (Wq, S) of expert e.  Returns
+    ``gate_up(e)`` / ``down(e)`` return (Wq, S), or (Wq, S, Z) for zero-point
+    experts, of expert e.  Returns
     {t: float64 row} for the requested tokens (all when None).  Weights are
     dequantized one expert at a time, so only the experts used by the
     requested tokens are touched.
@@ -203,8 +207,8 @@ def moe_layer(X, ids, topk_weights, gate_up, down, tokens=None):
             need.setdefault(int(ids[t, j]), []).append((t, j))
     h2 = {}
     for e in sorted(need):
-        wgu = gemm.dequant_f64(*gate_up(e))
-        wdn = gemm.dequant_f64(*down(e))
+        wgu = gemm.dequant_weights_f64(*gate_up(e))
+        wdn = gemm.dequant_weights_f64(*down(e))
         I = wgu.shape[0] // 2
         for (t, j) in need[e]:
             h1 = bf16.to_f32(gemm.to_bf16(x[t] @ wgu.T)).astype(np.float64)

@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import bf16, gemm, moe, quant
+from oracle import bf16, gemm, moe, quant, quant_asym
 
 
 # --------------------------------------------------------------------------
@@ -188,3 +188,61 @@ def test_layer_definition_equals_aligned_pipeline(B):
     out = moe.moe_sum(H2, w)
     for t in range(T):
         assert np.array_equal(out[t], ref[t])
+
+
+# --------------------------------------------------------------------------
+# zero-point experts ("Quantization basics: from FP32 to INT4" §2.3)
+# --------------------------------------------------------------------------
+
+def _integer_zp_expert(rng, N, K):
+    """Integer weights whose groups span exactly [lo, lo + 15], lo drawn per
+    group from [-15, 0]: the asymmetric quantizer gives s = 1, z = -lo, and
+    the dequantized weights are the integers themselves."""
+    G = K // 32
+    lo = rng.integers(-15, 1, size=(N, G, 1)).astype(np.float32)
+    w = lo + rng.integers(0, 16, size=(N, G, 32)).astype(np.float32)
+    w[:, :, 5] = lo[:, :, 0]
+    w[:, :, 20] = lo[:, :, 0] + 15.0
+    return w.reshape(N, K)
+
+
+def test_grouped_gemm_zero_point_integer_experts_is_integer_matmul():
+    """Per-group zero points that differ by row, group and expert: every
+    grouped row is the textbook integer product with its expert's weights."""
+    rng = np.random.default_rng(61)
+    T, E, k, N, K, B = 10, 3, 2, 40, 96, 4
+    ws = [_integer_zp_expert(rng, N, K) for _ in range(E)]
+    bank = [quant_asym.quantize_pack_asym(bf16.rne(w)) for w in ws]
+    for w, (_, S, Z) in zip(ws, bank):
+        assert np.all(bf16.to_f32(S) == 1.0)
+        assert len(np.unique(Z)) > 8
+    x = rng.integers(-3, 4, size=(T, K)).astype(np.float32)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    s, ex, ntpp = moe.align(ids, E, B)
+    rows = moe.grouped_gemm(bf16.rne(x), lambda e: bank[e], s, ex, ntpp, B, k, T * k)
+    assert sorted(rows) == list(range(T * k))
+    for f in range(T * k):
+        e = int(ids.reshape(-1)[f])
+        assert np.array_equal(rows[f], x[f // k].astype(np.float64) @ ws[e].astype(np.float64).T)
+
+
+def test_layer_zero_point_reencoding_equals_symmetric():
+    """Symmetric codes re-encoded as unsigned q + 8 with z = 8 dequantize to
+    the same weights, so the whole layer output is unchanged."""
+    rng = np.random.default_rng(62)
+    T, E, k, H, I = 8, 4, 2, 64, 32
+    gu = _expert_bank(rng, E, 2 * I, H)
+    dn = _expert_bank(rng, E, H, I)
+
+    def reencode(Wq, S):
+        q = quant.unpack(Wq).astype(np.int16) + 8
+        return quant_asym.pack_unsigned(q.astype(np.uint8)), S, np.full(S.shape, 8, np.uint8)
+
+    gu_z = [reencode(*w) for w in gu]
+    dn_z = [reencode(*w) for w in dn]
+    X = bf16.rne(rng.standard_normal((T, H)).astype(np.float32))
+    ids, w = moe.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    ref = moe.moe_layer(X, ids, w, lambda e: gu[e], lambda e: dn[e])
+    got = moe.moe_layer(X, ids, w, lambda e: gu_z[e], lambda e: dn_z[e])
+    for t in range(T):
+        assert np.array_equal(got[t], ref[t])
