@@ -24,7 +24,8 @@ the other alignment block sizes (16 / 32 / 64 and 32 / 64), and the
 per-expert row distribution; and under
 "asym" the zero-point variants: the decode sweep and the prefill product
 with zero-point weights (one uint8 zero point per group on top of the
-scale), asymmetric quantize + pack and fake quant.
+scale), asymmetric quantize + pack and fake quant, and the two MoE layers
+with zero-point experts (whole fused layer and its two grouped products).
 
 The CPU oracle is timed on this host on whole decode steps (the same four
 products over the same weight shape) until at least 10 s have passed, as a
@@ -362,6 +363,46 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     return res
 
 
+def bench_moe_layer_asym(name, w4, wmoe, synth, torch, iters, timer):
+    """The routed layer with zero-point experts: the fused layer and its
+    two grouped products at the picked block size."""
+    wl = synth.WORKLOADS[name]
+    T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
+    dev = torch.device("cuda")
+    gate_up = wmoe.quantize_experts(E, 2 * I, H,
+                                    lambda e: synth.expert_gate_up(e, I, H, seed, dev), dev,
+                                    asym=True)
+    down = wmoe.quantize_experts(E, H, I, lambda e: synth.expert_down(e, I, H, seed, dev), dev,
+                                 asym=True)
+    X = synth.activations(T, H, seed, device=dev)
+    logits = synth.router_logits(T, E, seed, wl["skew"], device=dev)
+    B = w4.w4_pick_block_size(T, k, E)
+    ids, tw = w4.w4_moe_route(logits, k)
+    buf = wmoe.alloc_buffers(T, k, E, H, I, B, dev, fused=True)
+    w4.moe_align_block_size(ids, E, B, buf.sorted_token_ids, buf.expert_ids, buf.ntpp)
+    gu = lambda i: wmoe.grouped_gemm_swiglu(X, gate_up, buf.sorted_token_ids, buf.expert_ids,
+                                            buf.ntpp, T, k, B, k, out=buf.A)
+    dn = lambda i: wmoe.grouped_gemm(buf.A, down, buf.sorted_token_ids, buf.expert_ids,
+                                     buf.ntpp, T, k, B, 1, out=buf.H2)
+
+    def layer(i):   # route, align, gate_up + SwiGLU, down, combine
+        w4.w4_moe_route(logits, k, ids, tw)
+        wmoe.moe_forward(X, ids, tw, gate_up, down, B=B, buffers=buf)
+    timer.settle(layer)
+    t_layer = timer.run(layer, iters) / iters
+    t_gu = timer.run(gu, iters) / iters
+    t_dn = timer.run(dn, iters) / iters
+    fl = gemm_flops(T * k, 2 * I, H) + gemm_flops(T * k, H, I)
+    res = {"T": T, "E": E, "k": k, "H": H, "I": I, "B": B,
+           "layer_us": round(t_layer * 1e3, 1),
+           "gate_up_swiglu_us": round(t_gu * 1e3, 1), "down_us": round(t_dn * 1e3, 1),
+           "layer_TFLOP/s": round(fl / (t_layer * 1e-3) / 1e12, 1),
+           "weight_bytes": gate_up.nbytes() + down.nbytes()}
+    del gate_up, down, buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline():
     """The oracle, as it stands, on one full decode step on this host."""
     import numpy as np  # noqa: F401
@@ -437,6 +478,11 @@ def main():
     if "asym" in sections:
         log("bench: zero-point variants")
         detail["asym"] = bench_asym(w4, synth, torch, args.steps, args.warmup, iters, timer)
+        for name in ("moe_qwen", "moe_kimi"):
+            if name in sections:
+                log(f"bench: {name} with zero-point experts")
+                detail["asym"][name] = bench_moe_layer_asym(name, w4, wmoe, synth, torch, iters,
+                                                            timer)
 
     cpu = None
     if not args.no_cpu_baseline:

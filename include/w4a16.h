@@ -216,8 +216,8 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
 
 /*
  * w4a16_moe_gemm_swiglu -- the gate_up projection with the SwiGLU of
- * w4_silu_mul fused into its epilogue (NEXT step of [RL] §4's "MoE operator
- * fusion"; the activation is a reading, as for w4_silu_mul).  Wq / S hold
+ * w4_silu_mul fused into its epilogue (one more step of the MoE operator
+ * fusion of [RL] §4; the activation is a reading, as for w4_silu_mul).  Wq / S hold
  * 2I weight rows per expert: rows [0, I) gate, [I, 2I) up.  For every
  * valid slot (as in w4a16_moe_gemm, topk weights not applied):
  *   g = bf16_rne(X[f / x_row_div, :] * dequant(W_e[0:I])^T)
@@ -233,6 +233,29 @@ int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* 
                           const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
                           int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
                           int32_t x_row_div, void* stream);
+
+/*
+ * w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu_asym -- the two grouped
+ * products with zero-point experts ([QB] §2.1 inverse map x_hat = (q - z) s,
+ * §2.3 asymmetric quantization; [RL] §4 fused MoE):  every dequantized
+ * weight is  w'[n, k] = bf16_rne( (q[n, k] - Z[e, n, k/32]) * S[e, n, k/32] )
+ * (exact product) with q the unsigned nibbles of Wq[e], as
+ * w4_quantize_pack_asym writes them per expert.  Z uint8 [E, N, K/32]
+ * (N = 2I for the SwiGLU form), values in [0, 15] (other values: results
+ * undefined).  Every other argument, rule and limit as in w4a16_moe_gemm /
+ * w4a16_moe_gemm_swiglu; Z == NULL is W4_ERR_NULL.
+ */
+int w4a16_moe_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                        const uint8_t* Z, const int32_t* sorted_token_ids,
+                        const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                        const float* topk_weights, uint16_t* Y, int64_t T, int32_t k,
+                        int32_t E, int64_t N, int64_t K, int32_t B, int32_t x_row_div,
+                        void* stream);
+int w4a16_moe_gemm_swiglu_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                               const uint8_t* Z, const int32_t* sorted_token_ids,
+                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                               uint16_t* A, int64_t T, int32_t k, int32_t E, int64_t I,
+                               int64_t K, int32_t B, int32_t x_row_div, void* stream);
 
 /*
  * w4_silu_mul -- SwiGLU between the expert projections (a reading: the

@@ -11,7 +11,8 @@ Layouts (all row-major, contiguous, on one GPU):
   Wq      int32 [N, K/8]      nibble j of word w holds the INT4 code of k = 8w + j
   S       bf16  [N, K/32]     one scale per 32 consecutive k
   X       bf16  [M, K]        activations;  Y bf16 [M, N]
-  experts stacked on a leading axis: Wq [E, N, K/8], S [E, N, K/32]
+  Z       uint8 [N, K/32]     zero points (the asymmetric variants)
+  experts stacked on a leading axis: Wq [E, N, K/8], S [E, N, K/32], Z [E, N, K/32]
 """
 
 import torch
@@ -22,6 +23,7 @@ __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
     "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
+    "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
 ]
 
@@ -212,14 +214,9 @@ def moe_align_block_size(topk_ids, E, B, sorted_token_ids=None, expert_ids=None,
     return sorted_token_ids, expert_ids, num_tokens_post_padded
 
 
-def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                   T, k, B, x_row_div, topk_weights=None, out=None):
-    """Grouped expert product over aligned blocks.
-
-    Row f of ``out`` [T*k, N] = X[f // x_row_div] * dequant(Wq[e], S[e])^T
-    (times topk_weights.flat[f] when given) for every valid slot f of every
-    block b < ntpp / B with e = expert_ids[b].  Other rows are not written.
-    """
+def _moe_args(X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded, T, k, B,
+              x_row_div):
+    """Checks shared by the grouped products; returns (E, N, K)."""
     _need(X, "X", torch.bfloat16, 2)
     _need(Wq, "Wq", torch.int32, 3)
     _need(S, "S", torch.bfloat16, 3)
@@ -227,6 +224,10 @@ def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padde
     K = kw * 8
     if X.shape[1] != K or tuple(S.shape) != (E, N, K // 32):
         raise ValueError("shape mismatch between X, Wq and S")
+    if Z is not None:
+        _need(Z, "Z", torch.uint8, 3)
+        if tuple(Z.shape) != (E, N, K // 32):
+            raise ValueError("Z must be [E, N, K/32]")
     if X.shape[0] != (T * k) // x_row_div:
         raise ValueError("X must have T*k / x_row_div rows")
     for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
@@ -235,6 +236,13 @@ def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padde
     cap = w4_moe_align_capacity(T, k, E, B)
     if sorted_token_ids.numel() < cap or expert_ids.numel() < cap // B:
         raise ValueError("alignment buffers are smaller than the capacity")
+    return E, N, K
+
+
+def _moe_gemm(name, X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded, T, k, B,
+              x_row_div, topk_weights, out):
+    E, N, K = _moe_args(X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded, T, k,
+                        B, x_row_div)
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", torch.float32)
         if topk_weights.numel() != T * k:
@@ -245,11 +253,51 @@ def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padde
     if out.numel() != T * k * N:
         raise ValueError("out must be [T*k, N]")
     lib = _lib.load()
-    _lib.check("w4a16_moe_gemm", lib.w4a16_moe_gemm(
-        _ptr(X), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
-        _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, k, E, N, K, B,
-        x_row_div, _stream(X)))
+    head = (_ptr(X), _ptr(Wq), _ptr(S)) + (() if Z is None else (_ptr(Z),))
+    _lib.check(name, getattr(lib, name)(
+        *head, _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded),
+        _ptr(topk_weights), _ptr(out), T, k, E, N, K, B, x_row_div, _stream(X)))
     return out
+
+
+def _moe_gemm_swiglu(name, X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded, T,
+                     k, B, x_row_div, out):
+    E, N, K = _moe_args(X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded, T, k,
+                        B, x_row_div)
+    if N % 2:
+        raise ValueError("Wq must hold 2I rows per expert")
+    I = N // 2
+    if out is None:
+        out = torch.empty((T * k, I), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * k * I:
+        raise ValueError("out must be [T*k, I]")
+    lib = _lib.load()
+    head = (_ptr(X), _ptr(Wq), _ptr(S)) + (() if Z is None else (_ptr(Z),))
+    _lib.check(name, getattr(lib, name)(
+        *head, _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded),
+        _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
+    return out
+
+
+def w4a16_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                   T, k, B, x_row_div, topk_weights=None, out=None):
+    """Grouped expert product over aligned blocks.
+
+    Row f of ``out`` [T*k, N] = X[f // x_row_div] * dequant(Wq[e], S[e])^T
+    (times topk_weights.flat[f] when given) for every valid slot f of every
+    block b < ntpp / B with e = expert_ids[b].  Other rows are not written.
+    """
+    return _moe_gemm("w4a16_moe_gemm", X, Wq, S, None, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, T, k, B, x_row_div, topk_weights, out)
+
+
+def w4a16_moe_gemm_asym(X, Wq, S, Z, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                        T, k, B, x_row_div, topk_weights=None, out=None):
+    """``w4a16_moe_gemm`` with zero-point experts: Z uint8 [E, N, K/32] and
+    w' = bf16((q - z) s) from the unsigned codes of Wq."""
+    return _moe_gemm("w4a16_moe_gemm_asym", X, Wq, S, Z, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, T, k, B, x_row_div, topk_weights, out)
 
 
 def w4a16_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
@@ -261,34 +309,15 @@ def w4a16_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids, num_tokens_pos
     bf16 gate and up products of X[f // x_row_div], i.e. exactly
     w4_silu_mul(w4a16_moe_gemm(...)).  Other rows are not written.
     """
-    _need(X, "X", torch.bfloat16, 2)
-    _need(Wq, "Wq", torch.int32, 3)
-    _need(S, "S", torch.bfloat16, 3)
-    E, N, kw = Wq.shape
-    K = kw * 8
-    if N % 2:
-        raise ValueError("Wq must hold 2I rows per expert")
-    I = N // 2
-    if X.shape[1] != K or tuple(S.shape) != (E, N, K // 32):
-        raise ValueError("shape mismatch between X, Wq and S")
-    if X.shape[0] != (T * k) // x_row_div:
-        raise ValueError("X must have T*k / x_row_div rows")
-    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
-                 (num_tokens_post_padded, "num_tokens_post_padded")):
-        _need(t, n, torch.int32)
-    cap = w4_moe_align_capacity(T, k, E, B)
-    if sorted_token_ids.numel() < cap or expert_ids.numel() < cap // B:
-        raise ValueError("alignment buffers are smaller than the capacity")
-    if out is None:
-        out = torch.empty((T * k, I), dtype=torch.bfloat16, device=X.device)
-    _need(out, "out", torch.bfloat16)
-    if out.numel() != T * k * I:
-        raise ValueError("out must be [T*k, I]")
-    lib = _lib.load()
-    _lib.check("w4a16_moe_gemm_swiglu", lib.w4a16_moe_gemm_swiglu(
-        _ptr(X), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
-        _ptr(num_tokens_post_padded), _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
-    return out
+    return _moe_gemm_swiglu("w4a16_moe_gemm_swiglu", X, Wq, S, None, sorted_token_ids,
+                            expert_ids, num_tokens_post_padded, T, k, B, x_row_div, out)
+
+
+def w4a16_moe_gemm_swiglu_asym(X, Wq, S, Z, sorted_token_ids, expert_ids,
+                               num_tokens_post_padded, T, k, B, x_row_div, out=None):
+    """``w4a16_moe_gemm_swiglu`` with zero-point experts (Z uint8 [E, 2I, K/32])."""
+    return _moe_gemm_swiglu("w4a16_moe_gemm_swiglu_asym", X, Wq, S, Z, sorted_token_ids,
+                            expert_ids, num_tokens_post_padded, T, k, B, x_row_div, out)
 
 
 def w4_silu_mul(H1, out=None):

@@ -31,6 +31,10 @@ SIGNATURES = {
                                       _i64, _i64, _i32, _i32, _p]),
     "w4a16_moe_gemm_swiglu": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32,
                                              _i64, _i64, _i32, _i32, _p]),
+    "w4a16_moe_gemm_asym": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32,
+                                           _i32, _i64, _i64, _i32, _i32, _p]),
+    "w4a16_moe_gemm_swiglu_asym": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32,
+                                                  _i32, _i64, _i64, _i32, _i32, _p]),
     "w4_silu_mul": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
     "w4_moe_sum": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i64, _p]),
     "w4_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),

@@ -177,11 +177,17 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t T, int32_t k, int32_t 
                                      num_tokens_post_padded, as_stream(stream)));
 }
 
-int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                   const int32_t* num_tokens_post_padded, const float* topk_weights, uint16_t* Y,
-                   int64_t T, int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
-                   int32_t x_row_div, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and dispatch of the grouped products (Z == nullptr:
+// symmetric codes).  N is the weight rows per expert (2I with the SwiGLU).
+int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                     bool asym, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_padded, const float* topk_weights,
+                     uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                     int32_t B, int32_t x_row_div, bool swiglu, void* stream) {
   if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
   if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
   if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
@@ -192,16 +198,45 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
   if (!fits_buffer((T * k / x_row_div) * K * 2) || !fits_buffer(N * (K / 2)))
     return W4_ERR_UNSUPPORTED;
   if (T == 0) return W4_OK;
-  if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y)
+  if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y ||
+      (asym && !Z))
     return W4_ERR_NULL;
   if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2) || !aligned(Y, 4) ||
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
       !aligned(num_tokens_post_padded, 4) || !aligned(topk_weights, 4))
     return W4_ERR_MISALIGNED;
-  if (w4::moe_gemm_workgroups(T, k, E, N, B, false) >= kMaxI32) return W4_ERR_UNSUPPORTED;
-  return hip_status(w4::launch_moe_gemm(X, Wq, S, sorted_token_ids, expert_ids,
-                                        num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B,
-                                        x_row_div, as_stream(stream)));
+  if (w4::moe_gemm_workgroups(T, k, E, N, B, swiglu) >= kMaxI32) return W4_ERR_UNSUPPORTED;
+  if (swiglu)
+    return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, asym ? Z : nullptr, sorted_token_ids,
+                                                 expert_ids, num_tokens_post_padded, Y, T, k, E,
+                                                 N / 2, K, B, x_row_div, as_stream(stream)));
+  return hip_status(w4::launch_moe_gemm(X, Wq, S, asym ? Z : nullptr, sorted_token_ids,
+                                        expert_ids, num_tokens_post_padded, topk_weights, Y, T,
+                                        k, E, N, K, B, x_row_div, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, const float* topk_weights, uint16_t* Y,
+                   int64_t T, int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
+                   int32_t x_row_div, void* stream) {
+  return moe_gemm_checked(X, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B, x_row_div,
+                          false, stream);
+}
+
+int w4a16_moe_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                        const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                        const int32_t* num_tokens_post_padded, const float* topk_weights,
+                        uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                        int32_t B, int32_t x_row_div, void* stream) {
+  return moe_gemm_checked(X, Wq, S, Z, true, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B, x_row_div,
+                          false, stream);
 }
 
 int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
@@ -209,27 +244,23 @@ int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* 
                           const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
                           int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
                           int32_t x_row_div, void* stream) {
-  if (T < 0 || k < 1 || E < 1 || I < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
-  if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
-  if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
-  const int64_t N = 2 * I;
-  if (T * k + (int64_t)E * B >= kMaxI32 || N > kMaxI32 || K > kMaxI32 ||
-      (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
-    return W4_ERR_UNSUPPORTED;
-  // one buffer spans X's rows, one an expert's Wq
-  if (!fits_buffer((T * k / x_row_div) * K * 2) || !fits_buffer(N * (K / 2)))
-    return W4_ERR_UNSUPPORTED;
-  if (T == 0) return W4_OK;
-  if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !A)
-    return W4_ERR_NULL;
-  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(S, 2) || !aligned(A, 4) ||
-      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
-      !aligned(num_tokens_post_padded, 4))
-    return W4_ERR_MISALIGNED;
-  if (w4::moe_gemm_workgroups(T, k, E, N, B, true) >= kMaxI32) return W4_ERR_UNSUPPORTED;
-  return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, sorted_token_ids, expert_ids,
-                                               num_tokens_post_padded, A, T, k, E, I, K, B,
-                                               x_row_div, as_stream(stream)));
+  if (I < 1) return W4_ERR_SHAPE;
+  const int64_t N = I > kMaxI32 ? kMaxI32 + 1 : 2 * I;   // past the limit: unsupported
+  return moe_gemm_checked(X, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, nullptr, A, T, k, E, N, K, B, x_row_div,
+                          true, stream);
+}
+
+int w4a16_moe_gemm_swiglu_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                               const uint8_t* Z, const int32_t* sorted_token_ids,
+                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                               uint16_t* A, int64_t T, int32_t k, int32_t E, int64_t I, int64_t K,
+                               int32_t B, int32_t x_row_div, void* stream) {
+  if (I < 1) return W4_ERR_SHAPE;
+  const int64_t N = I > kMaxI32 ? kMaxI32 + 1 : 2 * I;   // past the limit: unsupported
+  return moe_gemm_checked(X, Wq, S, Z, true, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, nullptr, A, T, k, E, N, K, B, x_row_div,
+                          true, stream);
 }
 
 int w4_silu_mul(const uint16_t* H1, uint16_t* A, int64_t R, int64_t I, void* stream) {

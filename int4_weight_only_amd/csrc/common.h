@@ -142,13 +142,15 @@ hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* 
 hipError_t launch_gemv_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st);
+// grouped products: Z == nullptr for symmetric codes, else Z [E, N, K/32]
 hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                           const int32_t* sorted_ids, const int32_t* expert_ids,
+                           const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                            int32_t x_row_div, hipStream_t st);
 hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                                  const int32_t* sorted_ids, const int32_t* expert_ids,
+                                  const uint8_t* Z, const int32_t* sorted_ids,
+                                  const int32_t* expert_ids,
                                   const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
                                   int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
                                   hipStream_t st);

@@ -59,8 +59,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
 // take gate rows [c, c + 2 WN) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
-// ZP (dense only): zero-point weights, unsigned codes and one zero point
-// byte per group in Z [N, K/32]; w' = bf16((q - z) s).
+// ZP: zero-point weights, unsigned codes and one zero point byte per group
+// in Z [N, K/32] (grouped: Z [E, N, K/32]); w' = bf16((q - z) s).
 // BM = 32 (one MFMA row tile, few rows per expert): four code register sets
 // and four to six workgroups per CU keep more weight bytes in flight, and
 // workgroups index runs rather than blocks.
@@ -143,7 +143,6 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     tile_n = in_group / gm;
   }
   static_assert(!SWI || (MOE && NW == 4), "fused SwiGLU: grouped product, four waves");
-  static_assert(!ZP || !MOE, "zero points: dense product");
   const int n_base = SWI ? (wave >> 1) * (N >> 1) + tile_n * (2 * WN) + (wave & 1) * WN
                          : tile_n * (NW * WN) + wave * WN;
   const int G = K >> 5;
@@ -273,7 +272,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
   const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
-  const __amdgpu_buffer_rsrc_t zr = rsrc(Z, ZP ? (uint32_t)N * (uint32_t)G : 0u);
+  const uint8_t* Zbase = ZP ? Z + (int64_t)expert * N * G : nullptr;
+  const __amdgpu_buffer_rsrc_t zr = rsrc(Zbase, ZP ? (uint32_t)N * (uint32_t)G : 0u);
 
   {
     // ---- row tables (thread r < BM fills row r)
@@ -709,9 +709,9 @@ int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t 
 }
 
 namespace {
-template <int BM, int WN, bool SWI>
+template <int BM, int WN, bool SWI, bool ZP>
 hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                           int32_t x_row_div, hipStream_t st) {
@@ -720,46 +720,60 @@ hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t
   const dim3 grid((unsigned)(ntn * moe_gemm_slots(T, k, E, B)));
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI>), grid, dim3(kNW * 64), 0, st, X,
-                       (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI, ZP>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
                        expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   else
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI>), grid, dim3(kNW * 64), 0, st, X,
-                       (const uint32_t*)Wq, S, nullptr, Y, 0, (int)N, (int)K, sorted_ids,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI, ZP>), grid, dim3(kNW * 64), 0, st, X,
+                       (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
                        expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
 }
 
+template <bool SWI, bool ZP>
+hipError_t launch_grouped_z(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                            const uint8_t* Z, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* ntpp, const float* topk_w,
+                            uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                            int32_t B, int32_t x_row_div, hipStream_t st) {
+  if (moe_tile_rows(T, k, E, B) == kBMMoeSmall)
+    return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI, ZP>(
+        X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N, K, B, x_row_div, st);
+  return launch_grouped_t<kBMMoe, kWN, SWI, ZP>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w,
+                                                Y, T, k, E, N, K, B, x_row_div, st);
+}
+
+// Z == nullptr: symmetric codes; else zero-point codes with Z [E, N, K/32]
 template <bool SWI>
 hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                           int32_t x_row_div, hipStream_t st) {
-  if (moe_tile_rows(T, k, E, B) == kBMMoeSmall)
-    return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y,
-                                              T, k, E, N, K, B, x_row_div, st);
-  return launch_grouped_t<kBMMoe, kWN, SWI>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k,
-                                       E, N, K, B, x_row_div, st);
+  if (Z != nullptr)
+    return launch_grouped_z<SWI, true>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T,
+                                       k, E, N, K, B, x_row_div, st);
+  return launch_grouped_z<SWI, false>(X, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, topk_w, Y,
+                                      T, k, E, N, K, B, x_row_div, st);
 }
 }  // namespace
 
 hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                           const int32_t* sorted_ids, const int32_t* expert_ids,
+                           const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
                            int32_t x_row_div, hipStream_t st) {
-  return launch_grouped<false>(X, Wq, S, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N, K,
-                               B, x_row_div, st);
+  return launch_grouped<false>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N,
+                               K, B, x_row_div, st);
 }
 
 hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
-                                  const int32_t* sorted_ids, const int32_t* expert_ids,
-                                  const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
-                                  int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
-                                  hipStream_t st) {
-  return launch_grouped<true>(X, Wq, S, sorted_ids, expert_ids, ntpp, nullptr, A, T, k, E, 2 * I,
-                              K, B, x_row_div, st);
+                                  const uint8_t* Z, const int32_t* sorted_ids,
+                                  const int32_t* expert_ids, const int32_t* ntpp, uint16_t* A,
+                                  int64_t T, int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
+                                  int32_t x_row_div, hipStream_t st) {
+  return launch_grouped<true>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, nullptr, A, T, k, E,
+                              2 * I, K, B, x_row_div, st);
 }
 
 }  // namespace w4

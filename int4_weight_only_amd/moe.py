@@ -13,7 +13,9 @@ moe_align_block_size, the fused expert GEMMs):
 
 The activation (silu(gate) * up, gate = the first I rows of gate_up) and
 the combine (weights applied after the down projection) are readings: the
-pages name the gate_up / down pair but give no formula.
+pages name the gate_up / down pair but give no formula.  Experts quantized
+with zero points ("Quantization basics: from FP32 to INT4" §2.3) run the
+``_asym`` forms of the two grouped products.
 """
 
 from dataclasses import dataclass
@@ -21,15 +23,18 @@ from dataclasses import dataclass
 import torch
 
 from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
-               w4_pick_block_size, w4_quantize_pack, w4_silu_mul, w4a16_moe_gemm,
-               w4a16_moe_gemm_swiglu)
+               w4_pick_block_size, w4_quantize_pack, w4_quantize_pack_asym, w4_silu_mul,
+               w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
+               w4a16_moe_gemm_swiglu_asym)
 
 
 @dataclass
 class ExpertWeights:
-    """Stacked packed weights of E experts: Wq int32 [E, N, K/8], S bf16 [E, N, K/32]."""
+    """Stacked packed weights of E experts: Wq int32 [E, N, K/8], S bf16 [E, N, K/32],
+    and for zero-point experts Z uint8 [E, N, K/32] (None: symmetric codes)."""
     Wq: torch.Tensor
     S: torch.Tensor
+    Z: torch.Tensor = None
 
     @property
     def E(self):
@@ -44,22 +49,47 @@ class ExpertWeights:
         return self.Wq.shape[2] * 8
 
     def nbytes(self):
-        return self.Wq.numel() * 4 + self.S.numel() * 2
+        z = 0 if self.Z is None else self.Z.numel()
+        return self.Wq.numel() * 4 + self.S.numel() * 2 + z
 
 
-def quantize_experts(E, N, K, source, device):
+def quantize_experts(E, N, K, source, device, asym=False):
     """Quantize E expert matrices one at a time into stacked buffers.
 
     ``source(e)`` returns expert e's bf16 [N, K] weight on ``device``; only
-    one source matrix is alive at a time.
+    one source matrix is alive at a time.  ``asym``: zero-point codes
+    (``w4_quantize_pack_asym``).
     """
     Wq = torch.empty((E, N, K // 8), dtype=torch.int32, device=device)
     S = torch.empty((E, N, K // 32), dtype=torch.bfloat16, device=device)
+    Z = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device) if asym else None
     for e in range(E):
         w = source(e)
-        w4_quantize_pack(w, Wq[e], S[e])
+        if asym:
+            w4_quantize_pack_asym(w, Wq[e], S[e], Z[e])
+        else:
+            w4_quantize_pack(w, Wq[e], S[e])
         del w
-    return ExpertWeights(Wq, S)
+    return ExpertWeights(Wq, S, Z)
+
+
+def grouped_gemm(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div,
+                 topk_weights=None, out=None):
+    """``w4a16_moe_gemm`` or its zero-point form, as the experts ``w`` need."""
+    if w.Z is None:
+        return w4a16_moe_gemm(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
+                              x_row_div, topk_weights, out)
+    return w4a16_moe_gemm_asym(X, w.Wq, w.S, w.Z, sorted_token_ids, expert_ids, ntpp, T, k, B,
+                               x_row_div, topk_weights, out)
+
+
+def grouped_gemm_swiglu(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div, out=None):
+    """``w4a16_moe_gemm_swiglu`` or its zero-point form, as the experts ``w`` need."""
+    if w.Z is None:
+        return w4a16_moe_gemm_swiglu(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
+                                     x_row_div, out)
+    return w4a16_moe_gemm_swiglu_asym(X, w.Wq, w.S, w.Z, sorted_token_ids, expert_ids, ntpp, T,
+                                      k, B, x_row_div, out)
 
 
 @dataclass
@@ -103,16 +133,15 @@ def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None, 
     b = buffers or alloc_buffers(T, k, E, H, I, B, X.device, fused)
     moe_align_block_size(topk_ids, E, B, b.sorted_token_ids, b.expert_ids, b.ntpp)
     if fused:
-        w4a16_moe_gemm_swiglu(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids,
-                              b.ntpp, T, k, B, k, out=b.A)
+        grouped_gemm_swiglu(X, gate_up, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, k,
+                            out=b.A)
     else:
         if b.H1 is None:
             raise ValueError("the unfused path needs buffers with H1 (fused=False)")
-        w4a16_moe_gemm(X, gate_up.Wq, gate_up.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
-                       T, k, B, k, out=b.H1)
+        grouped_gemm(X, gate_up, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, k,
+                     out=b.H1)
         w4_silu_mul(b.H1, out=b.A)
-    w4a16_moe_gemm(b.A, down.Wq, down.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
-                   T, k, B, 1, out=b.H2)
+    grouped_gemm(b.A, down, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, 1, out=b.H2)
     w4_moe_sum(b.H2, topk_weights, T, k, out=b.out)
     return b.out, b
 

@@ -256,6 +256,38 @@ def test_moe_gemm_swiglu_validation(lib):
     assert f(*bad_al, 4, 2, 8, 32, 64, 16, 1, None) == MISALIGNED
 
 
+def test_moe_gemm_asym_validation(lib):
+    f = lib.w4a16_moe_gemm_asym
+    good = [A16, A16, A2, A1, A4, A4, A4, None, A4]           # Z: any alignment
+    assert f(*good, 4, 2, 8, 64, 48, 16, 1, None) == SHAPE        # K % 32
+    assert f(*good, 4, 2, 8, 64, 64, 16, 3, None) == SHAPE        # x_row_div
+    assert f(*good, 4, 2, 2000, 64, 64, 16, 1, None) == UNSUPPORTED
+    assert f(*good, 4, 2, 8, 1 << 20, 4096, 16, 1, None) == UNSUPPORTED   # an expert = 2 GiB
+    assert f(*good, 0, 2, 8, 64, 64, 16, 1, None) == OK           # T == 0: no-op
+    no_z = list(good)
+    no_z[3] = None
+    assert f(*no_z, 4, 2, 8, 64, 64, 16, 1, None) == NULL
+    bad_al = list(good)
+    bad_al[1] = A4
+    assert f(*bad_al, 4, 2, 8, 64, 64, 16, 1, None) == MISALIGNED
+
+
+def test_moe_gemm_swiglu_asym_validation(lib):
+    f = lib.w4a16_moe_gemm_swiglu_asym
+    good = [A16, A16, A2, A1, A4, A4, A4, A4]
+    assert f(*good, 4, 2, 8, 32, 48, 16, 1, None) == SHAPE        # K % 32
+    assert f(*good, 4, 2, 8, 0, 64, 16, 1, None) == SHAPE         # I
+    assert f(*good, 4, 2, 8, 1 << 19, 4096, 16, 1, None) == UNSUPPORTED   # 2I rows = 2 GiB
+    assert f(*good, 4, 2, 8, 1 << 40, 64, 16, 1, None) == UNSUPPORTED     # 2I past int32
+    assert f(*good, 0, 2, 8, 32, 64, 16, 1, None) == OK           # T == 0: no-op
+    no_z = list(good)
+    no_z[3] = None
+    assert f(*no_z, 4, 2, 8, 32, 64, 16, 1, None) == NULL
+    bad_al = list(good)
+    bad_al[7] = A2
+    assert f(*bad_al, 4, 2, 8, 32, 64, 16, 1, None) == MISALIGNED
+
+
 def test_elementwise_validation(lib):
     assert lib.w4_silu_mul(A4, A4, 4, 3, None) == SHAPE
     assert lib.w4_silu_mul(None, A4, 4, 4, None) == NULL
