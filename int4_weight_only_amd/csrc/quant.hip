@@ -18,6 +18,36 @@
 
 namespace w4 {
 
+namespace {
+
+// rint_half_even(w / s) for bf16 values w, s with s in [2^-110, 2^100],
+// equal to rounding the IEEE fp32 quotient and then to an integer, in four
+// VALU ops instead of a full IEEE division.  With r = rcp(s) (1 ulp):
+//   y0 = w r  is w / s to ~2^-22 relative;
+//   e  = w - y0 s  is exact (an fma; |e| needs ~11 bits on the grid of
+//       y0 s, and that grid does not underflow for |w / s| >= 1/2 and
+//       s >= 2^-110);
+//   y1 = y0 + e r  is w / s to ~2^-42 absolute for |w / s| <= 16 (one
+//       Newton correction of the quotient, as in Markstein's division).
+// The rounded integer can only differ from that of the exact quotient where
+// w / s is a half-integer or very close to one.  For bf16 operands w / s is
+// either exactly a half-integer (a tie) or at least 2^-10 away from every
+// half-integer (the distance is a nonzero integer over 4 * 2^8), so y1
+// rounds to the tie exactly, rintf sends it to the even neighbour, and every
+// other quotient rounds like the exact one.  Outside the range of s (and for
+// s = 0) the callers divide.
+__device__ __forceinline__ float rint_quot(float w, float s, float r) {
+  const float y0 = w * r;
+  const float e = __builtin_fmaf(-y0, s, w);
+  return rintf(__builtin_fmaf(e, r, y0));
+}
+
+__device__ __forceinline__ bool quot_fast(float s) {
+  return s >= 0x1p-110f && s <= 0x1p100f;
+}
+
+}  // namespace
+
 // ASYM: "Quantization basics" §2.3 with the readings of the asymmetric
 // oracle: unsigned grid [0, 15], range widened to contain 0,
 // s = bf16(fp32(x_max - x_min) / 15), z = clamp(rint(-x_min / s), 0, 15),
@@ -35,7 +65,7 @@ __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, i
   const u32x4 v = W[i];
   const float w[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-  float s, zf = 0.0f;
+  float s, zf = 0.0f, lo_g = 0.0f;
   uint16_t sb;
   if constexpr (!ASYM) {
     // For finite bf16, |w| orders like its 15-bit magnitude field.
@@ -59,18 +89,32 @@ __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, i
     hi = fmaxf(hi, __uint_as_float(quad_xor2(__float_as_uint(hi))));
     lo = fminf(lo, 0.0f);                      // the grid always holds 0
     hi = fmaxf(hi, 0.0f);
+    lo_g = lo;
     sb = to_bf16((hi - lo) / 15.0f);           // fp32 subtraction, IEEE division, RNE
     s = bf16f(sb);
-    zf = (s == 0.0f) ? 0.0f : fminf(fmaxf(rintf(0.0f - lo / s), 0.0f), 15.0f);
   }
+  // rint_even(w / s) for the group's elements (and the zero point's
+  // rint_even(-lo / s)): the corrected reciprocal product where s allows,
+  // else IEEE division
+  float rq[8], rz = 0.0f;
+  if (quot_fast(s)) {
+    const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rq[j] = rint_quot(w[j], s, r);
+    if constexpr (ASYM) rz = rint_quot(0.0f - lo_g, s, r);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rq[j] = rintf(w[j] / s);
+    if constexpr (ASYM) rz = rintf((0.0f - lo_g) / s);
+  }
+  if constexpr (ASYM) zf = (s == 0.0f) ? 0.0f : fminf(fmaxf(rz, 0.0f), 15.0f);
   float q[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float r = rintf(w[j] / s);         // IEEE division, half to even
     if constexpr (!ASYM)
-      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r, -8.0f), 7.0f);
+      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(rq[j], -8.0f), 7.0f);
     else
-      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(r + zf, 0.0f), 15.0f);
+      q[j] = (s == 0.0f) ? 0.0f : fminf(fmaxf(rq[j] + zf, 0.0f), 15.0f);
   }
   if constexpr (!FAKE) {
     uint32_t word = 0;
