@@ -52,7 +52,8 @@ __device__ __forceinline__ bool quot_fast(float s) {
 // oracle: unsigned grid [0, 15], range widened to contain 0,
 // s = bf16(fp32(x_max - x_min) / 15), z = clamp(rint(-x_min / s), 0, 15),
 // q = clamp(rint(w / s) + z, 0, 15), dequant bf16((q - z) s); z is one byte
-// per group.  Every division is IEEE fp32, every rint half to even.
+// per group.  The scale is an IEEE fp32 division; every rint (half to even)
+// of a quotient equals that of the IEEE fp32 quotient (rint_quot).
 template <bool FAKE, bool ASYM>
 __global__ __launch_bounds__(256) void k_quantize(const u32x4* __restrict__ W, int64_t words,
                                                   uint32_t* __restrict__ Wq,
