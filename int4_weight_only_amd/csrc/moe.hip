@@ -168,52 +168,90 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
 // descending logit order (ties: lower index); the weights are
 // exp(l_j - l_0) / sum_i exp(l_i - l_0) over the picked logits, which equals
 // the softmax over all experts renormalised to the picked set.
-constexpr int kRouteMaxPerLane = kMaxExperts / 64;
+//
+// Each candidate is one 64-bit key that orders like (logit, -index): the
+// high word maps the fp32 logit to an unsigned integer of the same order
+// (sign set: all bits flipped; else the sign bit set), the low word is
+// ~index (-0 counts as +0).  A removed pick and a NaN logit get key 0, below every real key
+// (-inf included), so they are never picked again while any expert is left.
+// The wave maximum of the keys takes two DPP quad swaps and the two DPP
+// mirrors within each 16-lane row, then v_permlane16_swap and
+// v_permlane32_swap across rows: no LDS round trip.
+namespace {
 
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v + 0.0f);   // -0 -> +0: equal logits tie on the index
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (v != v) ? 0ull : ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t a) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)a, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(a >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t b = ((uint64_t)hi << 32) | lo;
+  return b > a ? b : a;
+}
+
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t a) {
+  a = dpp_max<0xB1>(a);     // quad_perm [1, 0, 3, 2]
+  a = dpp_max<0x4E>(a);     // quad_perm [2, 3, 0, 1]
+  a = dpp_max<0x141>(a);    // row_half_mirror: the other quad of each 8 lanes
+  a = dpp_max<0x140>(a);    // row_mirror: the other 8 lanes of each row
+  {
+    // rows (0, 1) and (2, 3): each lane meets the same lane of the paired row
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)a, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(a >> 32),
+                                                    false, false);
+    const uint64_t x = ((uint64_t)h[0] << 32) | l[0], y = ((uint64_t)h[1] << 32) | l[1];
+    a = x > y ? x : y;
+  }
+  {
+    // rows (0, 1) with (2, 3)
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)a, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(a >> 32),
+                                                    false, false);
+    const uint64_t x = ((uint64_t)h[0] << 32) | l[0], y = ((uint64_t)h[1] << 32) | l[1];
+    a = x > y ? x : y;
+  }
+  return a;
+}
+
+}  // namespace
+
+// NPER: candidates per lane (E <= 64 NPER)
+template <int NPER>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
                                                int k, int32_t* __restrict__ ids,
                                                float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= T) return;   // whole waves: every lane of a live wave takes part below
   const float* row = logits + (int64_t)t * E;
-  float v[kRouteMaxPerLane];
+  uint64_t key[NPER];
 #pragma unroll
-  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? row[e] : -__builtin_inff();
+    key[i] = (e < E) ? route_key(row[e], e) : 0ull;
   }
   float picked[16];
   int picked_id[16];
   for (int j = 0; j < k; ++j) {
-    // lane-local best (first index wins on ties: i ascending = index ascending)
-    float best = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > best || (v[i] == best && e < bi))) {
-        best = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ob = __shfl_xor(best, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-      }
-    }
-    picked[j] = best;
+    for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_key(best);
+    const int bi = (int)~(uint32_t)best;
+    picked[j] = key_value(best);
     picked_id[j] = bi;
-    // remove the pick: NaN is never greater than nor equal to anything, so
-    // a removed expert cannot be picked again even when the rest are -inf
-    // (masked experts); those then follow in index order
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i)
-      if (lane + 64 * i == bi) v[i] = __builtin_nanf("");
+    for (int i = 0; i < NPER; ++i)
+      if (lane + 64 * i == bi) key[i] = 0ull;
   }
   if (lane == 0) {
     float sum = 0.0f;
@@ -227,9 +265,17 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 
 hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
                         float* w, hipStream_t st) {
-  const int64_t blocks = (T + 3) / 4;
-  hipLaunchKernelGGL(k_route, dim3((unsigned)blocks), dim3(256), 0, st, logits, (int)T, (int)E,
-                     (int)k, ids, w);
+  const dim3 g((unsigned)((T + 3) / 4)), b(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_route<1>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_route<2>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_route<4>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_route<8>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
+  else
+    hipLaunchKernelGGL(k_route<16>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
   return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ def test_align_bit_exact(case):
 
 @pytest.mark.parametrize("T,E,k,kind", [(256, 128, 8, "qwen"), (4096, 384, 8, "kimi"),
                                         (33, 5, 5, "rand"), (17, 1000, 16, "rand"),
-                                        (10, 64, 1, "rand"), (6, 32, 4, "ties")])
+                                        (10, 64, 1, "rand"), (9, 200, 6, "rand"),
+                                        (6, 32, 4, "ties")])
 def test_route(T, E, k, kind):
     say(f"route {kind} T={T} E={E} k={k}")
     if kind == "qwen":
@@ -112,9 +113,9 @@ def test_route(T, E, k, kind):
 
 def test_route_masked_and_tied_logits():
     """Rows with fewer finite logits than k (masked experts at -inf), all
-    -inf, and all equal: the ids are distinct and follow (logit desc, index
-    asc), as the oracle orders them."""
-    T, E, k = 6, 40, 8
+    -inf, all equal, and -0 beside +0 (equal logits): the ids are distinct
+    and follow (logit desc, index asc), as the oracle orders them."""
+    T, E, k = 7, 40, 8
     lg = np.zeros((T, E), np.float32)
     lg[0, :] = -np.inf                                  # all masked
     lg[1, :] = -np.inf
@@ -123,6 +124,8 @@ def test_route_masked_and_tied_logits():
     lg[3, :] = np.linspace(-1, 1, E)[::-1]
     lg[4, ::2] = -np.inf
     lg[5, :] = np.random.default_rng(3).normal(size=E)
+    lg[6, :] = -1.0
+    lg[6, [3, 9, 20, 33]] = [-0.0, 0.0, -0.0, 0.0]
     ids_ref, w_ref = omoe.route(lg, k)
     ids, w = w4.w4_moe_route(up(lg), k)
     ids = down(ids)
