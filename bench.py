@@ -197,6 +197,15 @@ def bench_quant(w4, synth, torch, iters, timer):
         gbs = nbytes / (t * 1e-3) / 1e9
         out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "bytes": nbytes,
                      "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    # the QAT linear forward (pack W, then the W4A16 product on the codes)
+    from int4_weight_only_amd.qat import qat_linear
+    qat = {}
+    for M in (16, wl["M"][0]):
+        X = synth.activations(M, K, wl["seed"], device=dev)
+        fn = lambda i, X=X: qat_linear(X, W)
+        timer.settle(fn, SETTLE_MS / 3)
+        qat[str(M)] = round(timer.run(fn, iters) / iters * 1e3, 1)
+    out["qat_linear_forward_us_by_M"] = qat
     return out
 
 
@@ -251,6 +260,15 @@ def bench_asym(w4, synth, torch, steps, warmup, iters, timer):
         gbs = nbytes / (t * 1e-3) / 1e9
         out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "bytes": nbytes,
                      "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    # the QAT linear forward (pack W, then the W4A16 product on the codes)
+    from int4_weight_only_amd.qat import qat_linear
+    qat = {}
+    for M in (16, wl["M"][0]):
+        X = synth.activations(M, K, wl["seed"], device=dev)
+        fn = lambda i, X=X: qat_linear(X, W)
+        timer.settle(fn, SETTLE_MS / 3)
+        qat[str(M)] = round(timer.run(fn, iters) / iters * 1e3, 1)
+    out["qat_linear_forward_us_by_M"] = qat
     return out
 
 

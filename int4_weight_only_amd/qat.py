@@ -13,13 +13,23 @@ anything and equals the identity.
 The master weight stays bf16; only the forward sees the quantization grid,
 so training and INT4 inference use the same values (fake quant equals the
 dequantized packed weight bit for bit).
+
+``qat_linear`` is the layer form: y = x * fake_quant(W)^T.  Because the
+dequantized packed weight equals the fake-quantized one bit for bit, its
+forward packs W (``w4_quantize_pack``) and runs the W4A16 product on the
+codes ("INT4 QAT end-to-end for RL" §4) instead of writing W_fq and reading
+it back: 3.125 bytes of weight traffic per element (read W, write and read
+0.5625 bytes of codes and scales) instead of 6 (read W, write W_fq, read
+W_fq).  The backward is the straight-through estimator
+with two plain bf16 library GEMMs: dX = dY * W_fq (W_fq recomputed by
+``w4_fake_quant``) and dW = dY^T * X.
 """
 
 import torch
 
-from . import w4_fake_quant
+from . import w4_fake_quant, w4_quantize_pack, w4a16_gemm
 
-__all__ = ["FakeInt4STE", "fake_quant_ste"]
+__all__ = ["FakeInt4STE", "fake_quant_ste", "Int4QATLinear", "qat_linear"]
 
 
 class FakeInt4STE(torch.autograd.Function):
@@ -38,3 +48,39 @@ def fake_quant_ste(W):
     """Fake-quantized bf16 weight [N, K] (K % 32 == 0) whose gradient flows
     straight through to W."""
     return FakeInt4STE.apply(W)
+
+
+class Int4QATLinear(torch.autograd.Function):
+    """y = x * fake_quant(W)^T through the packed INT4 product; straight-through
+    backward to the bf16 master weight."""
+
+    @staticmethod
+    def forward(ctx, X, W):
+        N, K = W.shape
+        if X.shape[-1] != K:
+            raise ValueError(f"X has {X.shape[-1]} features, W expects {K}")
+        W = W.contiguous()
+        X2 = X.reshape(-1, K).contiguous()
+        Wq, S = w4_quantize_pack(W)
+        Y = w4a16_gemm(X2, Wq, S)
+        ctx.save_for_backward(X2, W)
+        ctx.x_shape = X.shape
+        return Y.reshape(*X.shape[:-1], N)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        X2, W = ctx.saved_tensors
+        N = W.shape[0]
+        dY = grad_out.reshape(-1, N).to(torch.bfloat16).contiguous()
+        dX = dW = None
+        if ctx.needs_input_grad[0]:
+            dX = torch.mm(dY, w4_fake_quant(W)).reshape(ctx.x_shape)
+        if ctx.needs_input_grad[1]:
+            dW = torch.mm(dY.t().contiguous(), X2)
+        return dX, dW
+
+
+def qat_linear(X, W):
+    """QAT linear layer without bias: X bf16 [..., K], W bf16 [N, K]
+    (K % 32 == 0) -> bf16 [..., N] = X * fake_quant(W)^T."""
+    return Int4QATLinear.apply(X, W)

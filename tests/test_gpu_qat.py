@@ -1,9 +1,13 @@
-"""GPU: the QAT op (fake quant forward, straight-through backward).
+"""GPU: the QAT ops (fake quant forward, straight-through backward).
 
 Forward: bit-exact against the oracle's fake quant.  Backward: the
 straight-through estimator passes the upstream gradient unchanged to the
 bf16 master weight (grad_W == grad_out bit for bit), also through a small
-linear layer whose loss depends on the fake-quantized weight.
+linear layer whose loss depends on the fake-quantized weight.  The QAT
+linear layer (forward through the packed INT4 product): forward within
+|y - y_ref| <= 2e-2 + 1e-2 |y_ref| of the fp64 product with the oracle's
+fake-quantized weight, and both gradients of the straight-through estimator
+against fp64 references.
 """
 
 import numpy as np
@@ -13,7 +17,7 @@ import torch
 import synth
 from gpu_util import dev, down_bits, say, up_bits
 from int4_weight_only_amd.qat import fake_quant_ste
-from oracle import quant
+from oracle import bf16, gemm, quant
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +62,49 @@ def test_gradient_through_a_linear_layer():
     # and the forward used the quantization grid
     ref = quant.fake_quant(synth.bits(W.detach().to(torch.bfloat16).cpu()))
     np.testing.assert_array_equal(synth.bits(Wq.detach().to(torch.bfloat16)), ref)
+
+
+# ------------------------------------------------------------ QAT linear --
+
+ATOL, RTOL = 2e-2, 1e-2
+
+
+@pytest.mark.parametrize("shape,N,K", [((1, 544), 96, 544), ((16, 256), 200, 256),
+                                       ((33, 512), 64, 512), ((2, 150, 160), 48, 160)])
+def test_qat_linear_forward_matches_oracle(shape, N, K):
+    """Forward = X * fake_quant(W)^T, the fake-quantized weight from the
+    oracle's own quantizer, fp64 product; decode (M <= 32) and tiled (M > 32)
+    products both run."""
+    from int4_weight_only_amd.qat import qat_linear
+    say(f"qat_linear forward X{shape} N={N} K={K}")
+    Wb = synth.bits(synth.weights(N, K, 31))
+    Xb = synth.bits(synth.activations(int(np.prod(shape[:-1])), K, 32)).reshape(*shape)
+    Y = qat_linear(up_bits(Xb), up_bits(Wb))
+    assert tuple(Y.shape) == tuple(shape[:-1]) + (N,)
+    wfq = bf16.to_f32(quant.fake_quant(Wb)).astype(np.float64)
+    ref = bf16.to_f32(Xb.reshape(-1, K)).astype(np.float64) @ wfq.T
+    ok, a, r = gemm.within_tolerance(down_bits(Y).reshape(-1, N), ref, ATOL, RTOL)
+    assert ok, (a, r)
+
+
+def test_qat_linear_backward_is_straight_through():
+    """dX = dY * fake_quant(W) and dW = dY^T * X (the estimator passes the
+    gradient of the quantized weight to the master weight)."""
+    from int4_weight_only_amd.qat import qat_linear
+    say("qat_linear backward")
+    M, N, K = 40, 64, 128
+    Wb = synth.bits(synth.weights(N, K, 41))
+    Xb = synth.bits(synth.activations(M, K, 42))
+    Gb = synth.bits(synth.activations(M, N, 43))
+    W = up_bits(Wb).requires_grad_(True)
+    X = up_bits(Xb).requires_grad_(True)
+    Y = qat_linear(X, W)
+    Y.backward(up_bits(Gb))
+    torch.cuda.synchronize()
+    g = bf16.to_f32(Gb).astype(np.float64)
+    x = bf16.to_f32(Xb).astype(np.float64)
+    wfq = bf16.to_f32(quant.fake_quant(Wb)).astype(np.float64)
+    for got, ref, name in ((X.grad, g @ wfq, "dX"), (W.grad, g.T @ x, "dW")):
+        assert got.dtype == torch.bfloat16
+        ok, a, r = gemm.within_tolerance(down_bits(got), ref, ATOL, RTOL)
+        assert ok, (name, a, r)
