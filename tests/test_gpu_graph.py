@@ -85,17 +85,18 @@ def test_quantize_graph_replay():
         np.testing.assert_array_equal(down_bits(Wf), down_bits(w4.w4_fake_quant(W)))
 
 
-@pytest.mark.parametrize("T,E,k", [(64, 16, 4), (7, 8, 2)])
-def test_moe_layer_graph_replay(T, E, k):
+@pytest.mark.parametrize("T,E,k,asym", [(64, 16, 4, False), (7, 8, 2, False), (64, 16, 4, True)])
+def test_moe_layer_graph_replay(T, E, k, asym):
     """Routing, alignment, the fused gate_up + SwiGLU, down and combine in
     one graph (the block count lives on the device, so the launches do not
-    depend on the routing)."""
+    depend on the routing); symmetric and zero-point experts."""
     H, I, seed = 512, 256, 11
-    say(f"graph moe T={T} E={E} k={k}")
+    say(f"graph moe T={T} E={E} k={k} asym={asym}")
     gate_up = wmoe.quantize_experts(
-        E, 2 * I, H, lambda e: synth.weights(2 * I, H, seed, stream=500 + e, device=DEV), DEV)
+        E, 2 * I, H, lambda e: synth.weights(2 * I, H, seed, stream=500 + e, device=DEV), DEV,
+        asym=asym)
     down = wmoe.quantize_experts(
-        E, H, I, lambda e: synth.weights(H, I, seed, stream=600 + e, device=DEV), DEV)
+        E, H, I, lambda e: synth.weights(H, I, seed, stream=600 + e, device=DEV), DEV, asym=asym)
     B = w4.w4_pick_block_size(T, k, E)
     bufs = wmoe.alloc_buffers(T, k, E, H, I, B, DEV)
     X = synth.activations(T, H, seed, device=DEV)

@@ -175,3 +175,27 @@ def layer_case(T, E, k, H, I, seed, B):
 def test_moe_layer_asym(T, E, k, H, I, B):
     say(f"moe layer asym T={T} E={E} k={k} H={H} I={I} B={B}")
     layer_case(T, E, k, H, I, 13, B)
+
+
+@pytest.mark.parametrize("T,E,k,N,K,B", [(5, 1024, 4, 1, 32, 1), (300, 3, 1, 17, 96, 1),
+                                         (64, 7, 3, 130, 4640, 128), (1, 2, 2, 64, 256, 1024)])
+def test_moe_gemm_asym_extreme(T, E, k, N, K, B):
+    """The most experts, one weight row, one group, blocks of one row and of
+    1024 rows, K past 4096 with K / 32 off a multiple of 8."""
+    say(f"moe_gemm_asym extreme T={T} E={E} k={k} N={N} K={K} B={B}")
+    rng = np.random.default_rng(T + E + N + K + B)
+    used = min(E, 6)
+    Wq, S, Z, ref_w = random_experts(used, N, K, 90)
+    if E > used:   # experts that no pair routes to: zero codes, scales and zero points
+        pad = E - used
+        Wq = torch.cat([Wq, torch.zeros((pad,) + tuple(Wq.shape[1:]), dtype=Wq.dtype, device=Wq.device)])
+        S = torch.cat([S, torch.zeros((pad,) + tuple(S.shape[1:]), dtype=S.dtype, device=S.device)])
+        Z = torch.cat([Z, torch.zeros((pad,) + tuple(Z.shape[1:]), dtype=Z.dtype, device=Z.device)])
+    ids = rng.integers(0, used, size=(T, k)).astype(np.int32)
+    Xb = synth.bits(synth.activations(T, K, 91))
+    s, e, n = w4.moe_align_block_size(up(ids), E, B)
+    Y = canary_bf16((T * k, N))
+    w4.w4a16_moe_gemm_asym(up_bits(Xb), Wq, S, Z, s, e, n, T, k, B, k, out=Y)
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    ref = omoe.grouped_gemm(Xb, ref_w, s_ref, e_ref, n_ref, B, k, T * k)
+    assert_rows_close(down_bits(Y), ref, "moe asym extreme")
