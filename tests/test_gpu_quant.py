@@ -112,3 +112,35 @@ def fuzz_bits(seed, N, K, max_exp):
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_bit_pattern_fuzz(seed):
     check_quantize(fuzz_bits(seed, 256, 1024, 254), f"fuzz seed {seed}")
+
+
+def _group_with_scale(s0, rng, ties):
+    """32 bf16 weights whose scale bf16(amax / 7) is exactly s0 (a bf16 with
+    a mantissa of at most two bits after the point, so amax = 7 s0 and every
+    k s0 / 2 below are exact bf16 values): with ``ties`` the others are
+    k s0 / 2, |k| <= 13 (w / s0 = k / 2: exact half-integer ties for odd
+    k), else random values below amax."""
+    a = 7.0 * s0
+    if ties:
+        v = rng.integers(-13, 14, size=32).astype(np.float64) * (s0 / 2.0)
+    else:
+        v = rng.uniform(-a, a, size=32)
+    v[int(rng.integers(32))] = a if rng.random() < 0.5 else -a
+    g = bf16.rne(v.astype(np.float32))
+    if ties:
+        assert np.all(bf16.to_f32(g).astype(np.float64) == v)
+    return g
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_scales_at_the_quotient_range_ends(ties):
+    """Scales on both sides of the ends of the range where the kernels round
+    w / s without a division ([2^-110, 2^100]), and on the ends themselves,
+    with and without exact ties: bit-exact against the oracle."""
+    rng = np.random.default_rng(77 + ties)
+    scales = [f * 2.0 ** e for e in (-111, -110, -109, 99, 100, 101) for f in (1.0, 1.25, 1.5)]
+    rows = [np.concatenate([_group_with_scale(s0, rng, ties) for _ in range(8)]) for s0 in scales]
+    W = np.stack(rows)
+    _, S = quant.quantize_pack(W)
+    assert np.array_equal(bf16.to_f32(S)[:, 0].astype(np.float64), np.array(scales))
+    check_quantize(W, f"scale range ends ties={ties}")
