@@ -61,8 +61,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
 // ZP: zero-point weights, unsigned codes and one zero point byte per group
 // in Z [N, K/32] (grouped: Z [E, N, K/32]); w' = bf16((q - z) s).
-// BM = 32 (one MFMA row tile, few rows per expert): four code register sets
-// and four to six workgroups per CU keep more weight bytes in flight, and
+// BM = 32 (one MFMA row tile, few rows per expert): eight code register
+// sets filled four steps at a time (a row's 128-byte code line is requested
+// in four back-to-back loads instead of across four steps, when L2 may have
+// dropped it) and four workgroups per CU keep weight bytes in flight, and
 // workgroups index runs rather than blocks.
 template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k_gemm(
@@ -77,7 +79,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   constexpr int XI = BM / 8;           // 1 KB direct-to-LDS loads per activation stage
   constexpr int XPW = XI / NW;         // ... issued by each wave
   constexpr int STAGE = BM * kStepK;   // bf16 elements per activation stage
-  constexpr int kWS = BM <= 32 ? 4 : 2;   // code register sets (steps ahead)
+  // 32-row tile: eight code register sets filled four at a time (steps
+  // 4u + 8 .. 4u + 11 after step 4u + 3), so the four 32-byte pieces of a
+  // row's 128-byte code line are requested back to back
+  constexpr bool kGroupW = BM <= 32;
+  constexpr int kWS = kGroupW ? 8 : 2;   // code register sets (steps ahead)
   constexpr int kU = kWS > kXS ? kWS : kXS;   // K-loop unroll: stage and set named statically
   constexpr bool kRunSlots = MOE && BM <= 32;  // grouped product: slots index runs
   static_assert(kU % kXS == 0 && kU % kWS == 0, "unroll");
@@ -429,6 +435,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     // ahead.  MSE activation tiles are multiplied (rows past the tile read
     // zero).  Per 16-wide K slice j all operand reads are issued first and
     // the MSE x NS MFMAs that follow are independent (no accumulator chain).
+    u32x4 wset[kWS][NS];       // code register sets: step t uses set t % kWS
     u32x4 sraw[NS];            // scale window in flight
     uint32_t scw[NS][4];       // scale window in use
     u32x2 zraw[NS];            // zero-point window in flight (ZP)
@@ -444,20 +451,26 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
       // two register sets the prologue has one code set fewer in the first
       // steps, so 2 XPW + 2 NS loads may stay in flight (in steady state
       // this also waits for the codes of step - 1, which that step
-      // consumed); with four sets the prologue has more, and steady state
-      // allows 2 XPW + 3 NS.  Scale and zero-point windows add loads, which
-      // only makes the wait stricter.  Then
+      // consumed).  The 32-row tile issues its codes four steps at a time,
+      // at the end of each step 4u + 3 (steps 4u + 8 .. 4u + 11, before
+      // their activations), so after the activations of step s come those
+      // of s + 1 and s + 2 and, unless s % 4 == 3, one group of four code
+      // sets: 2 XPW + 4 NS loads may stay in flight (2 XPW when
+      // s % 4 == 3); its prologue issues in the same order.  Scale and
+      // zero-point windows add loads, which only makes the wait stricter.
+      // Then
       // a bare s_barrier: __syncthreads' release fence would also wait for
       // the later stages' DMA, which nothing reads yet.  The empty asm
       // statements keep LDS accesses on their side of the barrier.
-      constexpr int kAfter = (kXS - 2) * XPW + (kWS < 3 ? kWS : 3) * NS;
+      constexpr int P = decltype(pos)::value % 4;
+      constexpr int kAfter = kGroupW ? (kXS - 2) * XPW + (P != 3 ? 4 * NS : 0)
+                                     : (kXS - 2) * XPW + (kWS < 3 ? kWS : 3) * NS;
       static_assert(kAfter <= 63, "vmcnt range");
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kAfter) : "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       load_x(step + kXS - 1, st_next);
       // P = step % 4 (static); the 8-step scale window's half is (step >> 2) & 1
-      constexpr int P = decltype(pos)::value % 4;
       if (P == 0 && (step & 4) == 0) {   // a new scale window: unpack it, fetch the next
         unpack_s(sraw, scw);
         load_s((step >> 3) + 1, sraw);
@@ -502,19 +515,41 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
             for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
         }
       }
-      load_w(step + kWS, wreg);
+      if constexpr (kGroupW) {
+        if constexpr (P == 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            load_w(step + 5 + i, wset[(decltype(pos)::value + 5 + i) % kWS]);
+        }
+      } else {
+        load_w(step + kWS, wreg);
+      }
     };
 
-    u32x4 wset[kWS][NS];       // code register sets: step t uses set t % kWS
-    load_x(0, xs0);
-    load_w(0, wset[0]);
-    load_s(0, sraw);
-    if constexpr (ZP) load_z(0, zraw);
-    load_x(1, xs1);
-    load_w(1, wset[1]);
-    load_x(2, xs2);
+    if constexpr (kGroupW) {
+      // the order of the steady state: codes of steps 0..3, then the
+      // activations of steps 0..2, then codes of steps 4..7 (as issued at
+      // the end of a step 4u + 3)
 #pragma unroll
-    for (int i = 2; i < kWS; ++i) load_w(i, wset[i]);
+      for (int i = 0; i < 4; ++i) load_w(i, wset[i]);
+      load_s(0, sraw);
+      if constexpr (ZP) load_z(0, zraw);
+      load_x(0, xs0);
+      load_x(1, xs1);
+      load_x(2, xs2);
+#pragma unroll
+      for (int i = 4; i < 8; ++i) load_w(i, wset[i]);
+    } else {
+      load_x(0, xs0);
+      load_w(0, wset[0]);
+      load_s(0, sraw);
+      if constexpr (ZP) load_z(0, zraw);
+      load_x(1, xs1);
+      load_w(1, wset[1]);
+      load_x(2, xs2);
+#pragma unroll
+      for (int i = 2; i < kWS; ++i) load_w(i, wset[i]);
+    }
     // The steps and the epilogue, for MSE valid 32-row tiles
     // (accumulators of tiles that hold no valid row are never allocated).
     auto run_tile = [&](auto mse) __attribute__((always_inline)) {
