@@ -16,7 +16,7 @@ of sustained load to reach its steady clocks.
 
 The other workloads of the path are timed in the same run and reported
 under "detail": the prefill product (M = 4096, N = 14336, K = 4096,
-TFLOP/s), quantize + pack and fake quant of that weight (GB/s), and the two
+TFLOP/s), quantize + pack, fake quant and dequant of that weight (GB/s), and the two
 routed MoE layers (128 experts / top-8 / hidden 4096 / intermediate 1536 at
 256 tokens; 384 experts / top-8 / hidden 7168 / intermediate 2048 at 4096
 tokens with skewed routing), per stage and whole layer, the layer again at
@@ -190,8 +190,10 @@ def bench_quant(w4, synth, torch, iters, timer):
     out = {}
     qp_bytes = 2 * N * K + N * K // 2 + 2 * N * (K // 32)
     fq_bytes = 4 * N * K
+    w4.w4_quantize_pack(W, Wq, S)
     for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
-                             ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes)):
+                             ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes),
+                             ("dequant", lambda i: w4.w4_dequant(Wq, S, Wf), qp_bytes)):
         timer.settle(fn, SETTLE_MS / 3)
         t = timer.run(fn, iters) / iters
         gbs = nbytes / (t * 1e-3) / 1e9

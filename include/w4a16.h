@@ -121,6 +121,29 @@ int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K,
                        uint16_t* W_fq, void* stream);
 
 /*
+ * w4_dequant -- packed codes back to bf16 weights ([RL] §4 dequantization,
+ * the values the products multiply; [RL] §2.1: the same values fake
+ * quantization gives, so restoring a bf16 copy of packed weights needs no
+ * source weights):
+ *   W[n, k] = bf16_rne( q[n, k] * S[n, k/32] )   (the fp32 product is exact)
+ * Wq int32 [N, K/8] (4-byte aligned), S bf16 [N, K/32], W bf16 [N, K]
+ * output, 16-byte aligned, not overlapping the inputs.  K % 32 == 0; N or
+ * K == 0 is a no-op.  Bit-exact: w4_dequant(w4_quantize_pack(W)) equals
+ * w4_fake_quant(W).
+ */
+int w4_dequant(const int32_t* Wq, const uint16_t* S, int64_t N, int64_t K,
+               uint16_t* W, void* stream);
+
+/*
+ * w4_dequant_asym -- the same for zero-point codes ([QB] §2.1 inverse map):
+ *   W[n, k] = bf16_rne( (q[n, k] - Z[n, k/32]) * S[n, k/32] )
+ * with q the unsigned nibbles of Wq and Z uint8 [N, K/32] in [0, 15].
+ * w4_dequant_asym(w4_quantize_pack_asym(W)) equals w4_fake_quant_asym(W).
+ */
+int w4_dequant_asym(const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                    int64_t N, int64_t K, uint16_t* W, void* stream);
+
+/*
  * w4a16_gemm -- Y = X * dequant(Wq, S)^T ([RL] §4: INT4 weights, BF16
  * activations, dequantized in registers, BF16 matrix cores, fp32
  * accumulation).
@@ -134,7 +157,9 @@ int w4_fake_quant_asym(const uint16_t* W, int64_t N, int64_t K,
  * offsets): W4_ERR_UNSUPPORTED otherwise.  For K <= 16384 the decode
  * kernel multiplies the exact q * s (integer codes through the MFMA, the
  * group scale on the fp32 partial) instead of bf16_rne(q * s): each
- * product moves by at most 2^-9 |q s|.
+ * product moves by at most 2^-9 |q s|.  Scales must stay below 2^118
+ * (weights below about 2e36): the dequant step of the tiled product (and
+ * of the decode kernel above K = 16384) overflows beyond.
  */
 int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
@@ -150,6 +175,7 @@ int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
  * Layout, alignment, size limits, dispatch and accumulation as w4a16_gemm.
  * For K <= 16384 the decode kernel scales the exact integer sum of
  * x (q - z) per group instead of rounding w' to bf16, as in w4a16_gemm.
+ * Scales below 2^118, as in w4a16_gemm.
  */
 int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                     const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
@@ -205,7 +231,8 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t T, int32_t k,
  * is read on the device, never by the host).
  * topk_weights float32 [T*k] or NULL.  K % 32 == 0, N >= 1, B in [1, 1024],
  * x_row_div in {1, k}.  X and one expert's Wq each below 2 GiB (32-bit
- * buffer offsets), else W4_ERR_UNSUPPORTED.
+ * buffer offsets), else W4_ERR_UNSUPPORTED.  Scales below 2^118 (the
+ * dequant step overflows beyond).
  */
 int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,

@@ -21,6 +21,7 @@ from . import _lib
 
 __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
+    "w4_dequant", "w4_dequant_asym",
     "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
@@ -132,6 +133,38 @@ def w4_fake_quant_asym(W, out=None):
     lib = _lib.load()
     _lib.check("w4_fake_quant_asym", lib.w4_fake_quant_asym(_ptr(W), N, K, _ptr(out), _stream(W)))
     return out
+
+
+def _dequant(name, Wq, S, Z, out):
+    _need(Wq, "Wq", torch.int32, 2)
+    _need(S, "S", torch.bfloat16, 2)
+    N, kw = Wq.shape
+    K = kw * 8
+    if tuple(S.shape) != (N, K // 32):
+        raise ValueError(f"S must be [{N}, {K // 32}], got {tuple(S.shape)}")
+    if Z is not None:
+        _need(Z, "Z", torch.uint8, 2)
+        if tuple(Z.shape) != (N, K // 32):
+            raise ValueError(f"Z must be [{N}, {K // 32}], got {tuple(Z.shape)}")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=Wq.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != N * K:
+        raise ValueError("out size does not match [N, K]")
+    lib = _lib.load()
+    head = (_ptr(Wq), _ptr(S)) + (() if Z is None else (_ptr(Z),))
+    _lib.check(name, getattr(lib, name)(*head, N, K, _ptr(out), _stream(Wq)))
+    return out
+
+
+def w4_dequant(Wq, S, out=None):
+    """Packed codes -> bf16 W [N, K] = bf16(q * s): the fake-quantized values."""
+    return _dequant("w4_dequant", Wq, S, None, out)
+
+
+def w4_dequant_asym(Wq, S, Z, out=None):
+    """Zero-point codes -> bf16 W [N, K] = bf16((q - z) * s)."""
+    return _dequant("w4_dequant_asym", Wq, S, Z, out)
 
 
 def w4a16_gemm(X, Wq, S, out=None):

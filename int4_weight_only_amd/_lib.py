@@ -24,6 +24,8 @@ SIGNATURES = {
     "w4_fake_quant_asym": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
     "w4a16_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "w4a16_gemm_asym": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "w4_dequant": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
+    "w4_dequant_asym": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p, _p]),
     "w4_pick_block_size": (_i32, [_i64, _i32, _i32]),
     "w4_moe_align_capacity": (_i64, [_i64, _i32, _i32, _i32]),
     "moe_align_block_size": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),

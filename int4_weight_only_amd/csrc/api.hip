@@ -109,6 +109,35 @@ int w4_fake_quant(const uint16_t* W, int64_t N, int64_t K, uint16_t* W_fq, void*
                                         as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+int dequant_checked(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, bool asym, int64_t N,
+                    int64_t K, uint16_t* W, void* stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (N == 0 || K == 0) return W4_OK;
+  if (!Wq || !S || !W || (asym && !Z)) return W4_ERR_NULL;
+  if (!aligned(Wq, 4) || !aligned(S, 2) || !aligned(W, 16)) return W4_ERR_MISALIGNED;
+  const int64_t words = N * (K / 8);
+  if (words / (K / 8) != N || words > ((int64_t)1 << 38)) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_dequant(Wq, S, asym ? Z : nullptr, W, words, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_dequant(const int32_t* Wq, const uint16_t* S, int64_t N, int64_t K, uint16_t* W,
+               void* stream) {
+  return dequant_checked(Wq, S, nullptr, false, N, K, W, stream);
+}
+
+int w4_dequant_asym(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, int64_t N, int64_t K,
+                    uint16_t* W, void* stream) {
+  return dequant_checked(Wq, S, Z, true, N, K, W, stream);
+}
+
 int w4a16_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y, int64_t M,
                int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;

@@ -131,6 +131,9 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
 namespace w4 {
 hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16_t* S,
                            uint8_t* Z, uint16_t* Wfq, bool fake, bool asym, hipStream_t st);
+// packed codes -> bf16 weights (Z == nullptr: symmetric codes)
+hipError_t launch_dequant(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, uint16_t* W,
+                          int64_t words, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,

@@ -160,6 +160,50 @@ hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16
   return hipGetLastError();
 }
 
+// Packed codes back to bf16 weights, the values fake quantization gives:
+// W'[n, k] = bf16(q s) (ASYM: bf16((q - z) s)), with the 17-op dequant of the
+// W4A16 products (exact product, one rounding).  One lane per packed word:
+// a 4-byte load, the group's scale (and zero point) shared by its four
+// lanes, one 16-byte store.
+// The 17-op step computes (1024 + n) s + c0 with c0 = -(1032 or 1024 + z) s,
+// which overflows fp32 for s above about 3e35 (2^118); such groups take the
+// direct product q * s (exact in fp32 as well).
+template <bool ASYM>
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ Wq,
+                                                 const uint16_t* __restrict__ S,
+                                                 const uint8_t* __restrict__ Z,
+                                                 u32x4* __restrict__ W, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= words) return;
+  const uint32_t w = Wq[i];
+  const float s = bf16f(S[i >> 2]);
+  const float z = ASYM ? (float)Z[i >> 2] : 0.0f;
+  if (s <= 0x1p100f) {
+    W[i] = dequant8<ASYM>(w, ASYM ? deq_scale_zp(s, z) : deq_scale(s));
+  } else {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q = ASYM ? (float)((w >> (4 * j)) & 0xFu) - z
+                           : (float)((int32_t)(w << (28 - 4 * j)) >> 28);
+      v[j] = q * s;
+    }
+    W[i] = u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]), pk_bf16(v[4], v[5]),
+                 pk_bf16(v[6], v[7])};
+  }
+}
+
+hipError_t launch_dequant(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, uint16_t* W,
+                          int64_t words, hipStream_t st) {
+  const dim3 g((unsigned)((words + 255) / 256)), b(256);
+  if (Z != nullptr)
+    hipLaunchKernelGGL(k_dequant<true>, g, b, 0, st, (const uint32_t*)Wq, S, Z, (u32x4*)W, words);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, g, b, 0, st, (const uint32_t*)Wq, S, nullptr,
+                       (u32x4*)W, words);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_zero_bf16(uint16_t* __restrict__ Y, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     Y[i] = 0;

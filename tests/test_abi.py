@@ -312,3 +312,15 @@ def test_qat_op_refuses_cpu_tensors():
     W = torch.zeros((4, 32), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fake_quant_ste(W)
+
+
+def test_dequant_validation(lib):
+    assert lib.w4_dequant(A4, A2, 4, 48, A16, None) == SHAPE
+    assert lib.w4_dequant(A4, A2, -1, 32, A16, None) == SHAPE
+    assert lib.w4_dequant(A4, A2, 0, 32, A16, None) == OK
+    assert lib.w4_dequant(None, A2, 4, 32, A16, None) == NULL
+    assert lib.w4_dequant(A4, A2, 4, 32, A4, None) == MISALIGNED
+    assert lib.w4_dequant(A2, A2, 4, 32, A16, None) == MISALIGNED
+    assert lib.w4_dequant(A4, A2, (1 << 32) + 1, 512, A16, None) == UNSUPPORTED   # > 2^38 words
+    assert lib.w4_dequant_asym(A4, A2, None, 4, 32, A16, None) == NULL
+    assert lib.w4_dequant_asym(A4, A2, A1, 4, 40, A16, None) == SHAPE

@@ -1,7 +1,8 @@
-"""GPU parity: w4_quantize_pack and w4_fake_quant against the oracle.
+"""GPU parity: w4_quantize_pack, w4_fake_quant and w4_dequant against the
+oracle.
 
-Bit-exact on every byte: the packed codes, the bf16 scales and the
-fake-quantized weights, on the small dense workload, on the full decode and
+Bit-exact on every byte: the packed codes, the bf16 scales, the
+fake-quantized weights and the dequantized packed codes, on the small dense workload, on the full decode and
 prefill weight shapes, on ragged shapes and on hand-built groups that hit
 exact rounding ties, zero groups, subnormal magnitudes and extreme values.
 """
@@ -12,7 +13,7 @@ import torch
 
 import int4_weight_only_amd as w4
 import synth
-from gpu_util import down, down_bits, say, up_bits
+from gpu_util import down, down_bits, say, up, up_bits
 from oracle import bf16, quant
 
 pytestmark = pytest.mark.gpu
@@ -28,6 +29,8 @@ def check_quantize(Wbits, label):
     say(f"fake_quant {label}")
     ref = quant.fake_quant(Wbits)
     np.testing.assert_array_equal(down_bits(w4.w4_fake_quant(W)), ref)
+    say(f"dequant {label}")
+    np.testing.assert_array_equal(down_bits(w4.w4_dequant(Wq, S)), ref)
     # in place
     W2 = W.clone()
     w4.w4_fake_quant(W2, out=W2)
@@ -144,3 +147,28 @@ def test_scales_at_the_quotient_range_ends(ties):
     _, S = quant.quantize_pack(W)
     assert np.array_equal(bf16.to_f32(S)[:, 0].astype(np.float64), np.array(scales))
     check_quantize(W, f"scale range ends ties={ties}")
+
+
+# -------------------------------------------------------------- dequant --
+
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 160), (129, 64), (300, 4096)])
+def test_dequant_matches_oracle_and_fake_quant(N, K):
+    """w4_dequant of the packed codes equals the oracle's dequantization of
+    the same codes and, bit for bit, the fake quantization of the source."""
+    Wb = synth.bits(synth.weights(N, K, 5 + N))
+    Wq_r, S_r = quant.quantize_pack(Wb)
+    say(f"dequant N={N} K={K}")
+    Wq, S = w4.w4_quantize_pack(up_bits(Wb))
+    Wd = down_bits(w4.w4_dequant(Wq, S))
+    np.testing.assert_array_equal(Wd, quant.dequant(quant.unpack(Wq_r), S_r))
+    np.testing.assert_array_equal(Wd, quant.fake_quant(Wb))
+
+
+def test_dequant_special_groups():
+    """Zero groups, subnormal and huge scales, exact ties (the hand-built
+    groups of the quantizer tests)."""
+    Wb = special_groups()
+    Wq_r, S_r = quant.quantize_pack(Wb)
+    say("dequant special groups")
+    Wd = down_bits(w4.w4_dequant(up(Wq_r), up_bits(S_r)))
+    np.testing.assert_array_equal(Wd, quant.dequant(quant.unpack(Wq_r), S_r))

@@ -28,6 +28,8 @@ def check(Wbits, label):
     say(f"fake_quant_asym {label}")
     ref = quant_asym.fake_quant_asym(Wbits)
     np.testing.assert_array_equal(down_bits(w4.w4_fake_quant_asym(W)), ref)
+    say(f"dequant_asym {label}")
+    np.testing.assert_array_equal(down_bits(w4.w4_dequant_asym(Wq, S, Z)), ref)
     W2 = W.clone()
     w4.w4_fake_quant_asym(W2, out=W2)
     np.testing.assert_array_equal(down_bits(W2), ref)
