@@ -167,6 +167,45 @@ def test_grouped_gemm_single_expert_equals_dense():
         assert np.array_equal(rows[f], dense[f])
 
 
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("B,x_row_div,weighted", [(1, 3, False), (4, 3, True), (16, 1, True),
+                                                  (5, 1, False)])
+def test_grouped_gemm_batched_rows_equal_exact_dot_products(zp, B, x_row_div, weighted):
+    """Each expert's rows are one stacked float64 matmul; every row must be
+    the exact dot product X[f // x_row_div] . w'_e[n] (math.fsum of the
+    products, each exact in float64: bf16 times bf16) within float64
+    summation rounding, times the pair's top-k weight.  A wrong expert,
+    row, block or weight index fails by orders of magnitude."""
+    rng = np.random.default_rng(91 + B + 7 * x_row_div + zp)
+    T, k, E, N, K = 9, 3, 4, 6, 64
+    if zp:
+        bank = []
+        for _ in range(E):
+            W = bf16.rne((rng.standard_normal((N, K)) * 0.05 + 0.01).astype(np.float32))
+            bank.append(quant_asym.quantize_pack_asym(W))
+    else:
+        bank = _expert_bank(rng, E, N, K)
+    rows = T * k // x_row_div
+    X = bf16.rne(rng.standard_normal((rows, K)).astype(np.float32))
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)     # some ids skipped
+    tw = rng.random((T, k)).astype(np.float32) if weighted else None
+    s, ex, ntpp = moe.align(ids, E, B)
+    got = moe.grouped_gemm(X, lambda e: bank[e], s, ex, ntpp, B, x_row_div, T * k,
+                           topk_weights=tw)
+    x = bf16.to_f32(X).astype(np.float64)
+    expect_rows = {f for f in range(T * k) if 0 <= ids.flat[f] < E}
+    assert set(got) == expect_rows
+    for f in expect_rows:
+        w = gemm.dequant_weights_f64(*bank[int(ids.flat[f])])
+        xr = x[f // x_row_div]
+        for n in range(N):
+            exact = math.fsum(float(a) * float(b) for a, b in zip(xr, w[n]))
+            if weighted:
+                exact *= float(tw.flat[f])
+            bound = 1e-14 * (math.fsum(abs(float(a) * float(b)) for a, b in zip(xr, w[n])) + 1e-300)
+            assert abs(got[f][n] - exact) <= bound, (f, n, got[f][n], exact)
+
+
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_layer_definition_equals_aligned_pipeline(B):
     """The per-token definition and the align -> grouped GEMM -> SwiGLU ->
