@@ -72,6 +72,23 @@ def activations(M, K, seed, stream=S_X, device="cpu"):
     return normal_bf16((M, K), 1.0, seed, stream, device)
 
 
+def activations_wide(M, K, seed, gain=1.0, outlier_frac=0.0, outlier_gain=1.0,
+                     stream=S_X, device="cpu"):
+    """N(0, 1) activations times a power-of-two ``gain`` (exact in bf16),
+    with a seeded ``outlier_frac`` of the K channels times a further
+    power-of-two ``outlier_gain`` (the few large channels of real hidden
+    states).  Returns (bf16 tensor, sorted outlier channel indices)."""
+    x = activations(M, K, seed, stream, device)
+    if gain != 1.0:
+        x = x * gain
+    g = generator(seed, stream + 500, "cpu")
+    n_out = int(round(outlier_frac * K))
+    ch = torch.sort(torch.randperm(K, generator=g)[:n_out]).values
+    if n_out:
+        x[:, ch.to(x.device)] *= outlier_gain
+    return x, ch.numpy()
+
+
 def expert_gate_up(e, I, H, seed, device="cpu"):
     return normal_bf16((2 * I, H), WEIGHT_SIGMA, seed, S_GATE_UP + e, device)
 
@@ -80,14 +97,24 @@ def expert_down(e, I, H, seed, device="cpu"):
     return normal_bf16((H, I), WEIGHT_SIGMA, seed, S_DOWN + e, device)
 
 
+def _skew_draw(T, E, seed, skew):
+    gs = generator(seed, S_SKEW, "cpu")
+    hot = torch.randperm(E, generator=gs)[: skew["hot"]]
+    biased = torch.randperm(T, generator=gs)[: T // skew["frac_div"]]
+    return hot, biased
+
+
+def hot_experts(T, E, seed, skew):
+    """The experts the skew biases (sorted), as router_logits draws them."""
+    return sorted(int(e) for e in _skew_draw(T, E, seed, skew)[0])
+
+
 def router_logits(T, E, seed, skew=None, device="cpu"):
     """float32 [T, E] logits; optional hot-expert skew (see module doc)."""
     g = generator(seed, S_LOGITS, "cpu")
     lg = torch.randn((T, E), generator=g, dtype=torch.float32)
     if skew is not None:
-        gs = generator(seed, S_SKEW, "cpu")
-        hot = torch.randperm(E, generator=gs)[: skew["hot"]]
-        biased = torch.randperm(T, generator=gs)[: T // skew["frac_div"]]
+        hot, biased = _skew_draw(T, E, seed, skew)
         lg[biased.unsqueeze(1), hot.unsqueeze(0)] += skew["bias"]
     return lg.to(device)
 

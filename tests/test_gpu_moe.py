@@ -6,14 +6,20 @@ SwiGLU, the top-k combine and the whole MoE layer, against the oracle.
 * routing: ids exact (the oracle orders the same fp32 logits), weights to
   fp32 rounding.
 * GEMMs and the layer: |y - y_ref| <= 2e-2 + 1e-2 |y_ref| against fp64.
-* Full-size expert layers (128 experts x [3072 x 4096] + [4096 x 1536],
-  and 384 experts x [4096 x 7168] + [7168 x 2048] with skewed routing):
-  alignment in full, GEMM rows of sampled experts and the layer output of
-  sampled tokens.  The GPU side is fed the oracle's routing (ids, weights)
-  so that the later stages never depend on a near-tie in fp32 softmax.
+* Full-size expert layers.  128 experts x [3072 x 4096] + [4096 x 1536]:
+  alignment in full for each block size, every gate_up and down row of
+  every expert, the layer output of every token.  384 experts x
+  [4096 x 7168] + [7168 x 2048] with skewed routing: alignment in full,
+  every row of the 8 hot experts and 24 random ones, the layer output of
+  64 tokens.  The GPU side is fed the oracle's routing (ids, weights) so
+  that the later stages never depend on a near-tie in fp32 softmax.
 Expert weight sources are drawn on the GPU by ``synth`` (seeded); the
 oracle gets the same bf16 sources downloaded and quantizes them itself.
 """
+
+import collections
+import concurrent.futures
+import os
 
 import numpy as np
 import pytest
@@ -405,8 +411,9 @@ def test_moe_gemm_one_expert_is_dense():
 # --------------------------------------------------- full-size MoE layers --
 
 class Experts:
-    """Full-size stacked experts quantized on the GPU from GPU-drawn sources,
-    plus the oracle's own quantization of any expert on request."""
+    """Full-size stacked experts quantized on the GPU from GPU-drawn sources.
+    ``sources(e)`` downloads expert e's bf16 sources and the GPU's packing
+    of them; the oracle quantizes the sources itself (``oracle_pack``)."""
 
     def __init__(self, wl):
         self.wl = wl
@@ -416,23 +423,43 @@ class Experts:
             E, 2 * I, H, lambda e: synth.expert_gate_up(e, I, H, seed, dev), dev)
         self.down = wmoe.quantize_experts(
             E, H, I, lambda e: synth.expert_down(e, I, H, seed, dev), dev)
-        self._ref = {}
 
-    def ref(self, kind, e):
-        key = (kind, e)
-        if key not in self._ref:
-            H, I, seed = self.wl["H"], self.wl["I"], self.wl["seed"]
-            draw = synth.expert_gate_up if kind == "gate_up" else synth.expert_down
-            src = synth.bits(draw(e, I, H, seed, torch.device("cuda")))
-            Wq, S = quant.quantize_pack(src)
-            stacked = self.gate_up if kind == "gate_up" else self.down
-            np.testing.assert_array_equal(down(stacked.Wq[e]), Wq)
-            np.testing.assert_array_equal(down_bits(stacked.S[e]), S)
-            self._ref[key] = (Wq, S)
-        return self._ref[key]
+    def sources(self, e):
+        H, I, seed = self.wl["H"], self.wl["I"], self.wl["seed"]
+        dev = torch.device("cuda")
+        out = {}
+        for kind, draw, st in (("gate_up", synth.expert_gate_up, self.gate_up),
+                               ("down", synth.expert_down, self.down)):
+            out[kind] = (synth.bits(draw(e, I, H, seed, dev)), down(st.Wq[e]), down_bits(st.S[e]))
+        return out
 
 
-def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
+def oracle_pack(src):
+    """The oracle's packing of one expert's sources, asserted equal to the
+    GPU's (bit-exact quantize + pack on the full-size expert weights)."""
+    packed = {}
+    for kind, (w_bits, gpu_wq, gpu_s) in src.items():
+        Wq, S = quant.quantize_pack(w_bits)
+        np.testing.assert_array_equal(gpu_wq, Wq, err_msg=f"{kind} codes")
+        np.testing.assert_array_equal(gpu_s, S, err_msg=f"{kind} scales")
+        packed[kind] = (Wq, S)
+    return packed
+
+
+def oracle_threads():
+    """Threads for the per-expert oracle work (numpy releases the GIL in its
+    array operations); the GPU machine gives a process 16 CPUs."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_layer(name, B_list, n_random_experts=None, n_tokens=None):
+    """Full-size layer: alignment bit-exact over the whole buffers for each
+    B; every grouped gate_up row (each B) and down row of the checked
+    experts; the fused SwiGLU equal to the unfused pair bit for bit; the
+    layer output of the checked tokens.  ``n_random_experts`` / ``n_tokens``
+    None: every expert and every token; otherwise the skew's hot experts
+    plus that many seeded random experts, and the first and last token
+    plus seeded random tokens up to ``n_tokens``."""
     wl = synth.WORKLOADS[name]
     T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
     say(f"moe layer {name}: drawing and quantizing {E} experts")
@@ -441,12 +468,19 @@ def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
     ids, tw = omoe.route(lg, k)
     Xb = synth.bits(synth.activations(T, H, seed))
     X = up_bits(Xb)
-    counts = np.bincount(ids.reshape(-1), minlength=E)
     rng = np.random.default_rng(seed)
-    busiest, idlest = int(np.argmax(counts)), int(np.argmin(counts))
-    pool = [e for e in range(E) if e not in (busiest, idlest)]
-    extra = list(rng.choice(pool, max(0, n_gate_up_experts - 2), replace=False))
-    gu_experts = {busiest, idlest, *map(int, extra)}
+    if n_random_experts is None:
+        checked = set(range(E))
+    else:
+        hot = set(synth.hot_experts(T, E, seed, wl["skew"])) if wl["skew"] else set()
+        pool = [e for e in range(E) if e not in hot]
+        checked = hot | {int(e) for e in rng.choice(pool, n_random_experts, replace=False)}
+    if n_tokens is None:
+        toks = list(range(T))
+    else:
+        toks = sorted({0, T - 1, *map(int, rng.choice(np.arange(1, T - 1), n_tokens - 2,
+                                                       replace=False))})
+    h1_by_B = {}
     for B in B_list:
         say(f"moe layer {name}: B={B}")
         s_ref, e_ref, n_ref = omoe.align(ids, E, B)
@@ -454,41 +488,77 @@ def run_layer(name, B_list, n_gate_up_experts, n_down_experts, n_tokens):
         np.testing.assert_array_equal(down(buf.sorted_token_ids), s_ref)
         np.testing.assert_array_equal(down(buf.expert_ids), e_ref)
         assert int(down(buf.ntpp)[0]) == n_ref
-        h1 = down_bits(buf.H1)
-        ref = omoe.grouped_gemm(Xb, lambda e: ex.ref("gate_up", e), s_ref, e_ref, n_ref, B, k,
-                                T * k, experts=gu_experts)
-        assert_rows_close(h1, ref, f"{name} gate_up B={B}")
+        h1_by_B[B] = down_bits(buf.H1)
         # the fused gate_up + SwiGLU gives the unfused A bit for bit
         a_unfused = down_bits(buf.A)
-        del buf
+        del buf, out
         A = w4.w4a16_moe_gemm_swiglu(X, ex.gate_up.Wq, ex.gate_up.S, *map(
             up, (s_ref, e_ref, np.array([n_ref], np.int32))), T, k, B, k)
         np.testing.assert_array_equal(down_bits(A), a_unfused)
-        del A
+        del A, a_unfused
     # down projection on its own, on seeded activations
     say(f"moe layer {name}: down projection")
-    B = B_list[0]
-    s_ref, e_ref, n_ref = omoe.align(ids, E, B)
+    B0 = B_list[0]
+    s_ref, e_ref, n_ref = omoe.align(ids, E, B0)
     Ab = synth.bits(synth.activations(T * k, I, seed, stream=77))
-    s, e, n = w4.moe_align_block_size(up(ids), E, B)
-    h2 = down_bits(w4.w4a16_moe_gemm(up_bits(Ab), ex.down.Wq, ex.down.S, s, e, n, T, k, B, 1))
-    dn_experts = set(sorted(gu_experts)[:n_down_experts]) | {busiest}
-    ref = omoe.grouped_gemm(Ab, lambda e: ex.ref("down", e), s_ref, e_ref, n_ref, B, 1, T * k,
-                            experts=dn_experts)
-    assert_rows_close(h2, ref, f"{name} down")
-    # the whole layer on sampled tokens
-    say(f"moe layer {name}: sampled tokens")
-    out, _ = wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B_list[0])
-    o = down_bits(out)
-    toks = sorted({0, T - 1, *map(int, rng.choice(T, max(0, n_tokens - 2), replace=False))})
-    ref = omoe.moe_layer(Xb, ids, tw, lambda e: ex.ref("gate_up", e),
-                         lambda e: ex.ref("down", e), tokens=toks)
-    assert_rows_close(o, ref, f"{name} layer output")
+    s, e, n = w4.moe_align_block_size(up(ids), E, B0)
+    h2 = down_bits(w4.w4a16_moe_gemm(up_bits(Ab), ex.down.Wq, ex.down.S, s, e, n, T, k, B0, 1))
+    say(f"moe layer {name}: layer output")
+    o = down_bits(wmoe.moe_forward(X, up(ids), up(tw), ex.gate_up, ex.down, B=B0)[0])
+
+    pairs = omoe.pairs_by_expert(ids, toks)
+    todo = sorted(checked | set(pairs))
+    say(f"moe layer {name}: oracle over {len(todo)} experts ({len(checked)} with every row), "
+        f"{len(toks)} tokens, {oracle_threads()} threads")
+    n_rows = collections.Counter()
+
+    def check_expert(e, src):
+        packed = oracle_pack(src)
+        h2_layer, rows = {}, collections.Counter()
+        if e in checked:
+            ref = omoe.grouped_gemm(Xb, lambda _: packed["gate_up"], s_ref, e_ref, n_ref, B0, k,
+                                    T * k, experts={e})
+            for B, h1 in h1_by_B.items():
+                assert_rows_close(h1, ref, f"{name} gate_up expert {e} B={B}")
+            rows["gate_up"] += len(ref)
+            ref = omoe.grouped_gemm(Ab, lambda _: packed["down"], s_ref, e_ref, n_ref, B0, 1,
+                                    T * k, experts={e})
+            assert_rows_close(h2, ref, f"{name} down expert {e}")
+            rows["down"] += len(ref)
+        if e in pairs:
+            h2_layer = omoe.expert_h2(Xb, pairs[e], packed["gate_up"], packed["down"])
+        return h2_layer, rows
+
+    h2_layer = {}
+
+    def collect(fut):
+        got, rows = fut.result()
+        h2_layer.update(got)
+        n_rows.update(rows)
+
+    with concurrent.futures.ThreadPoolExecutor(oracle_threads()) as pool:
+        futs = collections.deque()
+        for e in todo:
+            futs.append(pool.submit(check_expert, e, ex.sources(e)))
+            while len(futs) >= 2 * oracle_threads():      # bound the sources held at once
+                collect(futs.popleft())
+        while futs:
+            collect(futs.popleft())
+    say(f"moe layer {name}: rows checked gate_up {n_rows['gate_up']} down {n_rows['down']}")
+    ref = omoe.combine_tokens(tw, h2_layer, toks)
+    assert_rows_close(o, ref, f"{name} layer output over {len(toks)} tokens")
+    if n_random_experts is None:
+        assert n_rows["gate_up"] == n_rows["down"] == int(np.sum((ids >= 0) & (ids < E)))
 
 
+@pytest.mark.timeout(900)
 def test_moe_qwen_layer():
-    run_layer("moe_qwen", [16, 32, 64], 5, 3, 3)
+    """128-expert layer: every expert, every row, every token."""
+    run_layer("moe_qwen", [16, 32, 64])
 
 
+@pytest.mark.timeout(900)
 def test_moe_kimi_layer():
-    run_layer("moe_kimi", [64], 3, 2, 2)
+    """384-expert skewed layer: all rows of the 8 hot experts and 24 random
+    ones, and the layer output of 64 tokens."""
+    run_layer("moe_kimi", [64], n_random_experts=24, n_tokens=64)
