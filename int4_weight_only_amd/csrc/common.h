@@ -40,52 +40,51 @@ __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uin
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Per-group constants of dequant8: s, s / 16, -1032 s and -72 s.  Both
-// products are exact in fp32 (an 8-bit-mantissa scale times a constant
-// whose set bits span at most 8 places).
+// Per-group constants of dequant8: s, -1032 s and -72 s.  Both products are
+// exact in fp32 (an 8-bit-mantissa scale times a constant whose set bits
+// span at most 8 places).
 struct DeqScale {
-  float s, s16, c0, c1;
+  float s, c0, c1;
 };
-__device__ __forceinline__ DeqScale deq_scale(float s) {
-  return {s, s * 0.0625f, -1032.0f * s, -72.0f * s};
-}
+__device__ __forceinline__ DeqScale deq_scale(float s) { return {s, -1032.0f * s, -72.0f * s}; }
 
 // Zero-point codes (unsigned q in [0, 15], w' = bf16((q - z) s)): the same
 // operation without the nibble flip, with c0 = -(1024 + z) s and
 // c1 = -(64 + z) s (exact: at most 11 and 7 significant bits times s).
 __device__ __forceinline__ DeqScale deq_scale_zp(float s, float z) {
-  return {s, s * 0.0625f, -(1024.0f + z) * s, -(64.0f + z) * s};
+  return {s, -(1024.0f + z) * s, -(64.0f + z) * s};
 }
 
 // Eight INT4 codes of one packed word -> eight bf16 w' = bf16_rne(q * s),
 // in k order (element j of the word -> bf16 j of the result: word x holds
 // j = 0, 1, word y holds 2, 3, ...).
-//   A nibble t (two's complement, q = t < 8 ? t : t - 16) sits in the low
-//   mantissa bits of an fp16 whose other bits are those of 1024.0: one
-//   v_bitop3 computes (w & mask) ^ magic for two nibbles at once, the XOR
-//   flipping the nibble's top bit, so the fp16 values are 1024 + (q + 8)
-//   (nibbles at bits 0..3 of a half) or 1024 + 16 (q + 8) (bits 4..7).
-//   v_fma_mix_f32 widens that fp16 exactly and computes
-//   (1024 + q + 8) s - 1032 s, resp. (1024 + 16 (q + 8)) s/16 - 72 s, i.e.
-//   q * s; it is exact (a 4-bit integer times an 8-bit-mantissa scale fits
-//   in fp32), so the only rounding is the final bf16 one.
+//   A nibble t (two's complement, q = t < 8 ? t : t - 16) sits in the
+//   mantissa of an fp16 whose other bits are those of 1024.0 (nibble at
+//   bits 0..3 of a half: mantissa unit 1) or of 64.0 (nibble at bits 4..7:
+//   mantissa unit 1/16).  One v_bitop3 computes (w & mask) ^ magic for two
+//   nibbles at once, the XOR flipping the nibble's top bit, so the fp16
+//   values are 1024 + (q + 8) resp. 64 + (q + 8).  v_fma_mix_f32 widens
+//   that fp16 exactly and computes (1024 + q + 8) s - 1032 s, resp.
+//   (64 + q + 8) s - 72 s, i.e. q * s; it is exact (a 4-bit integer times
+//   an 8-bit-mantissa scale fits in fp32), so the only rounding is the
+//   final bf16 one.
 // 17 VALU ops for 8 weights: one shift, four bitop3, eight fma_mix, four
-// v_cvt_pk_bf16_f32.  UNSIGNED: zero-point codes, no flip (magic 1024 only)
+// v_cvt_pk_bf16_f32.  UNSIGNED: zero-point codes, no flip (plain magics)
 // and the constants of deq_scale_zp.
 template <bool UNSIGNED = false>
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, const DeqScale& d) {
   constexpr uint32_t kLo = UNSIGNED ? 0x64006400u : 0x64086408u;   // 1024 (+ 8: flip)
-  constexpr uint32_t kHi = UNSIGNED ? 0x64006400u : 0x64806480u;   // 1024 (+ 128: flip)
+  constexpr uint32_t kHi = UNSIGNED ? 0x54005400u : 0x54805480u;   // 64 (+ 8/16 units: flip)
   const uint32_t w8 = w >> 8;
   const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) ^ kLo);    // j = 0, 4
   const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) ^ kHi);    // j = 1, 5
   const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) ^ kLo);   // j = 2, 6
   const f16x2 e = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) ^ kHi);   // j = 3, 7
   u32x4 r;
-  r.x = pk_bf16(__builtin_fmaf((float)a.x, d.s, d.c0), __builtin_fmaf((float)b.x, d.s16, d.c1));
-  r.y = pk_bf16(__builtin_fmaf((float)c.x, d.s, d.c0), __builtin_fmaf((float)e.x, d.s16, d.c1));
-  r.z = pk_bf16(__builtin_fmaf((float)a.y, d.s, d.c0), __builtin_fmaf((float)b.y, d.s16, d.c1));
-  r.w = pk_bf16(__builtin_fmaf((float)c.y, d.s, d.c0), __builtin_fmaf((float)e.y, d.s16, d.c1));
+  r.x = pk_bf16(__builtin_fmaf((float)a.x, d.s, d.c0), __builtin_fmaf((float)b.x, d.s, d.c1));
+  r.y = pk_bf16(__builtin_fmaf((float)c.x, d.s, d.c0), __builtin_fmaf((float)e.x, d.s, d.c1));
+  r.z = pk_bf16(__builtin_fmaf((float)a.y, d.s, d.c0), __builtin_fmaf((float)b.y, d.s, d.c1));
+  r.w = pk_bf16(__builtin_fmaf((float)c.y, d.s, d.c0), __builtin_fmaf((float)e.y, d.s, d.c1));
   return r;
 }
 

@@ -96,9 +96,40 @@ def test_decode_full(M):
     run_case(M, wl["N"], wl["K"], wl["seed"], "decode")
 
 
-def test_prefill_sampled():
-    """Full prefill shape; the oracle checks 96 sampled rows (all N) and 48
-    sampled columns (all M)."""
+@pytest.fixture(scope="module")
+def decode_weights():
+    """The decode workload's W [12288, 4096], zero-point packed by the GPU
+    (asserted equal to the oracle's) and dequantized by the oracle in fp64."""
+    wl = synth.WORKLOADS["decode"]
+    Wq, S, Z, Wq_r, S_r, Z_r = quantized_pair(
+        synth.bits(synth.weights(wl["N"], wl["K"], wl["seed"])))
+    return Wq, S, Z, gemm.dequant_asym_f64(Wq_r, S_r, Z_r)
+
+
+WIDE = [("x8", 8.0, 0.0, 1.0), ("x16", 16.0, 0.0, 1.0), ("outliers_1pct_x32", 1.0, 0.01, 32.0)]
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32, 64])
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: c[0])
+def test_wide_activations(decode_weights, M, case):
+    """Zero-point weights against activations scaled x8 / x16 or with 1% of
+    the channels x32: near-zero outputs of these wide-spread products pass
+    the fixed absolute tolerance only if every weight multiplied is the
+    definition's bf16((q - z) s).  M = 64 runs the tiled kernel."""
+    name, gain, frac, ogain = case
+    Wq, S, Z, w64 = decode_weights
+    wl = synth.WORKLOADS["decode"]
+    say(f"gemm_asym wide activations {name} M={M}")
+    X, _ = synth.activations_wide(M, wl["K"], 60 + M, gain, frac, ogain)
+    Xb = synth.bits(X)
+    y = down_bits(w4.w4a16_gemm_asym(up_bits(Xb), Wq, S, Z))
+    ref = bf16.to_f32(Xb).astype(np.float64) @ w64.T
+    assert_close(y, ref, f"wide {name} M={M}")
+
+
+def test_prefill_full():
+    """The prefill workload (M = 4096, N = 14336, K = 4096) checked against
+    the fp64 oracle in every output element."""
     wl = synth.WORKLOADS["prefill"]
     M, N, K = wl["M"][0], wl["N"], wl["K"]
     say(f"gemm_asym prefill M={M} N={N} K={K}")
@@ -106,14 +137,7 @@ def test_prefill_sampled():
     Xb = synth.bits(synth.activations(M, K, wl["seed"]))
     Wq, S, Z, Wq_r, S_r, Z_r = quantized_pair(Wb)
     y = down_bits(w4.w4a16_gemm_asym(up_bits(Xb), Wq, S, Z))
-    rng = np.random.default_rng(8)
-    rows = np.sort(rng.choice(M, 96, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    assert_close(y[rows], gemm.w4a16_gemm_asym(Xb[rows], Wq_r, S_r, Z_r), "prefill rows")
-    cols = np.sort(rng.choice(N, 48, replace=False))
-    cols[-1] = N - 1
-    assert_close(y[:, cols], gemm.w4a16_gemm_asym(Xb, Wq_r[cols], S_r[cols], Z_r[cols]),
-                 "prefill cols")
+    assert_close(y, gemm.w4a16_gemm_asym(Xb, Wq_r, S_r, Z_r), "prefill")
 
 
 def test_deterministic():
