@@ -27,9 +27,12 @@ with zero-point weights (one uint8 zero point per group on top of the
 scale), asymmetric quantize + pack and fake quant, and the two MoE layers
 with zero-point experts (whole fused layer and its two grouped products).
 
-The CPU oracle is timed on this host on whole decode steps (the same four
-products over the same weight shape) until at least 10 s have passed, as a
-reported baseline.
+The CPU oracle is timed on this host as a reported baseline: whole decode
+steps (the same four products over the same weight shape) for the headline
+value, and once per other stage of the path on a bounded sample
+(quantize + pack, fake quant, a prefill row block, routing and alignment of
+the 384-expert layer, the grouped products of 8 experts of the 128-expert
+layer), on the cores this process may use (BLAS threads set to match).
 """
 
 import argparse
@@ -41,6 +44,20 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+
+def host_cores():
+    """CPUs this process may run on, capped by an OMP_NUM_THREADS the
+    environment already sets (a container's CPU share)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n
+
+
+# the CPU oracle's BLAS uses exactly the cores reported; set before numpy loads
+CPU_CORES = host_cores()
+for _var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_var] = str(CPU_CORES)
 
 METRIC = "W4A16 GEMM: decode HBM GB/s (% peak) + prefill/MoE TFLOP/s (% MFMA peak)"
 PEAK_HBM_GBS = 8000.0
@@ -69,14 +86,19 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sections", default="decode,prefill,quant,moe_qwen,moe_kimi,asym")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-block-sweep", action="store_true",
+                   help="MoE layers at the picked block size only")
+    p.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                   help="untimed sustained load before each timed region (0 under a profiler)")
     return p.parse_args()
 
 
 class Timer:
     """HIP events on the current (launch) stream around a region."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, settle_ms=SETTLE_MS):
         self.torch = torch
+        self.settle_scale = settle_ms / SETTLE_MS
 
     def run(self, fn, iters):
         torch = self.torch
@@ -96,17 +118,23 @@ class Timer:
         idle the GPU needs a few tens of milliseconds of load to reach its
         steady clocks; numbers taken earlier describe the ramp, not the
         kernel."""
+        min_ms = min_ms * self.settle_scale
         done, n = 0.0, 1
         while done < min_ms:
             done += self.run(fn, n)
             n = min(2 * n, 1024)
 
 
-def source_hash():
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+# the sources each measured kernel is built from
+KERNEL_SOURCES = {"decode_gemv": ("gemv.hip", "common.h")}
+
+
+def source_hash(files=None):
+    """Hash of kernel sources (all of csrc/ by default), to tell whether
+    stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_weight_only_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files or os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -121,7 +149,7 @@ def stored_traffic(kernel_key):
     with open(path) as fh:
         d = json.load(fh)
     ent = d.get(kernel_key)
-    if not ent or ent.get("source_hash") != source_hash():
+    if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES[kernel_key]):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -147,20 +175,42 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
     timer.settle(step)
     ms = timer.run(step, steps)
     step_bytes = sum(decode_bytes(M) for M in DECODE_MS)
-    per_m = {}
-    for M in DECODE_MS:
-        def one(i, M=M):
-            r = i % ROTATE
-            w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
-        timer.run(one, warmup)
-        timer.settle(one, SETTLE_MS / 3)
-        t = timer.run(one, steps) / steps
-        per_m[str(M)] = {"us": round(t * 1e3, 3),
-                         "GB/s": round(decode_bytes(M) / (t * 1e-3) / 1e9, 1),
-                         "frac_hbm": round(decode_bytes(M) / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    per_m = graph_per_m(
+        torch, timer, steps, lambda M, r: w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M]),
+        lambda M: decode_bytes(M))
     launches = steps * len(DECODE_MS)
     return dict(ms_step=ms / steps, step_bytes=step_bytes, launches=launches, total_ms=ms,
                 per_m=per_m)
+
+
+def graph_per_m(torch, timer, steps, launch, nbytes):
+    """Per-M decode time from a HIP graph of ROTATE back-to-back launches
+    (one per weight copy), replayed: the GPU runs the products without the
+    host's per-call cost, so a lone small product is timed on the GPU, not
+    on the host.  Each launch's time includes the gap between consecutive
+    kernels of the graph."""
+    per_m = {}
+    for M in DECODE_MS:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(ROTATE):
+                launch(M, r)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(ROTATE):
+                launch(M, r)
+        reps = max(4, steps // 6)
+        replay = lambda i: g.replay()
+        timer.settle(replay, SETTLE_MS / 3)
+        t = timer.run(replay, reps) / (reps * ROTATE)
+        gbs = nbytes(M) / (t * 1e-3) / 1e9
+        per_m[str(M)] = {"us": round(t * 1e3, 3), "GB/s": round(gbs, 1),
+                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                         "timing": f"HIP graph of {ROTATE} launches x {reps} replays"}
+        del g
+    return per_m
 
 
 def bench_prefill(w4, synth, torch, iters, timer):
@@ -221,21 +271,11 @@ def bench_asym(w4, synth, torch, steps, warmup, iters, timer):
     Wq0, S0, Z0 = w4.w4_quantize_pack_asym(src)
     del src
     ws = [(Wq0, S0, Z0)] + [(Wq0.clone(), S0.clone(), Z0.clone()) for _ in range(ROTATE - 1)]
-    per_m = {}
-    for M in DECODE_MS:
-        X = synth.activations(M, DECODE_K, 1, device=dev)
-        Y = torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev)
-
-        def one(i, X=X, Y=Y):
-            Wq, S, Z = ws[i % ROTATE]
-            w4.w4a16_gemm_asym(X, Wq, S, Z, out=Y)
-        timer.run(one, warmup)
-        timer.settle(one, SETTLE_MS / 3)
-        t = timer.run(one, steps) / steps
-        nb = decode_bytes(M, zero_points=True)
-        per_m[str(M)] = {"us": round(t * 1e3, 3), "GB/s": round(nb / (t * 1e-3) / 1e9, 1),
-                         "frac_hbm": round(nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    out["decode_per_M"] = per_m
+    Xs = {M: synth.activations(M, DECODE_K, 1, device=dev) for M in DECODE_MS}
+    Ys = {M: torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
+    out["decode_per_M"] = graph_per_m(
+        torch, timer, steps, lambda M, r: w4.w4a16_gemm_asym(Xs[M], *ws[r], out=Ys[M]),
+        lambda M: decode_bytes(M, zero_points=True))
     del ws, Wq0, S0, Z0
 
     wl = synth.WORKLOADS["prefill"]
@@ -291,7 +331,7 @@ def bench_copy(torch, iters, timer):
 MOE_B_SWEEP = {"moe_qwen": (16, 32, 64), "moe_kimi": (32, 64)}
 
 
-def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
+def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True):
     wl = synth.WORKLOADS[name]
     T, E, k, H, I, seed = wl["T"], wl["E"], wl["k"], wl["H"], wl["I"], wl["seed"]
     dev = torch.device("cuda")
@@ -342,7 +382,7 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer):
     ntpp = int(buf.ntpp.item())
     # the whole (fused) layer at other alignment block sizes
     by_B = {str(B): round(t_layer * 1e3, 1)}
-    for B2 in MOE_B_SWEEP.get(name, ()):
+    for B2 in (MOE_B_SWEEP.get(name, ()) if block_sweep else ()):
         if B2 == B:
             continue
         b2 = wmoe.alloc_buffers(T, k, E, H, I, B2, dev, fused=True)
@@ -423,19 +463,45 @@ def bench_moe_layer_asym(name, w4, wmoe, synth, torch, iters, timer):
     return res
 
 
-def cpu_baseline():
-    """The oracle, as it stands, on one full decode step on this host."""
-    import numpy as np  # noqa: F401
-    import synth
-    from oracle import gemm, quant
+def blas_vendor():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        return ", ".join(f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} "
+                         f"threads)" for d in info) or "unknown"
+    except Exception as exc:      # threadpoolctl missing: say so, do not guess
+        return f"unknown ({type(exc).__name__})"
+
+
+def cpu_baseline():
+    """The oracle, as it stands, timed stage by stage on this host's cores.
+
+    The headline value is whole decode steps (the four products M = 1, 8,
+    16, 32 over W[12288 x 4096]) until at least 6 s have passed; each other
+    stage of the path runs once on a bounded sample of its workload, in the
+    same algorithmic units as the GPU numbers.  About 20 s in all."""
+    import numpy as np
+    import synth
+    from oracle import gemm, moe, quant
+
+    stages = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
     seed = synth.WORKLOADS["decode"]["seed"]
     Wb = synth.bits(synth.weights(DECODE_N, DECODE_K, seed))
-    Wq, S = quant.quantize_pack(Wb)
+    (Wq, S), dt = timed(lambda: quant.quantize_pack(Wb))
+    nb = 2 * DECODE_N * DECODE_K + DECODE_N * DECODE_K // 2 + 2 * DECODE_N * (DECODE_K // 32)
+    stages["quantize_pack"] = {"s": round(dt, 3), "GB/s": round(nb / dt / 1e9, 4),
+                               "sample": f"W[{DECODE_N}x{DECODE_K}]"}
+    _, dt = timed(lambda: quant.fake_quant(Wb))
+    nb = 4 * DECODE_N * DECODE_K
+    stages["fake_quant"] = {"s": round(dt, 3), "GB/s": round(nb / dt / 1e9, 4),
+                            "sample": f"W[{DECODE_N}x{DECODE_K}]"}
+
     Xs = {M: synth.bits(synth.activations(M, DECODE_K, 1)) for M in DECODE_MS}
     t0 = time.perf_counter()
     reps = 0
@@ -443,14 +509,61 @@ def cpu_baseline():
         for M in DECODE_MS:
             gemm.w4a16_gemm(Xs[M], Wq, S)
         reps += 1
-        if time.perf_counter() - t0 > 10:    # a bounded sample: ~10-20 s of CPU work
+        if time.perf_counter() - t0 > 6:
             break
-    dt = time.perf_counter() - t0
-    nbytes = reps * sum(decode_bytes(M) for M in DECODE_MS)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    dt_dec = time.perf_counter() - t0
+    dec_bytes = reps * sum(decode_bytes(M) for M in DECODE_MS)
+    stages["decode_gemm"] = {"s": round(dt_dec, 3), "GB/s": round(dec_bytes / dt_dec / 1e9, 4),
+                             "sample": f"{reps} decode step(s)"}
+
+    wl = synth.WORKLOADS["prefill"]
+    Mp = 256
+    Wp = synth.bits(synth.weights(wl["N"], wl["K"], wl["seed"]))
+    Wqp, Sp = quant.quantize_pack(Wp)
+    Xp = synth.bits(synth.activations(Mp, wl["K"], wl["seed"]))
+    _, dt = timed(lambda: gemm.w4a16_gemm(Xp, Wqp, Sp))
+    stages["prefill_gemm"] = {"s": round(dt, 3),
+                              "GFLOP/s": round(gemm_flops(Mp, wl["N"], wl["K"]) / dt / 1e9, 3),
+                              "sample": f"{Mp} of {wl['M'][0]} rows x W[{wl['N']}x{wl['K']}] "
+                                        "(dequant + fp64 matmul)"}
+
+    c4 = synth.WORKLOADS["moe_kimi"]
+    lg = synth.router_logits(c4["T"], c4["E"], c4["seed"], c4["skew"]).numpy()
+    (ids, tw), dt = timed(lambda: moe.route(lg, c4["k"]))
+    stages["route"] = {"s": round(dt, 3), "tokens/s": round(c4["T"] / dt, 1),
+                       "sample": f"T={c4['T']} E={c4['E']} k={c4['k']}"}
+    B4 = moe.pick_block_size(c4["T"], c4["k"], c4["E"])
+    _, dt = timed(lambda: moe.align(ids, c4["E"], B4))
+    stages["align"] = {"s": round(dt, 3), "pairs/s": round(c4["T"] * c4["k"] / dt, 1),
+                       "sample": f"{c4['T'] * c4['k']} pairs, E={c4['E']}, B={B4}"}
+
+    c3 = synth.WORKLOADS["moe_qwen"]
+    T3, E3, k3, H3, I3 = c3["T"], c3["E"], c3["k"], c3["H"], c3["I"]
+    ids3, _ = moe.route(synth.router_logits(T3, E3, c3["seed"]).numpy(), k3)
+    B3 = moe.pick_block_size(T3, k3, E3)
+    s3, e3, n3 = moe.align(ids3, E3, B3)
+    ex = list(range(8))
+    gu = {e: quant.quantize_pack(synth.bits(synth.expert_gate_up(e, I3, H3, c3["seed"])))
+          for e in ex}
+    dn = {e: quant.quantize_pack(synth.bits(synth.expert_down(e, I3, H3, c3["seed"])))
+          for e in ex}
+    X3 = synth.bits(synth.activations(T3, H3, c3["seed"]))
+    A3 = synth.bits(synth.activations(T3 * k3, I3, c3["seed"], stream=77))
+    rows, dt = timed(lambda: (
+        moe.grouped_gemm(X3, lambda e: gu[e], s3, e3, n3, B3, k3, T3 * k3, experts=set(ex)),
+        moe.grouped_gemm(A3, lambda e: dn[e], s3, e3, n3, B3, 1, T3 * k3, experts=set(ex))))
+    nrows = len(rows[0])
+    fl = gemm_flops(nrows, 2 * I3, H3) + gemm_flops(nrows, H3, I3)
+    stages["grouped_gemms"] = {"s": round(dt, 3), "GFLOP/s": round(fl / dt / 1e9, 3),
+                               "sample": f"gate_up + down of {len(ex)} of {E3} experts "
+                                         f"({nrows} rows), 128-expert layer"}
+
+    return {"value": round(dec_bytes / dt_dec / 1e9, 4), "unit": "GB/s", "cores": CPU_CORES,
             "kind": "oracle",
             "sample": f"{reps} full decode step(s): M in {{1,8,16,32}} x W[12288x4096] "
-                      f"int4 g32, numpy fp64, {dt:.1f} s"}
+                      f"int4 g32, numpy dequant + fp64 matmul, {dt_dec:.1f} s",
+            "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas_vendor(),
+            "stages": stages}
 
 
 def main():
@@ -468,7 +581,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    timer = Timer(torch)
+    timer = Timer(torch, args.settle_ms)
     sections = [s for s in args.sections.split(",") if s]
     detail = {}
 
@@ -493,7 +606,8 @@ def main():
     for name in ("moe_qwen", "moe_kimi"):
         if name in sections:
             log(f"bench: {name}")
-            detail[name] = bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer)
+            detail[name] = bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer,
+                                           block_sweep=not args.no_block_sweep)
 
     if "asym" in sections:
         log("bench: zero-point variants")
@@ -510,7 +624,7 @@ def main():
         cpu = cpu_baseline()
 
     line = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "scaling": "weak",
+            "warmup": args.warmup, "settle_ms": args.settle_ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "decode W4A16 GEMV sweep: packed int4 W[12288x4096] group 32 "
                                    "bf16 scales, X[M,4096] bf16, M in {1,8,16,32}",
