@@ -164,67 +164,67 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
 }
 
 // ------------------------------------------------------------------ route --
-// One wave per token: repeated wave-wide argmax picks the k experts in
-// descending logit order (ties: lower index); the weights are
-// exp(l_j - l_0) / sum_i exp(l_i - l_0) over the picked logits, which equals
-// the softmax over all experts renormalised to the picked set.
-//
-// Each candidate is one 64-bit key that orders like (logit, -index): the
-// high word maps the fp32 logit to an unsigned integer of the same order
-// (sign set: all bits flipped; else the sign bit set), the low word is
-// ~index (-0 counts as +0).  A removed pick and a NaN logit get key 0, below every real key
-// (-inf included), so they are never picked again while any expert is left.
-// The wave maximum of the keys takes two DPP quad swaps and the two DPP
-// mirrors within each 16-lane row, then v_permlane16_swap and
-// v_permlane32_swap across rows: no LDS round trip.
+// One wave per token.  Round j picks the j-th expert: the wave maximum of
+// the logits not yet taken (v_max_f32 in each lane, then two DPP quad
+// swaps, the two DPP mirrors within each 16-lane row, v_permlane16_swap and
+// v_permlane32_swap across rows: every lane ends with the maximum), then
+// the lowest expert index holding that value (one ballot per candidate
+// slot, slots in index order).  v_max_f32 returns the other operand when
+// one is NaN, so NaN logits and taken experts never win while any expert
+// with a number is left; -0 equals +0, so equal logits tie on the index.
+// Lane j keeps pick j; the weights are exp(l_j - l_0) / sum over the k
+// picks, which equals the softmax over all experts renormalised to the
+// picked set.  If fewer than k experts have a number, the remaining picks
+// are the lowest untaken indices (distinct; unspecified by the ABI).
 namespace {
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  const uint32_t u = __float_as_uint(v + 0.0f);   // -0 -> +0: equal logits tie on the index
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (v != v) ? 0ull : ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t a) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)a, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(a >> 32), CTRL, 0xF, 0xF, false);
-  const uint64_t b = ((uint64_t)hi << 32) | lo;
-  return b > a ? b : a;
+__device__ __forceinline__ float dpp_fmax(float a) {
+  const float b =
+      __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
+  return fmaxf(a, b);
 }
 
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t a) {
-  a = dpp_max<0xB1>(a);     // quad_perm [1, 0, 3, 2]
-  a = dpp_max<0x4E>(a);     // quad_perm [2, 3, 0, 1]
-  a = dpp_max<0x141>(a);    // row_half_mirror: the other quad of each 8 lanes
-  a = dpp_max<0x140>(a);    // row_mirror: the other 8 lanes of each row
+__device__ __forceinline__ float wave_fmax(float a) {
+  a = dpp_fmax<0xB1>(a);     // quad_perm [1, 0, 3, 2]
+  a = dpp_fmax<0x4E>(a);     // quad_perm [2, 3, 0, 1]
+  a = dpp_fmax<0x141>(a);    // row_half_mirror: the other quad of each 8 lanes
+  a = dpp_fmax<0x140>(a);    // row_mirror: the other 8 lanes of each row
   {
-    // rows (0, 1) and (2, 3): each lane meets the same lane of the paired row
-    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)a, false, false);
-    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(a >> 32),
-                                                    false, false);
-    const uint64_t x = ((uint64_t)h[0] << 32) | l[0], y = ((uint64_t)h[1] << 32) | l[1];
-    a = x > y ? x : y;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a),
+                                                    false, false);   // rows (0, 1), (2, 3)
+    a = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
   {
-    // rows (0, 1) with (2, 3)
-    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)a, false, false);
-    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(a >> 32),
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                    false, false);   // rows (0, 1) with (2, 3)
+    a = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return a;
+}
+
+// wave-wide sum, every lane ends with it (same ladder as wave_fmax)
+__device__ __forceinline__ float wave_fsum(float a) {
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, false));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, false));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a),
                                                     false, false);
-    const uint64_t x = ((uint64_t)h[0] << 32) | l[0], y = ((uint64_t)h[1] << 32) | l[1];
-    a = x > y ? x : y;
+    a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                    false, false);
+    a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
   return a;
 }
 
 }  // namespace
 
-// NPER: candidates per lane (E <= 64 NPER)
+// NPER: candidates per lane (E <= 64 NPER); candidate i of lane l is expert l + 64 i
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
                                                int k, int32_t* __restrict__ ids,
@@ -233,33 +233,49 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;   // whole waves: every lane of a live wave takes part below
   const float* row = logits + (int64_t)t * E;
-  uint64_t key[NPER];
+  const float qnan = __uint_as_float(0x7FC00000u);
+  float v[NPER];
+  uint32_t live = 0;    // bit i: candidate i is an expert not yet taken
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? route_key(row[e], e) : 0ull;
+    const float x = (e < E) ? row[e] : qnan;
+    v[i] = (x != x) ? qnan : x;    // any NaN becomes a quiet one, which v_max_f32 skips
+    live |= (e < E) ? (1u << i) : 0u;
   }
-  float picked[16];
-  int picked_id[16];
+  int my_id = 0;
+  float my_val = 0.0f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    float m = qnan;
 #pragma unroll
-    for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_key(best);
-    const int bi = (int)~(uint32_t)best;
-    picked[j] = key_value(best);
-    picked_id[j] = bi;
+    for (int i = 0; i < NPER; ++i) m = fmaxf(m, ((live >> i) & 1u) ? v[i] : qnan);
+    m = wave_fmax(m);
+    int win = -1;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (lane + 64 * i == bi) key[i] = 0ull;
-  }
-  if (lane == 0) {
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += expf(picked[j] - picked[0]);
-    for (int j = 0; j < k; ++j) {
-      ids[(int64_t)t * k + j] = picked_id[j];
-      wts[(int64_t)t * k + j] = expf(picked[j] - picked[0]) / sum;
+    for (int i = 0; i < NPER; ++i) {
+      const uint64_t b = __ballot(((live >> i) & 1u) && v[i] == m);
+      if (win < 0 && b) win = 64 * i + (int)__builtin_ctzll(b);
     }
+    if (win < 0) {        // no expert with a number left: lowest untaken index
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const uint64_t b = __ballot((live >> i) & 1u);
+        if (win < 0 && b) win = 64 * i + (int)__builtin_ctzll(b);
+      }
+    }
+    if (lane == (win & 63)) live &= ~(1u << (win >> 6));
+    if (lane == j) {
+      my_id = win;
+      my_val = m;
+    }
+  }
+  // lane j < k holds pick j; l_0 (the largest) from lane 0
+  const float l0 = __shfl(my_val, 0);
+  const float ex = (lane < k) ? expf(my_val - l0) : 0.0f;
+  const float sum = wave_fsum(ex);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    wts[(int64_t)t * k + lane] = ex / sum;
   }
 }
 
@@ -272,6 +288,8 @@ hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, in
     hipLaunchKernelGGL(k_route<2>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
   else if (E <= 256)
     hipLaunchKernelGGL(k_route<4>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
+  else if (E <= 384)
+    hipLaunchKernelGGL(k_route<6>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
   else if (E <= 512)
     hipLaunchKernelGGL(k_route<8>, g, b, 0, st, logits, (int)T, (int)E, (int)k, ids, w);
   else

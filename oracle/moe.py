@@ -11,7 +11,8 @@ expert activation; the readings used here are:
 
 * Routing: p = softmax(logits[t, :]) over the E experts; the k experts with
   the largest logits (ties to the lower expert index) are selected and their
-  probabilities renormalised to sum to 1.  (parity unpinned as a choice of
+  probabilities renormalised to sum to 1.  A NaN logit is never selected
+  while a number is left and takes no part in the softmax.  (parity unpinned as a choice of
   method; pinned as arithmetic by closed-form identities.)
 * Block size: B = min(64, max(16, next_pow2(ceil(T*k / E)))).  (parity
   unpinned: a convention.)
@@ -51,8 +52,12 @@ def route(logits, k):
     w = np.empty((T, k), dtype=np.float32)
     for t in range(T):
         row = lg[t]
-        p = np.exp(row - row.max())
-        p = p / p.sum()
+        num = ~np.isnan(row)           # NaN logits are never picked and carry no mass
+        p = np.zeros(E)
+        if num.any():
+            p[num] = np.exp(row[num] - row[num].max())
+            p = p / p.sum()
+        p[~num] = np.nan
         order = np.lexsort((np.arange(E), -row))[:k]
         sel = p[order]
         ids[t] = order

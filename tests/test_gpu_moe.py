@@ -119,9 +119,12 @@ def test_route(T, E, k, kind):
 
 def test_route_masked_and_tied_logits():
     """Rows with fewer finite logits than k (masked experts at -inf), all
-    -inf, all equal, and -0 beside +0 (equal logits): the ids are distinct
-    and follow (logit desc, index asc), as the oracle orders them."""
-    T, E, k = 7, 40, 8
+    -inf, all equal, -0 beside +0 (equal logits), NaN logits among numbers
+    (never picked) and a row with only 3 numbers among NaNs (the remaining
+    picks are the lowest NaN indices, as the oracle's order gives): the ids
+    are distinct and follow (logit desc, index asc), as the oracle orders
+    them."""
+    T, E, k = 9, 40, 8
     lg = np.zeros((T, E), np.float32)
     lg[0, :] = -np.inf                                  # all masked
     lg[1, :] = -np.inf
@@ -132,6 +135,10 @@ def test_route_masked_and_tied_logits():
     lg[5, :] = np.random.default_rng(3).normal(size=E)
     lg[6, :] = -1.0
     lg[6, [3, 9, 20, 33]] = [-0.0, 0.0, -0.0, 0.0]
+    lg[7, :] = np.random.default_rng(4).normal(size=E)
+    lg[7, [0, 7, 11, 12, 39]] = np.nan
+    lg[8, :] = np.nan
+    lg[8, [6, 21, 2]] = [0.25, -3.0, 1.5]
     ids_ref, w_ref = omoe.route(lg, k)
     ids, w = w4.w4_moe_route(up(lg), k)
     ids = down(ids)

@@ -31,6 +31,30 @@ def test_route_identities():
         assert all(lg[t, ids[t][i]] >= lg[t, ids[t][i + 1]] for i in range(k - 1))
 
 
+def test_route_nan_logits_never_picked_and_carry_no_mass():
+    """NaN logits (absent experts) are never selected while numbers are
+    left, and the weights are the softmax over the selected logits alone
+    (closed form exp(l_j - l_0) / sum_i exp(l_i - l_0), computed here with
+    math.exp on the selected values)."""
+    rng = np.random.default_rng(11)
+    lg = rng.normal(size=(3, 40)).astype(np.float32)
+    lg[0, [0, 7, 11, 12, 39]] = np.nan
+    lg[1, ::3] = np.nan
+    lg[2, :] = np.nan
+    lg[2, [6, 21, 2]] = [0.25, -3.0, 1.5]
+    ids, w = moe.route(lg, 8)
+    for t in (0, 1):
+        assert not np.any(np.isnan(lg[t, ids[t]]))
+        sel = [float(lg[t, e]) for e in ids[t]]
+        assert sel == sorted(sel, reverse=True)
+        ex = [math.exp(v - sel[0]) for v in sel]
+        np.testing.assert_allclose(w[t], np.array(ex) / math.fsum(ex), rtol=1e-6)
+        finite = np.sort(lg[t][~np.isnan(lg[t])])[::-1][:8]
+        np.testing.assert_array_equal(np.sort(lg[t, ids[t]])[::-1], finite)
+    # fewer numbers than k: the numbers first, then the lowest NaN indices
+    assert ids[2].tolist() == [2, 6, 21, 0, 1, 3, 4, 5]
+
+
 def test_route_tie_break_lower_index_first():
     lg = np.zeros((1, 6), dtype=np.float32)
     lg[0, 4] = 1.0
