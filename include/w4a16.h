@@ -179,6 +179,93 @@ int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                     void* stream);
 
 /*
+ * Kernel-order code layout ([RL] §4: after loading INT4 weights the
+ * inference engine converts them into the layout its kernel reads, and
+ * restores the original layout before new weights are loaded).  Per [N, K]
+ * matrix: ceil(N/32) x ceil(K/64) blocks of 1 KB; block (r, c) starts at
+ * byte 1024 * (r * ceil(K/64) + c); its 16-byte unit u (u = 0..63) holds
+ * the 16 bytes of group 2c + u/32 (32 codes, as in the canonical word
+ * layout) of row 32r + u%32.  Units of rows >= N or groups >= K/32 are
+ * zero.  E matrices (stacked experts) are stored one after the other.
+ * Scales and zero points keep their [N, K/32] layout.  The products read
+ * each step's codes of 32 rows as one contiguous kilobyte.
+ *
+ * w4_repacked_words -- int32 words of one matrix in kernel order:
+ *   ceil(N/32) * ceil(K/64) * 256.  -1 on invalid sizes.
+ */
+int64_t w4_repacked_words(int64_t N, int64_t K);
+
+/*
+ * w4_repack -- canonical codes Wq [E, N, K/8] -> kernel order
+ * Wt [E * w4_repacked_words(N, K)] (padding units written as zero).
+ * w4_restore -- the inverse: kernel order -> canonical (padding ignored).
+ * Both are pure permutations of 16-byte units: w4_restore(w4_repack(Wq))
+ * equals Wq bit for bit.  Symmetric and zero-point codes alike.  Wq and Wt
+ * 16-byte aligned, not overlapping; K % 32 == 0; E, N or K == 0 is a no-op.
+ */
+int w4_repack(const int32_t* Wq, int64_t E, int64_t N, int64_t K, int32_t* Wt,
+              void* stream);
+int w4_restore(const int32_t* Wt, int64_t E, int64_t N, int64_t K, int32_t* Wq,
+               void* stream);
+
+/*
+ * w4a16_gemm_tiled -- w4a16_gemm (Z == NULL) or w4a16_gemm_asym (Z given)
+ * with the codes in kernel order (Wt from w4_repack, E = 1).  Same
+ * definition, arguments, limits and dispatch; the results equal those of
+ * the canonical-layout call bit for bit.
+ */
+int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
+                     const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                     void* stream);
+
+/*
+ * w4a16_moe_gemm_tiled, w4a16_moe_gemm_swiglu_tiled -- the grouped
+ * products (symmetric with Z == NULL, zero-point with Z [E, N, K/32]) with
+ * every expert's codes in kernel order (Wt from w4_repack with E experts).
+ * Definitions, arguments and limits as w4a16_moe_gemm(_asym) and
+ * w4a16_moe_gemm_swiglu(_asym); results equal the canonical-layout calls
+ * bit for bit.
+ */
+int w4a16_moe_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
+                         const uint8_t* Z, const int32_t* sorted_token_ids,
+                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                         const float* topk_weights, uint16_t* Y, int64_t T, int32_t k,
+                         int32_t E, int64_t N, int64_t K, int32_t B, int32_t x_row_div,
+                         void* stream);
+int w4a16_moe_gemm_swiglu_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
+                                const uint8_t* Z, const int32_t* sorted_token_ids,
+                                const int32_t* expert_ids,
+                                const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
+                                int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
+                                int32_t x_row_div, void* stream);
+
+/*
+ * w4_dequant_t -- the dequantized weight, transposed ([RL] §2.1: the QAT
+ * forward multiplies W' = fake_quant(W); with the straight-through
+ * estimator the input gradient is dX = dY W', which w4_bf16_gemm_nt
+ * computes from this W'^T):
+ *   WT[k, n] = bf16_rne( q[n, k] * S[n, k/32] )            (Z == NULL)
+ *   WT[k, n] = bf16_rne( (q[n, k] - Z[n, k/32]) * S[n, k/32] )   (Z given)
+ * the values of w4_dequant(_asym), bit for bit.  Wq int32 [N, K/8]
+ * (4-byte aligned), S bf16 [N, K/32], Z uint8 [N, K/32] or NULL, WT bf16
+ * [K, N] output, 16-byte aligned.  K % 32 == 0; N or K == 0 is a no-op.
+ */
+int w4_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                 int64_t N, int64_t K, uint16_t* WT, void* stream);
+
+/*
+ * w4_bf16_gemm_nt -- C = A B^T for bf16 matrices with fp32 accumulation
+ * (the QAT input gradient dX = dY W' with A = dY [M, N_w], B = W'^T from
+ * w4_dequant_t; [RL] §2.1):
+ *   C[m, n] = bf16_rne( sum_k A[m, k] * B[n, k] )    (order fixed)
+ * A bf16 [M, K], B bf16 [N, K], both 16-byte aligned; C bf16 [M, N],
+ * 2-byte aligned.  K % 8 == 0 (W4_ERR_SHAPE otherwise); K == 0 writes
+ * zeros; A and B each below 2 GiB (W4_ERR_UNSUPPORTED otherwise).
+ */
+int w4_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
+                    int64_t N, int64_t K, void* stream);
+
+/*
  * w4_pick_block_size -- alignment block size from the token count and the
  * expert count ([TAG] [35]):  B = min(64, max(16, next_pow2(ceil(T*k/E)))).
  * Returns 0 if T < 0, k < 1 or E < 1.

@@ -13,6 +13,8 @@ Layouts (all row-major, contiguous, on one GPU):
   X       bf16  [M, K]        activations;  Y bf16 [M, N]
   Z       uint8 [N, K/32]     zero points (the asymmetric variants)
   experts stacked on a leading axis: Wq [E, N, K/8], S [E, N, K/32], Z [E, N, K/32]
+  Wt      int32 [E, w4_repacked_words(N, K)]  codes in the kernel-order layout
+          (w4_repack / w4_restore); the *_tiled products read it
 """
 
 import torch
@@ -21,11 +23,13 @@ from . import _lib
 
 __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
-    "w4_dequant", "w4_dequant_asym",
+    "w4_dequant", "w4_dequant_asym", "w4_dequant_t", "w4_bf16_gemm_nt",
     "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
+    "w4_repacked_words", "w4_repack", "w4_restore", "w4a16_gemm_tiled",
+    "w4a16_moe_gemm_tiled", "w4a16_moe_gemm_swiglu_tiled",
 ]
 
 
@@ -165,6 +169,49 @@ def w4_dequant(Wq, S, out=None):
 def w4_dequant_asym(Wq, S, Z, out=None):
     """Zero-point codes -> bf16 W [N, K] = bf16((q - z) * s)."""
     return _dequant("w4_dequant_asym", Wq, S, Z, out)
+
+
+def w4_dequant_t(Wq, S, Z=None, out=None):
+    """Packed codes -> bf16 W'^T [K, N] (the dequantized weight, transposed;
+    zero-point codes when Z uint8 [N, K/32] is given)."""
+    _need(Wq, "Wq", torch.int32, 2)
+    _need(S, "S", torch.bfloat16, 2)
+    N, kw = Wq.shape
+    K = kw * 8
+    if tuple(S.shape) != (N, K // 32):
+        raise ValueError(f"S must be [{N}, {K // 32}], got {tuple(S.shape)}")
+    if Z is not None:
+        _need(Z, "Z", torch.uint8, 2)
+        if tuple(Z.shape) != (N, K // 32):
+            raise ValueError(f"Z must be [{N}, {K // 32}], got {tuple(Z.shape)}")
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.bfloat16, device=Wq.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != N * K:
+        raise ValueError("out size does not match [K, N]")
+    lib = _lib.load()
+    _lib.check("w4_dequant_t", lib.w4_dequant_t(_ptr(Wq), _ptr(S), _ptr(Z), N, K, _ptr(out),
+                                                _stream(Wq)))
+    return out
+
+
+def w4_bf16_gemm_nt(A, B, out=None):
+    """bf16 C [M, N] = A [M, K] * B [N, K]^T with fp32 accumulation (K % 8 == 0)."""
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)} B {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out size does not match [M, N]")
+    lib = _lib.load()
+    _lib.check("w4_bf16_gemm_nt", lib.w4_bf16_gemm_nt(_ptr(A), _ptr(B), _ptr(out), M, N, K,
+                                                      _stream(A)))
+    return out
 
 
 def w4a16_gemm(X, Wq, S, out=None):
@@ -408,3 +455,142 @@ def w4_moe_route(logits, k, topk_ids=None, topk_weights=None):
     _lib.check("w4_moe_route", lib.w4_moe_route(_ptr(logits), T, E, k, _ptr(topk_ids),
                                                 _ptr(topk_weights), _stream(logits)))
     return topk_ids, topk_weights
+
+
+# ------------------------------------------------------ kernel-order codes --
+
+def w4_repacked_words(N, K):
+    """int32 words of one [N, K] matrix in the kernel-order layout."""
+    n = int(_lib.load().w4_repacked_words(N, K))
+    if n < 0:
+        raise ValueError("invalid N or K")
+    return n
+
+
+def w4_repack(Wq, out=None):
+    """Canonical codes Wq [N, K/8] (or [E, N, K/8]) -> kernel order
+    Wt int32 [E, w4_repacked_words(N, K)] (E = 1 for a 2-D Wq)."""
+    _need(Wq, "Wq", torch.int32)
+    if Wq.dim() not in (2, 3):
+        raise ValueError("Wq must be [N, K/8] or [E, N, K/8]")
+    E, N, kw = (1,) + tuple(Wq.shape) if Wq.dim() == 2 else tuple(Wq.shape)
+    K = kw * 8
+    words = w4_repacked_words(N, K)
+    if out is None:
+        out = torch.empty((E, words), dtype=torch.int32, device=Wq.device)
+    _need(out, "out", torch.int32)
+    if out.numel() != E * words:
+        raise ValueError(f"out needs {E * words} words")
+    lib = _lib.load()
+    _lib.check("w4_repack", lib.w4_repack(_ptr(Wq), E, N, K, _ptr(out), _stream(Wq)))
+    return out
+
+
+def w4_restore(Wt, N, K, out=None):
+    """Kernel-order codes Wt [E, words] -> canonical Wq [E, N, K/8] (the
+    inverse of w4_repack; [N, K/8] when E = 1 and ``out`` is not given)."""
+    _need(Wt, "Wt", torch.int32)
+    words = w4_repacked_words(N, K)
+    if Wt.numel() % max(words, 1) != 0:
+        raise ValueError("Wt size is not a whole number of matrices")
+    E = Wt.numel() // max(words, 1)
+    if out is None:
+        shape = (N, K // 8) if E == 1 else (E, N, K // 8)
+        out = torch.empty(shape, dtype=torch.int32, device=Wt.device)
+    _need(out, "out", torch.int32)
+    if out.numel() != E * N * (K // 8):
+        raise ValueError("out size does not match [E, N, K/8]")
+    lib = _lib.load()
+    _lib.check("w4_restore", lib.w4_restore(_ptr(Wt), E, N, K, _ptr(out), _stream(Wt)))
+    return out
+
+
+def w4a16_gemm_tiled(X, Wt, S, Z=None, out=None):
+    """w4a16_gemm (Z None) / w4a16_gemm_asym (Z uint8 [N, K/32]) on
+    kernel-order codes Wt [1, w4_repacked_words(N, K)]; N and K from S."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wt, "Wt", torch.int32)
+    _need(S, "S", torch.bfloat16, 2)
+    M, K = X.shape
+    N = S.shape[0]
+    if S.shape[1] * 32 != K or Wt.numel() != w4_repacked_words(N, K):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} Wt {tuple(Wt.shape)} "
+                         f"S {tuple(S.shape)}")
+    if Z is not None:
+        _need(Z, "Z", torch.uint8, 2)
+        if tuple(Z.shape) != tuple(S.shape):
+            raise ValueError("Z must be [N, K/32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out size does not match [M, N]")
+    lib = _lib.load()
+    _lib.check("w4a16_gemm_tiled", lib.w4a16_gemm_tiled(
+        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(out), M, N, K, _stream(X)))
+    return out
+
+
+def _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div):
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wt, "Wt", torch.int32)
+    _need(S, "S", torch.bfloat16, 3)
+    E, N, G = S.shape
+    K = 32 * G
+    if X.shape[1] != K or Wt.numel() != E * w4_repacked_words(N, K):
+        raise ValueError("shape mismatch between X, Wt and S")
+    if Z is not None:
+        _need(Z, "Z", torch.uint8, 3)
+        if tuple(Z.shape) != (E, N, G):
+            raise ValueError("Z must be [E, N, K/32]")
+    if X.shape[0] != (T * k) // x_row_div:
+        raise ValueError("X must have T*k / x_row_div rows")
+    return E, N, K
+
+
+def w4a16_moe_gemm_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                         T, k, B, x_row_div, Z=None, topk_weights=None, out=None):
+    """``w4a16_moe_gemm`` (Z None) / ``w4a16_moe_gemm_asym`` on kernel-order
+    expert codes Wt [E, w4_repacked_words(N, K)]; E, N, K from S."""
+    E, N, K = _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div)
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, n, torch.int32)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32)
+        if topk_weights.numel() != T * k:
+            raise ValueError("topk_weights must have T*k entries")
+    if out is None:
+        out = torch.empty((T * k, N), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * k * N:
+        raise ValueError("out must be [T*k, N]")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm_tiled", lib.w4a16_moe_gemm_tiled(
+        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, k, E, N, K, B,
+        x_row_div, _stream(X)))
+    return out
+
+
+def w4a16_moe_gemm_swiglu_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                T, k, B, x_row_div, Z=None, out=None):
+    """``w4a16_moe_gemm_swiglu`` (Z None) / ``..._asym`` on kernel-order
+    expert codes Wt [E, w4_repacked_words(2I, K)]."""
+    E, N, K = _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div)
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, n, torch.int32)
+    if N % 2:
+        raise ValueError("Wt must hold 2I rows per expert")
+    I = N // 2
+    if out is None:
+        out = torch.empty((T * k, I), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * k * I:
+        raise ValueError("out must be [T*k, I]")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm_swiglu_tiled", lib.w4a16_moe_gemm_swiglu_tiled(
+        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
+    return out

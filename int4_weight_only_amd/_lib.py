@@ -40,6 +40,16 @@ SIGNATURES = {
     "w4_silu_mul": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
     "w4_moe_sum": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i64, _p]),
     "w4_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),
+    "w4_dequant_t": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p, _p]),
+    "w4_bf16_gemm_nt": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "w4_repacked_words": (_i64, [_i64, _i64]),
+    "w4_repack": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p]),
+    "w4_restore": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p]),
+    "w4a16_gemm_tiled": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "w4a16_moe_gemm_tiled": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32,
+                                            _i32, _i64, _i64, _i32, _i32, _p]),
+    "w4a16_moe_gemm_swiglu_tiled": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32,
+                                                   _i32, _i64, _i64, _i32, _i32, _p]),
 }
 
 _lib = None

@@ -174,6 +174,85 @@ int w4a16_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S, con
   return hip_status(w4::launch_gemm_zp(X, Wq, S, Z, Y, M, N, K, as_stream(stream)));
 }
 
+int64_t w4_repacked_words(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K % 32 != 0 || N > kMaxI32 || K > kMaxI32) return -1;
+  return w4::tiled_words(N, K);
+}
+
+namespace {
+int relayout_checked(const int32_t* src, int32_t* dst, int64_t E, int64_t N, int64_t K,
+                     bool restore, void* stream) {
+  if (E < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (E == 0 || N == 0 || K == 0) return W4_OK;
+  if (N > kMaxI32 || K > kMaxI32 || E * w4::tiled_words(N, K) > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (!src || !dst) return W4_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return W4_ERR_MISALIGNED;
+  // the two buffers must not overlap
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  const uintptr_t la = (uintptr_t)(restore ? E * w4::tiled_words(N, K) : E * N * (K / 8)) * 4;
+  const uintptr_t lb = (uintptr_t)(restore ? E * N * (K / 8) : E * w4::tiled_words(N, K)) * 4;
+  if (a < b + lb && b < a + la) return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_relayout(src, dst, E, N, K, restore, as_stream(stream)));
+}
+}  // namespace
+
+int w4_repack(const int32_t* Wq, int64_t E, int64_t N, int64_t K, int32_t* Wt, void* stream) {
+  return relayout_checked(Wq, Wt, E, N, K, false, stream);
+}
+
+int w4_restore(const int32_t* Wt, int64_t E, int64_t N, int64_t K, int32_t* Wq, void* stream) {
+  return relayout_checked(Wt, Wq, E, N, K, true, stream);
+}
+
+int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S, const uint8_t* Z,
+                     uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!Y) return W4_ERR_NULL;
+  if (!aligned(Y, 4)) return W4_ERR_MISALIGNED;
+  if (M > kMaxI32 || N > kMaxI32 || K > kMaxI32 || M * N > ((int64_t)1 << 40) ||
+      N * (K / 8) > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  const bool decode = use_decode(M, K);
+  if (!decode && !(fits_buffer(M * K * 2) && fits_buffer(w4::tiled_words(N, K) * 4) &&
+                   ((M + 127) / 128) * ((N + 255) / 256) < ((int64_t)1 << 31) - 8))
+    return W4_ERR_UNSUPPORTED;
+  if (K == 0) return hip_status(w4::launch_zero_bf16(Y, M * N, as_stream(stream)));
+  if (!X || !Wt || !S) return W4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Wt, 16) || !aligned(S, 2)) return W4_ERR_MISALIGNED;
+  if (decode)
+    return hip_status(w4::launch_gemv_any(X, Wt, S, Z, Y, M, N, K, true, as_stream(stream)));
+  return hip_status(w4::launch_gemm_any(X, Wt, S, Z, Y, M, N, K, true, as_stream(stream)));
+}
+
+int w4_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, int64_t N, int64_t K,
+                 uint16_t* WT, void* stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (N == 0 || K == 0) return W4_OK;
+  if (!Wq || !S || !WT) return W4_ERR_NULL;
+  if (!aligned(Wq, 4) || !aligned(S, 2) || !aligned(WT, 16)) return W4_ERR_MISALIGNED;
+  if (N > kMaxI32 || K > kMaxI32 || N * K > ((int64_t)1 << 40) ||
+      ((N + 63) / 64) * ((K + 127) / 128) >= kMaxI32)
+    return W4_ERR_UNSUPPORTED;
+  return hip_status(w4::launch_dequant_t(Wq, S, Z, WT, N, K, as_stream(stream)));
+}
+
+int w4_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N,
+                    int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 8 != 0) return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!C) return W4_ERR_NULL;
+  if (!aligned(C, 2)) return W4_ERR_MISALIGNED;
+  if (!fits_buffer(M * K * 2) || !fits_buffer(N * K * 2) ||
+      ((M + 127) / 128) * ((N + 127) / 128) >= kMaxI32 || M * N > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (K == 0) return hip_status(w4::launch_zero_bf16(C, M * N, as_stream(stream)));
+  if (!A || !B) return W4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return W4_ERR_MISALIGNED;
+  return hip_status(w4::launch_bf16_gemm_nt(A, B, C, M, N, K, as_stream(stream)));
+}
+
 int32_t w4_pick_block_size(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   const int64_t mean = (T * k + E - 1) / E;
@@ -216,7 +295,7 @@ int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, co
                      bool asym, const int32_t* sorted_token_ids, const int32_t* expert_ids,
                      const int32_t* num_tokens_post_padded, const float* topk_weights,
                      uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
-                     int32_t B, int32_t x_row_div, bool swiglu, void* stream) {
+                     int32_t B, int32_t x_row_div, bool swiglu, bool tiled, void* stream) {
   if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
   if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
   if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
@@ -224,7 +303,8 @@ int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, co
       (int64_t)E * N * (K / 8) > ((int64_t)1 << 40) || T * k * N > ((int64_t)1 << 40))
     return W4_ERR_UNSUPPORTED;
   // one buffer spans X's rows, one an expert's Wq
-  if (!fits_buffer((T * k / x_row_div) * K * 2) || !fits_buffer(N * (K / 2)))
+  if (!fits_buffer((T * k / x_row_div) * K * 2) ||
+      !fits_buffer(tiled ? w4::tiled_words(N, K) * 4 : N * (K / 2)))
     return W4_ERR_UNSUPPORTED;
   if (T == 0) return W4_OK;
   if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y ||
@@ -238,10 +318,11 @@ int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, co
   if (swiglu)
     return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, asym ? Z : nullptr, sorted_token_ids,
                                                  expert_ids, num_tokens_post_padded, Y, T, k, E,
-                                                 N / 2, K, B, x_row_div, as_stream(stream)));
+                                                 N / 2, K, B, x_row_div, tiled,
+                                                 as_stream(stream)));
   return hip_status(w4::launch_moe_gemm(X, Wq, S, asym ? Z : nullptr, sorted_token_ids,
                                         expert_ids, num_tokens_post_padded, topk_weights, Y, T,
-                                        k, E, N, K, B, x_row_div, as_stream(stream)));
+                                        k, E, N, K, B, x_row_div, tiled, as_stream(stream)));
 }
 
 }  // namespace
@@ -255,7 +336,7 @@ int w4a16_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                    int32_t x_row_div, void* stream) {
   return moe_gemm_checked(X, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
                           num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B, x_row_div,
-                          false, stream);
+                          false, false, stream);
 }
 
 int w4a16_moe_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
@@ -265,7 +346,7 @@ int w4a16_moe_gemm_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                         int32_t B, int32_t x_row_div, void* stream) {
   return moe_gemm_checked(X, Wq, S, Z, true, sorted_token_ids, expert_ids,
                           num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B, x_row_div,
-                          false, stream);
+                          false, false, stream);
 }
 
 int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
@@ -277,7 +358,7 @@ int w4a16_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* 
   const int64_t N = I > kMaxI32 ? kMaxI32 + 1 : 2 * I;   // past the limit: unsupported
   return moe_gemm_checked(X, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
                           num_tokens_post_padded, nullptr, A, T, k, E, N, K, B, x_row_div,
-                          true, stream);
+                          true, false, stream);
 }
 
 int w4a16_moe_gemm_swiglu_asym(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
@@ -289,7 +370,30 @@ int w4a16_moe_gemm_swiglu_asym(const uint16_t* X, const int32_t* Wq, const uint1
   const int64_t N = I > kMaxI32 ? kMaxI32 + 1 : 2 * I;   // past the limit: unsupported
   return moe_gemm_checked(X, Wq, S, Z, true, sorted_token_ids, expert_ids,
                           num_tokens_post_padded, nullptr, A, T, k, E, N, K, B, x_row_div,
-                          true, stream);
+                          true, false, stream);
+}
+
+int w4a16_moe_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
+                         const uint8_t* Z, const int32_t* sorted_token_ids,
+                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                         const float* topk_weights, uint16_t* Y, int64_t T, int32_t k, int32_t E,
+                         int64_t N, int64_t K, int32_t B, int32_t x_row_div, void* stream) {
+  return moe_gemm_checked(X, Wt, S, Z, Z != nullptr, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B, x_row_div,
+                          false, true, stream);
+}
+
+int w4a16_moe_gemm_swiglu_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
+                                const uint8_t* Z, const int32_t* sorted_token_ids,
+                                const int32_t* expert_ids,
+                                const int32_t* num_tokens_post_padded, uint16_t* A, int64_t T,
+                                int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
+                                int32_t x_row_div, void* stream) {
+  if (I < 1) return W4_ERR_SHAPE;
+  const int64_t N = I > kMaxI32 ? kMaxI32 + 1 : 2 * I;   // past the limit: unsupported
+  return moe_gemm_checked(X, Wt, S, Z, Z != nullptr, sorted_token_ids, expert_ids,
+                          num_tokens_post_padded, nullptr, A, T, k, E, N, K, B, x_row_div,
+                          true, true, stream);
 }
 
 int w4_silu_mul(const uint16_t* H1, uint16_t* A, int64_t R, int64_t I, void* stream) {

@@ -149,13 +149,13 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
-                           int32_t x_row_div, hipStream_t st);
+                           int32_t x_row_div, bool tiled, hipStream_t st);
 hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                                   const uint8_t* Z, const int32_t* sorted_ids,
                                   const int32_t* expert_ids,
                                   const int32_t* ntpp, uint16_t* A, int64_t T, int32_t k,
                                   int32_t E, int64_t I, int64_t K, int32_t B, int32_t x_row_div,
-                                  hipStream_t st);
+                                  bool tiled, hipStream_t st);
 // Slots of the grouped GEMM, and its workgroups (N-tiles x slots, a 1-D grid).
 int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B);
 int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B, bool swiglu);
@@ -168,4 +168,21 @@ hipError_t launch_moe_sum(const uint16_t* H2, const float* w, uint16_t* Out, int
 hipError_t launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
                         float* w, hipStream_t st);
 hipError_t launch_zero_bf16(uint16_t* Y, int64_t n, hipStream_t st);
+// kernel-order code layout: int32 words of one [N, K] matrix, and the
+// conversion canonical -> kernel order (restore: back) of E stacked matrices
+int64_t tiled_words(int64_t N, int64_t K);
+hipError_t launch_relayout(const int32_t* src, int32_t* dst, int64_t E, int64_t N, int64_t K,
+                           bool restore, hipStream_t st);
+// QAT input gradient: transposed dequant W'^T [K, N], and a bf16 NT GEMM
+hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, uint16_t* WT,
+                            int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
+                               int64_t N, int64_t K, hipStream_t st);
+// products on either layout (Z == nullptr: symmetric codes)
+hipError_t launch_gemv_any(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                           bool tiled, hipStream_t st);
+hipError_t launch_gemm_any(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                           bool tiled, hipStream_t st);
 }  // namespace w4

@@ -18,6 +18,17 @@
 // (v_mfma_f32_32x32x16_bf16); the activation operand is read with the
 // same K permutation, which leaves the sum unchanged.
 //
+// Code layouts (TL).  Canonical: Wq [N, K/8] row-major, so the 16-byte
+// pieces one step of a wave loads (group 2 c + h of 32 rows) lie 32 bytes
+// per row, K/2 bytes apart.  Kernel order (w4_repack): 32-row x 64-k blocks
+// of 1 KB, block (r, c) at byte 1024 (r ceil(K/64) + c), and inside it the
+// 16-byte unit 32 h + (n % 32) = group 2 c + h of row 32 r + n % 32 -- the
+// order in which the lanes of one load read them, so each load instruction
+// reads 1 KB of contiguous memory and a run of steps is one contiguous
+// stream (the weight-layout conversion the RL write-up's section 4 applies
+// before its inference kernel).  Nothing else changes: scales and zero
+// points keep their [N, K/32] layout, and the arithmetic is identical.
+//
 // Pipeline: activations go straight from HBM into LDS (16-byte
 // buffer_load ... lds, four stages: three steps ahead, no staging
 // registers); codes go to registers two steps ahead (two register sets;
@@ -66,7 +77,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // in four back-to-back loads instead of across four steps, when L2 may have
 // dropped it) and four workgroups per CU keep weight bytes in flight, and
 // workgroups index runs rather than blocks.
-template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false>
+template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false, bool TL = false>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K,
@@ -270,13 +281,16 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     rows = min(BM, M - tile_m * BM);
   }
 
-  const uint32_t* Wbase = Wq + (int64_t)expert * N * kw;
+  // tiled: each expert holds ceil(N/32) x ceil(K/64) blocks of 1 KB
+  const int64_t tl_words = (int64_t)((N + 31) >> 5) * ((K + kStepK - 1) / kStepK) * 256;
+  const uint32_t* Wbase = Wq + (int64_t)expert * (TL ? tl_words : (int64_t)N * kw);
   const uint16_t* Sbase = S + (int64_t)expert * N * G;
   const int nsteps = (K + kStepK - 1) / kStepK;
   const int nstepsp = (nsteps + kU - 1) / kU * kU;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t wr = rsrc(Wbase, (uint32_t)N * (uint32_t)kw * 4u);
+  const __amdgpu_buffer_rsrc_t wr =
+      rsrc(Wbase, TL ? (uint32_t)tl_words * 4u : (uint32_t)N * (uint32_t)kw * 4u);
   const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
   const uint8_t* Zbase = ZP ? Z + (int64_t)expert * N * G : nullptr;
   const __amdgpu_buffer_rsrc_t zr = rsrc(Zbase, ZP ? (uint32_t)N * (uint32_t)G : 0u);
@@ -343,8 +357,15 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
-        // rows past N lie past the buffer's end; a group past K reads zero
-        const uint32_t woff = (g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
+        // rows past N lie past the buffer's end (or in the zero padding of
+        // the last 32-row block); a group past K reads zero
+        uint32_t woff;
+        if constexpr (TL)
+          woff = (g < G) ? (((n >> 5) * (uint32_t)nsteps + (uint32_t)step) * 64u + (uint32_t)h * 32u +
+                            (n & 31u)) * 16u
+                         : kOOB;
+        else
+          woff = (g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
         wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
       }
     };
@@ -692,35 +713,45 @@ int64_t moe_tile_rows(int64_t T, int32_t k, int32_t E, int32_t B) {
 }
 }  // namespace
 
-hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+namespace {
+template <bool ZP, bool TL>
+hipError_t launch_dense_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                          hipStream_t st) {
   const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
   const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));   // whole rounds over the 8 XCDs
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false>), grid, dim3(kNW * 64), 0,
-                       st, X, (const uint32_t*)Wq, S, nullptr, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
-                       nullptr, nullptr, 0, 1, 1, 0);
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false, ZP, TL>), grid,
+                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
   else
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false>), grid, dim3(kNW * 64), 0,
-                       st, X, (const uint32_t*)Wq, S, nullptr, Y, (int)M, (int)N, (int)K, nullptr, nullptr,
-                       nullptr, nullptr, 0, 1, 1, 0);
+    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false, ZP, TL>), grid,
+                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
   return hipGetLastError();
+}
+}  // namespace
+
+// Z == nullptr: symmetric codes; tiled: codes in the kernel-order layout
+hipError_t launch_gemm_any(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                           bool tiled, hipStream_t st) {
+  if (Z != nullptr)
+    return tiled ? launch_dense_t<true, true>(X, Wq, S, Z, Y, M, N, K, st)
+                 : launch_dense_t<true, false>(X, Wq, S, Z, Y, M, N, K, st);
+  return tiled ? launch_dense_t<false, true>(X, Wq, S, nullptr, Y, M, N, K, st)
+               : launch_dense_t<false, false>(X, Wq, S, nullptr, Y, M, N, K, st);
+}
+
+hipError_t launch_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
+                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  return launch_gemm_any(X, Wq, S, nullptr, Y, M, N, K, false, st);
 }
 
 hipError_t launch_gemm_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
-  const int64_t tiles = ((N + kNW * kWN - 1) / (kNW * kWN)) * ((M + kBMDense - 1) / kBMDense);
-  const dim3 grid((unsigned)(((tiles + 7) / 8) * 8));
-  if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false, true>), grid,
-                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
-                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
-  else
-    hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false, true>), grid,
-                       dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
-                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
-  return hipGetLastError();
+  return launch_gemm_any(X, Wq, S, Z, Y, M, N, K, false, st);
 }
 
 // Slots (at most BM rows each: an alignment block, or one BM-row part of a
@@ -744,7 +775,7 @@ int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t 
 }
 
 namespace {
-template <int BM, int WN, bool SWI, bool ZP>
+template <int BM, int WN, bool SWI, bool ZP, bool TL>
 hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
@@ -755,41 +786,48 @@ hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t
   const dim3 grid((unsigned)(ntn * moe_gemm_slots(T, k, E, B)));
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI, ZP>), grid, dim3(kNW * 64), 0, st, X,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI, ZP, TL>), grid, dim3(kNW * 64), 0, st, X,
                        (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
                        expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   else
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI, ZP>), grid, dim3(kNW * 64), 0, st, X,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI, ZP, TL>), grid, dim3(kNW * 64), 0, st, X,
                        (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
                        expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
   return hipGetLastError();
 }
 
-template <bool SWI, bool ZP>
+template <bool SWI, bool ZP, bool TL>
 hipError_t launch_grouped_z(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                             const uint8_t* Z, const int32_t* sorted_ids,
                             const int32_t* expert_ids, const int32_t* ntpp, const float* topk_w,
                             uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
                             int32_t B, int32_t x_row_div, hipStream_t st) {
   if (moe_tile_rows(T, k, E, B) == kBMMoeSmall)
-    return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI, ZP>(
+    return launch_grouped_t<kBMMoeSmall, kWNMoeSmall, SWI, ZP, TL>(
         X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N, K, B, x_row_div, st);
-  return launch_grouped_t<kBMMoe, kWN, SWI, ZP>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w,
-                                                Y, T, k, E, N, K, B, x_row_div, st);
+  return launch_grouped_t<kBMMoe, kWN, SWI, ZP, TL>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp,
+                                                    topk_w, Y, T, k, E, N, K, B, x_row_div, st);
 }
 
-// Z == nullptr: symmetric codes; else zero-point codes with Z [E, N, K/32]
+// Z == nullptr: symmetric codes; else zero-point codes with Z [E, N, K/32].
+// tiled: every expert's codes in the kernel-order layout.
 template <bool SWI>
 hipError_t launch_grouped(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
-                          int32_t x_row_div, hipStream_t st) {
+                          int32_t x_row_div, bool tiled, hipStream_t st) {
   if (Z != nullptr)
-    return launch_grouped_z<SWI, true>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T,
-                                       k, E, N, K, B, x_row_div, st);
-  return launch_grouped_z<SWI, false>(X, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, topk_w, Y,
-                                      T, k, E, N, K, B, x_row_div, st);
+    return tiled ? launch_grouped_z<SWI, true, true>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp,
+                                                     topk_w, Y, T, k, E, N, K, B, x_row_div, st)
+                 : launch_grouped_z<SWI, true, false>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp,
+                                                      topk_w, Y, T, k, E, N, K, B, x_row_div, st);
+  return tiled ? launch_grouped_z<SWI, false, true>(X, Wq, S, nullptr, sorted_ids, expert_ids,
+                                                    ntpp, topk_w, Y, T, k, E, N, K, B, x_row_div,
+                                                    st)
+               : launch_grouped_z<SWI, false, false>(X, Wq, S, nullptr, sorted_ids, expert_ids,
+                                                     ntpp, topk_w, Y, T, k, E, N, K, B, x_row_div,
+                                                     st);
 }
 }  // namespace
 
@@ -797,18 +835,18 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
-                           int32_t x_row_div, hipStream_t st) {
+                           int32_t x_row_div, bool tiled, hipStream_t st) {
   return launch_grouped<false>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N,
-                               K, B, x_row_div, st);
+                               K, B, x_row_div, tiled, st);
 }
 
 hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                                   const uint8_t* Z, const int32_t* sorted_ids,
                                   const int32_t* expert_ids, const int32_t* ntpp, uint16_t* A,
                                   int64_t T, int32_t k, int32_t E, int64_t I, int64_t K, int32_t B,
-                                  int32_t x_row_div, hipStream_t st) {
+                                  int32_t x_row_div, bool tiled, hipStream_t st) {
   return launch_grouped<true>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, nullptr, A, T, k, E,
-                              2 * I, K, B, x_row_div, st);
+                              2 * I, K, B, x_row_div, tiled, st);
 }
 
 }  // namespace w4

@@ -29,6 +29,11 @@
 // per row.  Per-wave partials meet in LDS (fixed wave order,
 // deterministic) once per K pass; each output is owned by one thread.
 //
+// Kernel-order codes (TL, written by w4_repack): the 16 bytes of group g of
+// row n sit in the 1 KB block (n / 32, g / 2) at unit 32 (g % 2) + n % 32,
+// so one load instruction reads four 256-byte runs instead of 16 rows'
+// 64-byte pieces; the arithmetic is unchanged.
+//
 // Zero-point weights (ZP; "Quantization basics: from FP32 to INT4" §2.1 and
 // §2.3, w' = bf16((q - z) s) with unsigned q): the same step with the
 // unsigned form of dequant8; a lane row loads its row's eight zero points
@@ -119,6 +124,38 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
   out[3] = hi[1];
 }
 
+// Code buffer of a workgroup's rows [n0, n0 + rows) and the byte offset of
+// the 16 bytes of group g of its row nl (kOOB past K).  Canonical: rows of
+// K / 2 bytes from row n0.  Kernel order: the 1 KB blocks of the 32-row
+// blocks that hold those rows, ceil(K / 64) blocks per 32 rows.
+template <bool TL>
+struct CodeRows {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t rowb, nsteps, first;
+  __device__ CodeRows(const uint32_t* Wq, int n0, int rows, int K) {
+    rowb = (uint32_t)K >> 1;
+    nsteps = (uint32_t)(K + 63) >> 6;
+    if constexpr (TL) {
+      first = (uint32_t)n0 & 31u;              // row n0's place in its 32-row block
+      const uint32_t b0 = (uint32_t)n0 >> 5, b1 = ((uint32_t)(n0 + rows) + 31u) >> 5;
+      r = rsrc(Wq + (size_t)b0 * nsteps * 256u, (b1 - b0) * nsteps * 1024u);
+    } else {
+      first = 0;
+      r = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
+    }
+  }
+  __device__ __forceinline__ uint32_t off(uint32_t nl, int g, int G) const {
+    if (g >= G) return kOOB;
+    if constexpr (TL) {
+      const uint32_t n = first + nl;
+      return (((n >> 5) * nsteps + ((uint32_t)g >> 1)) * 64u + ((uint32_t)g & 1u) * 32u +
+              (n & 31u)) * 16u;
+    } else {
+      return nl * rowb + 16u * (uint32_t)g;
+    }
+  }
+};
+
 __device__ __forceinline__ uint32_t word_of(u32x4 v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
@@ -141,7 +178,7 @@ __device__ __forceinline__ DeqScale group_consts(const uint32_t (&sct)[4], uint3
 
 // M <= 16.  SALIGNED: K / 32 is a multiple of 8 (a wave's eight scales of
 // one row are one 16-byte load).  T: tiles of 16 weight rows per workgroup.
-template <bool SALIGNED, int T, bool ZP>
+template <bool SALIGNED, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -160,13 +197,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   const int n16 = lane & 15;
   const int kq = lane >> 4;
   const int G = K >> 5;
-  const uint32_t rowb = (uint32_t)K >> 1;          // packed bytes per weight row
   const int n0 = blockIdx.x * (T * 16);
   const int rows = min(T * 16, N - n0);
   const int ntiles = (rows + 15) >> 4;
 
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
+  const CodeRows<TL> wr(Wq, n0, rows, K);
   const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
   const __amdgpu_buffer_rsrc_t zr =
       rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
@@ -183,9 +219,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
       const uint32_t nl = (uint32_t)(t * 16 + n16);
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) {
-        const int g = 4 * (c0 + cc) + kq;
-        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
+                                                          0, 0);
       }
     }
     // ---- activations (L2 hits after the first CU's request): lane (m, kq)
@@ -280,7 +315,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 // region (direct-to-LDS loads issued with the others) and is read per group
 // where it is used.  Each dequantized word feeds the MFMAs of both halves.
 // The region then takes the wave's partial sums.
-template <bool SALIGNED, int T, bool ZP>
+template <bool SALIGNED, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -301,13 +336,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
   const int n16 = lane & 15;
   const int kq = lane >> 4;
   const int G = K >> 5;
-  const uint32_t rowb = (uint32_t)K >> 1;          // packed bytes per weight row
   const int n0 = blockIdx.x * (T * 16);
   const int rows = min(T * 16, N - n0);
   const int ntiles = (rows + 15) >> 4;
 
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t wr = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
+  const CodeRows<TL> wr(Wq, n0, rows, K);
   const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
   const __amdgpu_buffer_rsrc_t zr =
       rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
@@ -342,9 +376,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       const uint32_t nl = (uint32_t)(t * 16 + n16);
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) {
-        const int g = 4 * (c0 + cc) + kq;
-        const uint32_t woff = (g < G) ? nl * rowb + 16u * (uint32_t)g : kOOB;
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
+                                                          0, 0);
       }
     }
     // ---- half 1's activations into this wave's LDS region: load 4 cc + j
@@ -449,72 +482,83 @@ int cu_count() {
   return cus[dev];
 }
 
-template <bool SA, int T, bool ZP>
+template <bool SA, int T, bool ZP, bool TL>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<SA, T, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
-                     X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_decode16<SA, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                     st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, bool ZP>
+template <bool SA, bool ZP, bool TL>
 hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode16_t<SA, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<SA, 2, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<SA, 3, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode16_t<SA, 4, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode16_t<SA, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<SA, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<SA, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<SA, 4, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-template <bool SA, int T, bool ZP>
+template <bool SA, int T, bool ZP, bool TL>
 hipError_t run_decode32_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode32<SA, T, ZP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, st,
-                     X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_decode32<SA, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                     st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, bool ZP>
+template <bool SA, bool ZP, bool TL>
 hipError_t run_decode32(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode32_t<SA, 1, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode32_t<SA, 2, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode32_t<SA, 3, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode32_t<SA, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode32_t<SA, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode32_t<SA, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-template <bool ZP>
+template <bool ZP, bool TL>
 hipError_t launch_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                          hipStream_t st) {
   const bool sa = ((K >> 5) & 7) == 0;
   if (M <= 16)
-    return sa ? run_decode16<true, ZP>(X, Wq, S, Z, Y, M, N, K, st)
-              : run_decode16<false, ZP>(X, Wq, S, Z, Y, M, N, K, st);
-  return sa ? run_decode32<true, ZP>(X, Wq, S, Z, Y, M, N, K, st)
-            : run_decode32<false, ZP>(X, Wq, S, Z, Y, M, N, K, st);
+    return sa ? run_decode16<true, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st)
+              : run_decode16<false, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return sa ? run_decode32<true, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st)
+            : run_decode32<false, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 }  // namespace
 
+// Z == nullptr: symmetric codes; tiled: codes in the kernel-order layout
+hipError_t launch_gemv_any(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
+                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                           bool tiled, hipStream_t st) {
+  if (Z != nullptr)
+    return tiled ? launch_decode<true, true>(X, Wq, S, Z, Y, M, N, K, st)
+                 : launch_decode<true, false>(X, Wq, S, Z, Y, M, N, K, st);
+  return tiled ? launch_decode<false, true>(X, Wq, S, nullptr, Y, M, N, K, st)
+               : launch_decode<false, false>(X, Wq, S, nullptr, Y, M, N, K, st);
+}
+
 hipError_t launch_gemv(const uint16_t* X, const int32_t* Wq, const uint16_t* S, uint16_t* Y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  return launch_decode<false>(X, Wq, S, nullptr, Y, M, N, K, st);
+  return launch_gemv_any(X, Wq, S, nullptr, Y, M, N, K, false, st);
 }
 
 hipError_t launch_gemv_zp(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
-  return launch_decode<true>(X, Wq, S, Z, Y, M, N, K, st);
+  return launch_gemv_any(X, Wq, S, Z, Y, M, N, K, false, st);
 }
 
 }  // namespace w4

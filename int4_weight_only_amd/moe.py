@@ -15,7 +15,9 @@ The activation (silu(gate) * up, gate = the first I rows of gate_up) and
 the combine (weights applied after the down projection) are readings: the
 pages name the gate_up / down pair but give no formula.  Experts quantized
 with zero points ("Quantization basics: from FP32 to INT4" §2.3) run the
-``_asym`` forms of the two grouped products.
+``_asym`` forms of the two grouped products; experts converted to the
+kernel-order code layout (``repack_experts``, §4's weight-layout conversion)
+run the ``_tiled`` forms.
 """
 
 from dataclasses import dataclass
@@ -23,34 +25,47 @@ from dataclasses import dataclass
 import torch
 
 from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
-               w4_pick_block_size, w4_quantize_pack, w4_quantize_pack_asym, w4_silu_mul,
-               w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
-               w4a16_moe_gemm_swiglu_asym)
+               w4_pick_block_size, w4_quantize_pack, w4_quantize_pack_asym, w4_repack,
+               w4_silu_mul, w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
+               w4a16_moe_gemm_swiglu_asym, w4a16_moe_gemm_swiglu_tiled, w4a16_moe_gemm_tiled)
 
 
 @dataclass
 class ExpertWeights:
     """Stacked packed weights of E experts: Wq int32 [E, N, K/8], S bf16 [E, N, K/32],
-    and for zero-point experts Z uint8 [E, N, K/32] (None: symmetric codes)."""
+    and for zero-point experts Z uint8 [E, N, K/32] (None: symmetric codes).
+    Wt: the same codes in the kernel-order layout ([E, w4_repacked_words(N, K)],
+    from ``repack_experts``); when present the products read it and Wq may be
+    None."""
     Wq: torch.Tensor
     S: torch.Tensor
     Z: torch.Tensor = None
+    Wt: torch.Tensor = None
 
     @property
     def E(self):
-        return self.Wq.shape[0]
+        return self.S.shape[0]
 
     @property
     def N(self):
-        return self.Wq.shape[1]
+        return self.S.shape[1]
 
     @property
     def K(self):
-        return self.Wq.shape[2] * 8
+        return self.S.shape[2] * 32
 
     def nbytes(self):
         z = 0 if self.Z is None else self.Z.numel()
-        return self.Wq.numel() * 4 + self.S.numel() * 2 + z
+        codes = self.Wt if self.Wt is not None else self.Wq
+        return codes.numel() * 4 + self.S.numel() * 2 + z
+
+
+def repack_experts(w, keep_canonical=False):
+    """The experts with their codes converted to the kernel-order layout
+    (``w4_repack``); the canonical codes are dropped unless asked for
+    (``w4_restore`` brings them back)."""
+    Wt = w4_repack(w.Wq)
+    return ExpertWeights(w.Wq if keep_canonical else None, w.S, w.Z, Wt)
 
 
 def quantize_experts(E, N, K, source, device, asym=False):
@@ -75,7 +90,11 @@ def quantize_experts(E, N, K, source, device, asym=False):
 
 def grouped_gemm(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div,
                  topk_weights=None, out=None):
-    """``w4a16_moe_gemm`` or its zero-point form, as the experts ``w`` need."""
+    """``w4a16_moe_gemm``, its zero-point form or their kernel-order forms,
+    as the experts ``w`` need."""
+    if w.Wt is not None:
+        return w4a16_moe_gemm_tiled(X, w.Wt, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
+                                    x_row_div, Z=w.Z, topk_weights=topk_weights, out=out)
     if w.Z is None:
         return w4a16_moe_gemm(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
                               x_row_div, topk_weights, out)
@@ -84,7 +103,11 @@ def grouped_gemm(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div,
 
 
 def grouped_gemm_swiglu(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div, out=None):
-    """``w4a16_moe_gemm_swiglu`` or its zero-point form, as the experts ``w`` need."""
+    """``w4a16_moe_gemm_swiglu``, its zero-point form or their kernel-order
+    forms, as the experts ``w`` need."""
+    if w.Wt is not None:
+        return w4a16_moe_gemm_swiglu_tiled(X, w.Wt, w.S, sorted_token_ids, expert_ids, ntpp, T,
+                                           k, B, x_row_div, Z=w.Z, out=out)
     if w.Z is None:
         return w4a16_moe_gemm_swiglu(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
                                      x_row_div, out)

@@ -324,3 +324,65 @@ def test_dequant_validation(lib):
     assert lib.w4_dequant(A4, A2, (1 << 32) + 1, 512, A16, None) == UNSUPPORTED   # > 2^38 words
     assert lib.w4_dequant_asym(A4, A2, None, 4, 32, A16, None) == NULL
     assert lib.w4_dequant_asym(A4, A2, A1, 4, 40, A16, None) == SHAPE
+
+
+# ------------------------------------------------------ kernel-order codes --
+
+@pytest.mark.parametrize("N,K", [(1, 32), (32, 64), (33, 96), (12288, 4096), (14336, 4096),
+                                 (3072, 4096), (4096, 1536), (100, 0)])
+def test_repacked_words_matches_oracle(lib, N, K):
+    from oracle import layout
+    assert lib.w4_repacked_words(N, K) == layout.repacked_words(N, K)
+
+
+def test_repacked_words_bad_args(lib):
+    assert lib.w4_repacked_words(-1, 32) == -1
+    assert lib.w4_repacked_words(4, 33) == -1
+    assert lib.w4_repacked_words(4, -32) == -1
+
+
+D16 = ctypes.c_void_p(0x100000)       # a second buffer far from A16 (16-byte aligned)
+D4 = ctypes.c_void_p(0x100004)
+
+
+def test_repack_restore_validation(lib):
+    for f in (lib.w4_repack, lib.w4_restore):
+        assert f(A16, 1, 4, 33, D16, None) == SHAPE
+        assert f(A16, -1, 4, 32, D16, None) == SHAPE
+        assert f(None, 0, 4, 32, None, None) == OK             # empty: no-op
+        assert f(None, 1, 4, 32, D16, None) == NULL
+        assert f(A16, 1, 4, 32, None, None) == NULL
+        assert f(A4, 1, 4, 32, D16, None) == MISALIGNED
+        assert f(A16, 1, 4, 32, D4, None) == MISALIGNED
+        assert f(A16, 1, 4, 32, A16, None) == UNSUPPORTED      # overlapping buffers
+
+
+def test_gemm_tiled_validation(lib):
+    f = lib.w4a16_gemm_tiled
+    assert f(A16, A16, A2, None, A4, 4, 8, 33, None) == SHAPE
+    assert f(A16, A16, A2, None, A4, -1, 8, 32, None) == SHAPE
+    assert f(None, None, None, None, None, 0, 8, 32, None) == OK    # M == 0: no-op
+    assert f(None, A16, A2, None, A4, 4, 8, 32, None) == NULL
+    assert f(A16, None, A2, None, A4, 4, 8, 32, None) == NULL
+    assert f(A16, A16, A2, None, None, 4, 8, 32, None) == NULL
+    assert f(A4, A16, A2, None, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A4, A2, None, A4, 4, 8, 32, None) == MISALIGNED
+    assert f(A16, A16, A2, None, A2, 4, 8, 32, None) == MISALIGNED
+    # tiled product: the kernel-order weights must fit one 32-bit buffer
+    assert f(A16, A16, A2, None, A4, 64, 1 << 20, 8192, None) == UNSUPPORTED
+
+
+def test_moe_gemm_tiled_validation(lib):
+    f = lib.w4a16_moe_gemm_tiled
+    args = lambda **kw: dict(dict(X=A16, W=A16, S=A2, Z=None, s=A4, e=A4, n=A4, tw=None, Y=A4,
+                                  T=4, k=2, E=3, N=64, K=64, B=16, div=2), **kw)
+    call = lambda a: f(a["X"], a["W"], a["S"], a["Z"], a["s"], a["e"], a["n"], a["tw"], a["Y"],
+                       a["T"], a["k"], a["E"], a["N"], a["K"], a["B"], a["div"], None)
+    assert call(args(K=48)) == SHAPE
+    assert call(args(div=3)) == SHAPE
+    assert call(args(T=0)) == OK
+    assert call(args(W=None)) == NULL
+    assert call(args(W=A4)) == MISALIGNED
+    g = lib.w4a16_moe_gemm_swiglu_tiled
+    assert g(A16, A16, A2, None, A4, A4, A4, A4, 4, 2, 3, 0, 64, 16, 2, None) == SHAPE
+    assert g(A16, None, A2, None, A4, A4, A4, A4, 4, 2, 3, 32, 64, 16, 2, None) == NULL
