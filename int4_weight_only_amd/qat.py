@@ -20,15 +20,17 @@ forward packs W (``w4_quantize_pack``) and runs the W4A16 product on the
 codes ("INT4 QAT end-to-end for RL" §4) instead of writing W_fq and reading
 it back: 3.125 bytes of weight traffic per element (read W, write and read
 0.5625 bytes of codes and scales) instead of 6 (read W, write W_fq, read
-W_fq).  The backward is the straight-through estimator
-with two plain bf16 library GEMMs: dX = dY * W_fq (W_fq dequantized from
-the packed codes the forward made, ``w4_dequant``, 0.56 bytes read per
-element) and dW = dY^T * X.
+W_fq).  The backward is the straight-through estimator.  The input
+gradient dX = dY * W_fq runs in the library: ``w4_dequant_t`` writes W_fq^T
+from the packed codes the forward made (bit-exact with fake quant) and
+``w4_bf16_gemm_nt`` multiplies (N % 8 == 0).  The weight gradient
+dW = dY^T * X involves no quantized operand: it is a plain bf16 product of
+two activations and stays torch's matrix product.
 """
 
 import torch
 
-from . import w4_dequant, w4_fake_quant, w4_quantize_pack, w4a16_gemm
+from . import w4_bf16_gemm_nt, w4_dequant_t, w4_fake_quant, w4_quantize_pack, w4a16_gemm
 
 __all__ = ["FakeInt4STE", "fake_quant_ste", "Int4QATLinear", "qat_linear"]
 
@@ -75,7 +77,9 @@ class Int4QATLinear(torch.autograd.Function):
         dY = grad_out.reshape(-1, N).to(torch.bfloat16).contiguous()
         dX = dW = None
         if ctx.needs_input_grad[0]:
-            dX = torch.mm(dY, w4_dequant(Wq, S)).reshape(ctx.x_shape)
+            if N % 8:
+                raise ValueError(f"the QAT input gradient needs N % 8 == 0 (N = {N})")
+            dX = w4_bf16_gemm_nt(dY, w4_dequant_t(Wq, S)).reshape(ctx.x_shape)
         if ctx.needs_input_grad[1]:
             dW = torch.mm(dY.t().contiguous(), X2)
         return dX, dW

@@ -108,3 +108,52 @@ def test_qat_linear_backward_is_straight_through():
         assert got.dtype == torch.bfloat16
         ok, a, r = gemm.within_tolerance(down_bits(got), ref, ATOL, RTOL)
         assert ok, (name, a, r)
+
+
+# ------------------------------------------------- input-gradient kernels --
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("N,K", [(1, 32), (63, 96), (64, 128), (200, 544), (1000, 4096)])
+def test_dequant_t_bit_exact(asym, N, K):
+    """w4_dequant_t = the oracle's dequantized weight, transposed, bit for bit
+    (N not a multiple of 8 takes the element-store tail)."""
+    import int4_weight_only_amd as w4
+    from oracle import quant_asym
+    say(f"dequant_t asym={asym} N={N} K={K}")
+    Wb = synth.bits(synth.weights(N, K, 50 + N))
+    if asym:
+        Wq, S, Z = quant_asym.quantize_pack_asym(Wb)
+        ref = quant_asym.dequant_asym(quant_asym.unpack_unsigned(Wq), S, Z)
+        got = w4.w4_dequant_t(torch.from_numpy(Wq).to(dev()), up_bits(S),
+                              torch.from_numpy(Z).to(dev()))
+    else:
+        Wq, S = quant.quantize_pack(Wb)
+        ref = quant.dequant(quant.unpack(Wq), S)
+        got = w4.w4_dequant_t(torch.from_numpy(Wq).to(dev()), up_bits(S))
+    np.testing.assert_array_equal(down_bits(got), np.ascontiguousarray(ref.T))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 7, 24), (130, 257, 96), (64, 128, 4096),
+                                   (300, 200, 14336), (4096, 4096, 14336)])
+def test_bf16_gemm_nt_matches_oracle(M, N, K):
+    """C = A B^T against the fp64 product of the same bf16 operands; the
+    last shape is the input gradient of the prefill layer (dY [4096, 14336]
+    times W'^T [4096, 14336])."""
+    import int4_weight_only_amd as w4
+    say(f"bf16_gemm_nt M={M} N={N} K={K}")
+    Ab = synth.bits(synth.activations(M, K, 60))
+    Bb = synth.bits(synth.weights(N, K, 61))
+    C = down_bits(w4.w4_bf16_gemm_nt(up_bits(Ab), up_bits(Bb)))
+    ref = bf16.to_f32(Ab).astype(np.float64) @ bf16.to_f32(Bb).astype(np.float64).T
+    ok, a, r = gemm.within_tolerance(C, ref, ATOL, RTOL)
+    assert ok, (a, r)
+
+
+def test_qat_linear_input_gradient_needs_n_multiple_of_8():
+    from int4_weight_only_amd.qat import qat_linear
+    say("qat_linear N % 8 != 0")
+    W = synth.weights(36, 64, 70).to(dev()).requires_grad_(True)
+    X = synth.activations(4, 64, 71).to(dev()).requires_grad_(True)
+    Y = qat_linear(X, W)
+    with pytest.raises(ValueError, match="N % 8"):
+        Y.backward(torch.ones_like(Y))
