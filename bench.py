@@ -5,7 +5,9 @@
 
 Headline line (one JSON object on stdout): the decode W4A16 product over
 packed INT4 weights W[12288 x 4096] (group 32, bf16 scales) against
-M in {1, 8, 16, 32} bf16 activation rows.  One step = those four products,
+M in {1, 8, 16, 32} bf16 activation rows, with the codes in the
+kernel-order layout (w4_repack, converted once before timing, as an
+inference engine converts weights at load).  One step = those four products,
 each on its own copy of the weights (24 copies rotate, 680 MB in all, so
 the 256 MB last-level cache never holds the step's weights).  ``value`` is
 the algorithmic HBM traffic of the step (packed codes + scales + X + Y)
@@ -163,13 +165,15 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
     del src
     Wqs = [Wq0] + [Wq0.clone() for _ in range(ROTATE - 1)]
     Ss = [S0] + [S0.clone() for _ in range(ROTATE - 1)]
+    # the codes in the kernel-order layout, converted once as at weight load
+    Wts = [w4.w4_repack(W) for W in Wqs]
     Xs = {M: synth.activations(M, DECODE_K, 1, device=dev) for M in DECODE_MS}
     Ys = {M: torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
 
     def step(i):
         for j, M in enumerate(DECODE_MS):
             r = (4 * i + j) % ROTATE
-            w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M])
+            w4.w4a16_gemm_tiled(Xs[M], Wts[r], Ss[r], out=Ys[M])
 
     timer.run(step, warmup)
     timer.settle(step)
@@ -178,9 +182,12 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
     per_m = graph_per_m(
         torch, timer, steps, lambda M, r: w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M]),
         lambda M: decode_bytes(M))
+    per_m_tiled = graph_per_m(
+        torch, timer, steps, lambda M, r: w4.w4a16_gemm_tiled(Xs[M], Wts[r], Ss[r], out=Ys[M]),
+        lambda M: decode_bytes(M))
     launches = steps * len(DECODE_MS)
     return dict(ms_step=ms / steps, step_bytes=step_bytes, launches=launches, total_ms=ms,
-                per_m=per_m)
+                per_m=per_m, per_m_tiled=per_m_tiled)
 
 
 def graph_per_m(torch, timer, steps, launch, nbytes):
@@ -213,6 +220,24 @@ def graph_per_m(torch, timer, steps, launch, nbytes):
     return per_m
 
 
+def graph_time(torch, timer, fn, n, reps=4):
+    """Mean time (ms) of one fn() from a HIP graph of n back-to-back calls
+    replayed reps times (one warm-up call on the capture stream first)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    timer.run(lambda i: g.replay(), 1)
+    t = timer.run(lambda i: g.replay(), reps) / (reps * n)
+    del g
+    return t
+
+
 def bench_prefill(w4, synth, torch, iters, timer):
     wl = synth.WORKLOADS["prefill"]
     M, N, K = wl["M"][0], wl["N"], wl["K"]
@@ -225,8 +250,15 @@ def bench_prefill(w4, synth, torch, iters, timer):
     timer.settle(f)
     t = timer.run(f, iters) / iters
     tf = gemm_flops(M, N, K) / (t * 1e-3) / 1e12
+    Wt = w4.w4_repack(Wq)
+    ft = lambda i: w4.w4a16_gemm_tiled(X, Wt, S, out=Y)
+    timer.settle(ft, SETTLE_MS / 3)
+    tt = timer.run(ft, iters) / iters
+    tft = gemm_flops(M, N, K) / (tt * 1e-3) / 1e12
     return {"M": M, "N": N, "K": K, "us": round(t * 1e3, 1), "TFLOP/s": round(tf, 1),
-            "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
+            "kernel_order": {"us": round(tt * 1e3, 1), "TFLOP/s": round(tft, 1),
+                             "frac_mfma_bf16": round(tft / PEAK_BF16_TFLOPS, 4)}}
 
 
 def bench_quant(w4, synth, torch, iters, timer):
@@ -241,9 +273,14 @@ def bench_quant(w4, synth, torch, iters, timer):
     qp_bytes = 2 * N * K + N * K // 2 + 2 * N * (K // 32)
     fq_bytes = 4 * N * K
     w4.w4_quantize_pack(W, Wq, S)
+    Wt = w4.w4_repack(Wq)
+    Wr = torch.empty_like(Wq)
+    rp_bytes = 2 * (N * K // 2)
     for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
                              ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes),
-                             ("dequant", lambda i: w4.w4_dequant(Wq, S, Wf), qp_bytes)):
+                             ("dequant", lambda i: w4.w4_dequant(Wq, S, Wf), qp_bytes),
+                             ("repack", lambda i: w4.w4_repack(Wq, Wt), rp_bytes),
+                             ("restore", lambda i: w4.w4_restore(Wt, N, K, Wr), rp_bytes)):
         timer.settle(fn, SETTLE_MS / 3)
         t = timer.run(fn, iters) / iters
         gbs = nbytes / (t * 1e-3) / 1e9
@@ -370,10 +407,25 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
 
     timer.settle(layer)
     t_layer = timer.run(layer, iters) / iters
+    # the same layer on kernel-order experts
+    gu_t, dn_t = wmoe.repack_experts(gate_up), wmoe.repack_experts(down)
+    stages["gate_up_swiglu_kernel_order"] = lambda: wmoe.grouped_gemm_swiglu(
+        X, gu_t, buf.sorted_token_ids, buf.expert_ids, buf.ntpp, T, k, B, k, out=buf.A)
+    stages["down_kernel_order"] = lambda: wmoe.grouped_gemm(
+        buf.A, dn_t, buf.sorted_token_ids, buf.expert_ids, buf.ntpp, T, k, B, 1, out=buf.H2)
+
+    def layer_t(i):
+        for sname in ("route", "align", "gate_up_swiglu_kernel_order", "down_kernel_order",
+                      "combine"):
+            stages[sname]()
+
+    timer.settle(layer_t, SETTLE_MS / 3)
+    t_layer_t = timer.run(layer_t, iters) / iters
+    # per stage: a HIP graph of back-to-back launches, replayed (the small
+    # kernels would otherwise be timed on the host's launch cost)
     per = {}
     for sname, fn in stages.items():
-        t = timer.run(lambda i: fn(), iters) / iters
-        per[sname] = round(t * 1e3, 2)
+        per[sname] = round(graph_time(torch, timer, fn, iters) * 1e3, 2)
     pairs = T * k
     fl_gu = gemm_flops(pairs, 2 * I, H)
     fl_dn = gemm_flops(pairs, H, I)
@@ -402,6 +454,8 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
     res = {
         "T": T, "E": E, "k": k, "H": H, "I": I, "B": B,
         "layer_us": round(t_layer * 1e3, 1),
+        "layer_us_kernel_order": round(t_layer_t * 1e3, 1),
+        "layer_TFLOP/s_kernel_order": round((fl_gu + fl_dn) / (t_layer_t * 1e-3) / 1e12, 1),
         "stage_us": per,
         "layer_TFLOP/s": round((fl_gu + fl_dn) / (t_layer * 1e-3) / 1e12, 1),
         "gate_up_TFLOP/s": round(fl_gu / (per["gate_up"] * 1e-6) / 1e12, 1),
@@ -418,7 +472,7 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
         "rows_per_expert_p10_p50_p90": [round(float(v), 1) for v in q.tolist()],
         "padding_frac": round(1.0 - pairs / ntpp, 4),
     }
-    del gate_up, down, buf
+    del gate_up, down, buf, gu_t, dn_t
     torch.cuda.empty_cache()
     return res
 
@@ -592,7 +646,8 @@ def main():
     if "decode" in sections:
         log("bench: decode sweep")
         dec = bench_decode(w4, synth, torch, args.steps, args.warmup, timer)
-        detail["decode_per_M"] = dec["per_m"]
+        detail["decode_per_M"] = dec["per_m_tiled"]
+        detail["decode_per_M_canonical_layout"] = dec["per_m"]
     iters = max(3, min(args.steps, 20))
     if "prefill" in sections:
         log("bench: prefill")
@@ -628,7 +683,8 @@ def main():
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "decode W4A16 GEMV sweep: packed int4 W[12288x4096] group 32 "
                                    "bf16 scales, X[M,4096] bf16, M in {1,8,16,32}",
-                       "rotating_weight_copies": ROTATE}}
+                       "rotating_weight_copies": ROTATE,
+                       "code_layout": "kernel order (w4_repack, converted once at load)"}}
     if dec is not None:
         value = dec["step_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
         per_launch_bytes = dec["step_bytes"] / len(DECODE_MS)
@@ -640,7 +696,7 @@ def main():
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(achieved / PEAK_HBM_GBS, 4),
                             "traffic": traffic,
-                            "kernel": "k_decode (decode W4A16 product)",
+                            "kernel": "k_decode16 / k_decode32 on kernel-order codes",
                             "algorithmic_bytes_per_launch": per_launch_bytes,
                             "avg_launch_us": round(per_launch_us, 3)}
     else:

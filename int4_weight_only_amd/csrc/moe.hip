@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   const int f_lo = min(P, wave * chunk);
   const int f_hi = min(P, f_lo + chunk);
 
-  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&pos[0][0])[i] = 0;
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) pos[i / E][i % E] = 0;
   __syncthreads();
 
   // ids of kBatch rounds are loaded together (the rounds would otherwise
@@ -72,13 +72,18 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
     }
   };
 
-  // 1. per-wave histograms
+  // 1. per-wave histograms; a wave whose range fits one batch keeps its
+  // ids in registers for step 3
+  const bool one_batch = f_hi - f_lo <= 64 * kBatch;
+  int v0[kBatch];
   for (int base = f_lo; base < f_hi; base += 64 * kBatch) {
     int v[kBatch];
     load_batch(base, v);
 #pragma unroll
-    for (int r = 0; r < kBatch; ++r)
+    for (int r = 0; r < kBatch; ++r) {
       if (v[r] >= 0 && v[r] < E) atomicAdd(&pos[wave][v[r]], 1);
+      v0[r] = v[r];
+    }
   }
   __syncthreads();
 
@@ -115,19 +120,27 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   __syncthreads();
   const int total = total_sh;
 
-  // 3. stable placement, each wave through its own range
+  // 3. stable placement, each wave through its own range (ids from the
+  // registers of step 1 when they fit one batch); the expert ids need
+  // nbits bits, one ballot each
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 1;
   for (int base0 = f_lo; base0 < f_hi; base0 += 64 * kBatch) {
     int v[kBatch];
-    load_batch(base0, v);
+    if (one_batch) {
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) v[r] = v0[r];
+    } else {
+      load_batch(base0, v);
+    }
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int f = base0 + 64 * r + lane;
+      if (base0 + 64 * r >= f_hi) break;               // wave-uniform: past the range
       const int e = (v[r] >= 0 && v[r] < E) ? v[r] : -1;
       const bool valid = e >= 0;
       uint64_t match = ballot64(valid);
-#pragma unroll
-      for (int bit = 0; bit < 10; ++bit) {
+      for (int bit = 0; bit < nbits; ++bit) {
         const bool b = valid && ((e >> bit) & 1);
         const uint64_t ones = ballot64(b);
         match &= ((e >> bit) & 1) ? ones : ~ones;
