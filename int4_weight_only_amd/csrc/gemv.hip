@@ -15,8 +15,10 @@
 // Mapping (MI355X).  One workgroup of 16 waves per CU; wave w owns a
 // 256-element K slice (two 128-element "chunks") and keeps its slice of X
 // in registers (loaded once, reused for every weight row).  The workgroup
-// covers T tiles of 16 weight rows and each wave holds the codes of all T
-// tiles of its slice at once.  For one chunk, lane (n = l % 16, kq = l / 16)
+// covers T tiles of 16 weight rows and each wave issues the loads of all T
+// tiles of its slice at once (scales and activations first, then the codes
+// tile by tile) and processes tile t as soon as its codes are in, while the
+// later tiles' are still on the way.  For one chunk, lane (n = l % 16, kq = l / 16)
 // loads 16 bytes = group 4c + kq of row n (a 16-row tile is 16 contiguous
 // 64-byte runs) with a raw buffer load: rows or groups past the end read
 // as zero in hardware, so no load sits behind a branch and all of them are
@@ -210,19 +212,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
-    // ---- codes of every tile first, so the HBM stream starts at once (rows
-    // past the end read zero); a row's two chunks are adjacent requests (one
-    // 128-byte line)
-    u32x4 wv[T][kCPW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint32_t nl = (uint32_t)(t * 16 + n16);
-#pragma unroll
-      for (int cc = 0; cc < kCPW; ++cc) {
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
-                                                          0, 0);
-      }
-    }
+    // ---- scales (and zero points) first: lane row r fetches the wave's 8
+    // groups of row n16 of tile r
+    const int g0 = 4 * c0;
+    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
+    u32x2 zraw = u32x2{0u, 0u};
+    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
     // ---- activations (L2 hits after the first CU's request): lane (m, kq)
     // takes elements 8 kq .. 8 kq + 7 of group 4 c + j of row m
     u32x4 xop[kCPW][4];
@@ -236,12 +231,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
                                  : kOOB;
         xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
       }
-    // ---- scales (and zero points): lane row r fetches the wave's 8 groups
-    // of row n16 of tile r
-    const int g0 = 4 * c0;
-    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
-    u32x2 zraw = u32x2{0u, 0u};
-    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    // ---- codes, tile by tile (rows past the end read zero); a row's two
+    // chunks are adjacent requests (one 128-byte line).  Loads return in
+    // issue order, so tile t is processed as soon as its codes are in while
+    // the later tiles' are still on the way.
+    u32x4 wv[T][kCPW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint32_t nl = (uint32_t)(t * 16 + n16);
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) {
+        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
+                                                          0, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
     uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
@@ -255,36 +258,36 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
         for (int t = 0; t < T; ++t) sct[t][d] = b[t];
       }
     }
-
-    f32x4 acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t zc[kCPW][T];                // ZP: tile t's zero points of chunk cc's groups
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc) {
-      u32x4 u[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) u[t] = transpose_rows(wv[t][cc]);
-      uint32_t zc[T];                    // ZP: tile t's zero points of this chunk's groups
       if constexpr (ZP) {
         uint32_t b[4];
         broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
 #pragma unroll
-        for (int t = 0; t < T; ++t) zc[t] = b[t];
+        for (int t = 0; t < T; ++t) zc[cc][t] = b[t];
       } else {
 #pragma unroll
-        for (int t = 0; t < T; ++t) zc[t] = 0u;
+        for (int t = 0; t < T; ++t) zc[cc][t] = 0u;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const DeqScale dq = group_consts<ZP>(sct[t], zc[t], cc, j);
-          acc[t] = mfma16(xop[cc][j], dequant8<ZP>(word_of(u[t], j), dq), acc[t]);
-        }
     }
-    // lane holds D[m = 4 kq + r][n = n16] of every tile
+
 #pragma unroll
-    for (int t = 0; t < T; ++t) *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc[t];
+    for (int t = 0; t < T; ++t) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const u32x4 u = transpose_rows(wv[t][cc]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const DeqScale dq = group_consts<ZP>(sct[t], zc[cc][t], cc, j);
+          acc = mfma16(xop[cc][j], dequant8<ZP>(word_of(u, j), dq), acc);
+        }
+      }
+      // lane holds D[m = 4 kq + r][n = n16] of tile t
+      *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc;
+      __builtin_amdgcn_sched_barrier(0);   // tile t's work stays ahead of tile t + 1's wait
+    }
 
     // ---- sum over waves in a fixed order (deterministic): one thread per
     // output, rows m < M only
@@ -356,20 +359,27 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       const int row = 16 * hh + n16;
       return (g < G && row < M) ? ((uint32_t)row * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
     };
-    // ---- half 0's activations (issued first: the first wait is for them alone)
+    // ---- scales (and zero points) first: lane row r fetches the wave's 8
+    // groups of row n16 of tile r
+    const int g0 = 4 * c0;
+    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
+    u32x2 zraw = u32x2{0u, 0u};
+    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    // ---- half 0's activations into registers, half 1's into this wave's
+    // LDS region: load 4 cc + j of lane l lands at byte 1024 (4 cc + j) + 16 l
     u32x4 xop[kCPW][4];
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(0, cc, j), 0, 0);
-    // ---- scales (and zero points): lane row r fetches the wave's 8 groups
-    // of row n16 of tile r
-    const int g0 = 4 * c0;
-    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
-    u32x2 zraw = u32x2{0u, 0u};
-    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
-    // ---- codes of every tile (rows past the end read zero)
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16_to_lds(xr, &lds[wave][(4 * cc + j) * 256], x_off(1, cc, j));
+    // ---- codes, tile by tile (rows past the end read zero); loads return in
+    // issue order, so tile t is processed as soon as its codes are in
     u32x4 wv[T][kCPW];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -380,13 +390,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
                                                           0, 0);
       }
     }
-    // ---- half 1's activations into this wave's LDS region: load 4 cc + j
-    // of lane l lands at byte 1024 (4 cc + j) + 16 l
-#pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma16_to_lds(xr, &lds[wave][(4 * cc + j) * 256], x_off(1, cc, j));
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
     uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
@@ -400,39 +403,38 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
         for (int t = 0; t < T; ++t) sct[t][d] = b[t];
       }
     }
+    uint32_t zc[kCPW][T];                // ZP: tile t's zero points of chunk cc's groups
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc) {
+      if constexpr (ZP) {
+        uint32_t b[4];
+        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[cc][t] = b[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[cc][t] = 0u;
+      }
+    }
 
     f32x4 acc0[T], acc1[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc) {
-      u32x4 u[T];
+      for (int cc = 0; cc < kCPW; ++cc) {
+        const u32x4 u = transpose_rows(wv[t][cc]);
 #pragma unroll
-      for (int t = 0; t < T; ++t) u[t] = transpose_rows(wv[t][cc]);
-      uint32_t zc[T];                    // ZP: tile t's zero points of this chunk's groups
-      if constexpr (ZP) {
-        uint32_t b[4];
-        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[t] = b[t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[t] = 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const DeqScale dq = group_consts<ZP>(sct[t], zc[t], cc, j);
-          const u32x4 w = dequant8<ZP>(word_of(u[t], j), dq);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane];
+          const DeqScale dq = group_consts<ZP>(sct[t], zc[cc][t], cc, j);
+          const u32x4 w = dequant8<ZP>(word_of(u, j), dq);
           acc0[t] = mfma16(xop[cc][j], w, acc0[t]);
           acc1[t] = mfma16(x1, w, acc1[t]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);   // tile t's work stays ahead of tile t + 1's wait
     }
     // lane holds D[m = 16 hh + 4 kq + r][n = n16]; the region's activations
     // have all been read by this wave (LDS accesses in program order)

@@ -27,8 +27,9 @@ namespace w4 {
 //     expert, a scan over the waves in wave order turns the wave's count
 //     into the position where its first pair of that expert goes;
 //  3. every wave walks its range in order, 64 pairs per round: the lanes
-//     with the same expert are found with ten ballots (one per bit of the
-//     id), giving each lane its rank among equal lanes before it; the
+//     with the same expert are found with one ballot per bit of the id
+//     (ceil(log2 E) of them), giving each lane its rank among equal lanes
+//     before it; the
 //     round's first lane of each expert then advances the wave's position
 //     for that expert.  No barrier between rounds: positions are private to
 //     the wave, read and advanced in program order;
@@ -58,9 +59,6 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   const int f_lo = min(P, wave * chunk);
   const int f_hi = min(P, f_lo + chunk);
 
-  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) pos[i / E][i % E] = 0;
-  __syncthreads();
-
   // ids of kBatch rounds are loaded together (the rounds would otherwise
   // wait on one load each)
   constexpr int kBatch = 8;
@@ -72,18 +70,26 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
     }
   };
 
+  // the wave's first batch of ids is in flight while the counters are cleared
+  int v0[kBatch];
+  load_batch(f_lo, v0);
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) pos[i / E][i % E] = 0;
+  __syncthreads();
+
   // 1. per-wave histograms; a wave whose range fits one batch keeps its
   // ids in registers for step 3
   const bool one_batch = f_hi - f_lo <= 64 * kBatch;
-  int v0[kBatch];
   for (int base = f_lo; base < f_hi; base += 64 * kBatch) {
     int v[kBatch];
-    load_batch(base, v);
+    if (base == f_lo) {
 #pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      if (v[r] >= 0 && v[r] < E) atomicAdd(&pos[wave][v[r]], 1);
-      v0[r] = v[r];
+      for (int r = 0; r < kBatch; ++r) v[r] = v0[r];
+    } else {
+      load_batch(base, v);
     }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r)
+      if (v[r] >= 0 && v[r] < E) atomicAdd(&pos[wave][v[r]], 1);
   }
   __syncthreads();
 
@@ -370,14 +376,25 @@ __global__ __launch_bounds__(256) void k_moe_sum8(const u32x4* __restrict__ H2,
     for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < H8;
          c += (int64_t)gridDim.x * 256) {
       float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const float wj = w ? w[t * k + j] : 1.0f;
-        const u32x4 hv = H2[(t * k + j) * H8 + c];
-        const uint32_t d[4] = {hv.x, hv.y, hv.z, hv.w};
+      // the rows of 8 pairs are loaded together, then summed in pair order
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        u32x4 hv[8];
+        float wj[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          s[2 * q] = __builtin_fmaf(wj, bf16_lo(d[q]), s[2 * q]);
-          s[2 * q + 1] = __builtin_fmaf(wj, bf16_hi(d[q]), s[2 * q + 1]);
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + u;
+          hv[u] = j < k ? H2[(t * k + j) * H8 + c] : u32x4{0u, 0u, 0u, 0u};
+          wj[u] = j < k ? (w ? w[t * k + j] : 1.0f) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + u >= k) break;
+          const uint32_t d[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s[2 * q] = __builtin_fmaf(wj[u], bf16_lo(d[q]), s[2 * q]);
+            s[2 * q + 1] = __builtin_fmaf(wj[u], bf16_hi(d[q]), s[2 * q + 1]);
+          }
         }
       }
       Out[t * H8 + c] = u32x4{pk_bf16(s[0], s[1]), pk_bf16(s[2], s[3]), pk_bf16(s[4], s[5]),
