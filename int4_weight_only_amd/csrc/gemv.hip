@@ -13,23 +13,28 @@
 // bf16 are exact, only the order of the fp32 additions is the kernel's.
 //
 // Mapping (MI355X).  One workgroup of 16 waves per CU; wave w owns a
-// 256-element K slice (two 128-element "chunks") and keeps its slice of X
-// in registers (loaded once, reused for every weight row).  The workgroup
-// covers T tiles of 16 weight rows and each wave issues the loads of all T
-// tiles of its slice at once (scales and activations first, then the codes
-// tile by tile) and processes tile t as soon as its codes are in, while the
-// later tiles' are still on the way.  For one chunk, lane (n = l % 16, kq = l / 16)
-// loads 16 bytes = group 4c + kq of row n (a 16-row tile is 16 contiguous
-// 64-byte runs) with a raw buffer load: rows or groups past the end read
-// as zero in hardware, so no load sits behind a branch and all of them are
-// in flight together.  A 4 x 4 transpose across the four 16-lane rows
-// (v_permlane32_swap + v_permlane16_swap) then gives lane (n, kq) word kq
-// of all four groups, which is exactly its B operand slot for a one-group
-// MFMA (v_mfma_f32_16x16x32_bf16: A = X rows, B = weight rows): the A
-// operand of lane (m, kq) is then the contiguous 16 bytes 8 kq .. 8 kq + 7
-// of the group in X row m, so an X load instruction reads one 64-byte run
-// per row.  Per-wave partials meet in LDS (fixed wave order,
-// deterministic) once per K pass; each output is owned by one thread.
+// 256-element K slice (two 128-element "chunks" of four groups) and keeps
+// its slice of X in registers (loaded once, reused for every weight row).
+// The workgroup covers T tiles of 16 weight rows.  For one chunk c, lane
+// (n = l % 16, kq = l / 16) loads the 16 bytes of group 4 c + kq of row n
+// (a 16-row tile is 16 contiguous 64-byte runs) with a raw buffer load;
+// rows or groups past the end read as zero in hardware, so no load sits
+// behind a branch.  Word j of those 16 bytes is the lane's B operand of
+// MFMA j (v_mfma_f32_16x16x32_bf16: A = X rows, B = weight rows), whose 32
+// k values are elements 8 j .. 8 j + 7 of the four groups of the chunk, so
+// a lane dequantizes all four words of one group with one scale.  The
+// activations come in as contiguous 64-byte runs per row (lane (m, kq):
+// elements 8 kq .. 8 kq + 7 of group 4 c + j, one load per j) and a 4 x 4
+// transpose of 16-byte pieces across the four 16-lane rows (v_permlane32_swap
+// + v_permlane16_swap), done once per wave, gives lane (m, kq) its A
+// operands: elements 8 j .. 8 j + 7 of group 4 c + kq of row m.  A wave's
+// eight scales of a row are one 16-byte load: lane row r fetches tile r's,
+// permlane swaps broadcast them, and each lane picks its group's.
+//   Each wave issues all of its loads at once (scales and activations first,
+// then the codes tile by tile) and processes tile t as soon as its codes
+// are in, while the later tiles' are still on the way.  Per-wave partials
+// meet in LDS (fixed wave order, deterministic) once per K pass; each
+// output is owned by one thread.
 //
 // Kernel-order codes (TL, written by w4_repack): the 16 bytes of group g of
 // row n sit in the 1 KB block (n / 32, g / 2) at unit 32 (g % 2) + n % 32,
@@ -56,50 +61,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
                                            0x00020000);
 }
 
-// This lane row's 8 zero points of weight row srow, groups g0 .. g0 + 7
-// (two dwords); the SALIGNED block is clamped into the row like the scales.
-template <bool SALIGNED>
-__device__ __forceinline__ u32x2 load_zp8(__amdgpu_buffer_rsrc_t zr, uint32_t srow, int g0, int G) {
-  if constexpr (SALIGNED) {
-    const uint32_t gb = (uint32_t)min(g0, G - 8);
-    return __builtin_amdgcn_raw_buffer_load_b64(zr, srow * (uint32_t)G + gb, 0, 0);
-  } else {
-    uint32_t b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int gj = g0 + j;
-      const uint32_t zoff = (gj < G) ? srow * (uint32_t)G + (uint32_t)gj : kOOB;
-      b[j] = __builtin_amdgcn_raw_buffer_load_b8(zr, zoff, 0, 0);
-    }
-    return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                 b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
-  }
-}
-
-// This lane row's 8 scales of weight row srow, groups g0 .. g0 + 7 (four
-// dwords, bf16 pairs); a SALIGNED block past K is clamped into the row,
-// where codes and activations read zero.
-template <bool SALIGNED>
-__device__ __forceinline__ u32x4 load_scale8(__amdgpu_buffer_rsrc_t sr, uint32_t srow, int g0,
-                                             int G) {
-  if constexpr (SALIGNED) {
-    const uint32_t gb = (uint32_t)min(g0, G - 8);
-    return __builtin_amdgcn_raw_buffer_load_b128(sr, (srow * (uint32_t)G + gb) * 2u, 0, 0);
-  } else {
-    uint32_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int gj = g0 + j;
-      const uint32_t soff = (gj < G) ? (srow * (uint32_t)G + gj) * 2u : kOOB;
-      h[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
-    }
-    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                 h[6] | (h[7] << 16)};
-  }
-}
-
 // 4 x 4 transpose across the four 16-lane rows: on entry lane row r holds
-// words 0..3 of group r; on exit it holds word r of groups 0..3.
+// dwords 0..3 of item r; on exit it holds dword r of items 0..3.
 __device__ __forceinline__ u32x4 transpose_rows(u32x4 v) {
   auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
   auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
@@ -108,22 +71,25 @@ __device__ __forceinline__ u32x4 transpose_rows(u32x4 v) {
   return u32x4{c[0], c[1], d[0], d[1]};
 }
 
+// On entry lane (m, kq) holds in x[j] elements 8 kq .. 8 kq + 7 of group
+// 4 c + j of its row; on exit x[j] holds elements 8 j .. 8 j + 7 of group
+// 4 c + kq (the same transpose for each of the four dwords of a piece).
+__device__ __forceinline__ void transpose_pieces(u32x4 (&x)[4]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 v = transpose_rows(u32x4{x[0][d], x[1][d], x[2][d], x[3][d]});
+    x[0][d] = v.x;
+    x[1][d] = v.y;
+    x[2][d] = v.z;
+    x[3][d] = v.w;
+  }
+}
+
 // 16 bytes per lane from a buffer straight into LDS (buffer_load ... lds):
 // lane l's bytes land at dst + 16 l.
 __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            off, 0, 0, 0);
-}
-
-// Copies of v with all four 16-lane rows replaced by row 0, 1, 2, 3.
-__device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
-  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // [r0 r1 r0 r1], [r2 r3 r2 r3]
-  auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
-  auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
-  out[0] = lo[0];
-  out[1] = lo[1];
-  out[2] = hi[0];
-  out[3] = hi[1];
 }
 
 // Code buffer of a workgroup's rows [n0, n0 + rows) and the byte offset of
@@ -146,8 +112,10 @@ struct CodeRows {
       r = rsrc(Wq + (size_t)n0 * (K >> 3), (uint32_t)rows * rowb);
     }
   }
+  // FULL: every group index the caller passes is below G
+  template <bool FULL>
   __device__ __forceinline__ uint32_t off(uint32_t nl, int g, int G) const {
-    if (g >= G) return kOOB;
+    if (!FULL && g >= G) return kOOB;
     if constexpr (TL) {
       const uint32_t n = first + nl;
       return (((n >> 5) * nsteps + ((uint32_t)g >> 1)) * 64u + ((uint32_t)g & 1u) * 32u +
@@ -162,25 +130,134 @@ __device__ __forceinline__ uint32_t word_of(u32x4 v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// dequant8 constants of group 4 cc + j of the wave's chunk cc: scale from
-// the broadcast scale dwords sct (bf16 pairs, groups 0..7 of the slice),
-// zero point from byte j of zc
-template <bool ZP>
-__device__ __forceinline__ DeqScale group_consts(const uint32_t (&sct)[4], uint32_t zc, int cc,
-                                                 int j) {
-  const uint32_t sp = sct[2 * cc + (j >> 1)];
-  const float s = (j & 1) ? bf16_hi(sp) : bf16_lo(sp);
-  if constexpr (ZP)
-    return deq_scale_zp(s, (float)((zc >> (8 * j)) & 0xFFu));
-  else
-    return deq_scale(s);
+// This lane row's 8 scales of weight row srow, groups g0 .. g0 + 7 (four
+// dwords, bf16 pairs); SALIGNED (K / 32 a multiple of 8): one 16-byte load,
+// a block past K clamped into the row (where codes and activations read
+// zero); otherwise eight 2-byte loads, groups past K reading zero.
+template <bool SALIGNED>
+__device__ __forceinline__ u32x4 load_scale8(__amdgpu_buffer_rsrc_t sr, uint32_t srow, int g0,
+                                             int G) {
+  if constexpr (SALIGNED) {
+    const uint32_t gb = (uint32_t)min(g0, G - 8);
+    return __builtin_amdgcn_raw_buffer_load_b128(sr, (srow * (uint32_t)G + gb) * 2u, 0, 0);
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int gj = g0 + j;
+      const uint32_t soff = (gj < G) ? (srow * (uint32_t)G + gj) * 2u : kOOB;
+      h[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+    }
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                 h[6] | (h[7] << 16)};
+  }
+}
+
+// The same for the row's 8 zero points (two dwords).
+template <bool SALIGNED>
+__device__ __forceinline__ u32x2 load_zp8(__amdgpu_buffer_rsrc_t zr, uint32_t srow, int g0, int G) {
+  if constexpr (SALIGNED) {
+    const uint32_t gb = (uint32_t)min(g0, G - 8);
+    return __builtin_amdgcn_raw_buffer_load_b64(zr, srow * (uint32_t)G + gb, 0, 0);
+  } else {
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int gj = g0 + j;
+      const uint32_t zoff = (gj < G) ? srow * (uint32_t)G + (uint32_t)gj : kOOB;
+      b[j] = __builtin_amdgcn_raw_buffer_load_b8(zr, zoff, 0, 0);
+    }
+    return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                 b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  }
+}
+
+// Copies of v with all four 16-lane rows replaced by row 0, 1, 2, 3.
+__device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
+  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // [r0 r1 r0 r1], [r2 r3 r2 r3]
+  auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// The wave's scales (and zero points) of one pass.  Lane row r loads the 8
+// groups of the wave's slice of row n16 of tile r (one 16-byte load; 8
+// bytes of zero points) and permlane swaps broadcast them, so every lane
+// holds its row's 8 scales of every tile; lane (n16, kq) then takes group
+// 4 cc + kq of chunk cc (a dword select and a byte permute).
+template <bool SALIGNED, int T, bool ZP>
+struct PassScales {
+  uint32_t sct[T][4];      // [tile][dword]: 8 bf16 scales
+  uint32_t zc[kCPW][T];    // [chunk][tile]: the 4 zero points of the chunk's groups
+  u32x4 sraw;
+  u32x2 zraw;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t zr,
+                                       int n16, int kq, int g0, int G) {
+    sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
+    zraw = u32x2{0u, 0u};
+    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+  }
+  __device__ __forceinline__ void spread() {
+    const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t b[4];
+      broadcast_rows(rw[d], b);
+#pragma unroll
+      for (int t = 0; t < T; ++t) sct[t][d] = b[t];
+    }
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc) {
+      if constexpr (ZP) {
+        uint32_t b[4];
+        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[cc][t] = b[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) zc[cc][t] = 0u;
+      }
+    }
+  }
+  // dequant8 constants of group 4 cc + kq of tile t: its bf16 is bytes
+  // 2 kq, 2 kq + 1 of dwords 2 cc, 2 cc + 1 taken as one 8-byte value; one
+  // byte permute (sel) moves them to the high half over zero bits (an fp32)
+  __device__ __forceinline__ DeqScale consts(int t, int cc, uint32_t sel, int kq) const {
+    const uint32_t b = __builtin_amdgcn_perm(sct[t][2 * cc + 1], sct[t][2 * cc], sel);
+    const float s = __uint_as_float(b);
+    if constexpr (ZP)
+      return deq_scale_zp(s, (float)((zc[cc][t] >> (8 * kq)) & 0xFFu));
+    else
+      return deq_scale(s);
+  }
+};
+
+// The codes of one pass: lane (n16, kq) loads words 0..3 of group
+// 4 (c0 + cc) + kq of row t * 16 + n16, tile by tile (rows past the
+// workgroup's and groups past K read zero).
+template <bool FULL, int T, bool TL>
+__device__ __forceinline__ void load_codes(u32x4 (&wv)[T][kCPW], const CodeRows<TL>& wr, int c0,
+                                           int n16, int kq, int G) {
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int cc = 0; cc < kCPW; ++cc)
+      wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(
+          wr.r, wr.template off<FULL>((uint32_t)(t * 16 + n16), 4 * (c0 + cc) + kq, G), 0, 0);
 }
 
 }  // namespace
 
-// M <= 16.  SALIGNED: K / 32 is a multiple of 8 (a wave's eight scales of
-// one row are one 16-byte load).  T: tiles of 16 weight rows per workgroup.
-template <bool SALIGNED, int T, bool ZP, bool TL>
+// M <= 16.  KM: 0 = any K; 1 = K / 32 is a multiple of 8 (a wave's eight
+// scales of one row are one 16-byte load); 2 = K is a multiple of the
+// 4096-element pass as well (no group index is ever past K, so no offset
+// needs a range check).  Activation rows past M need none either: they lie
+// past the end of X's buffer and read zero.  T: tiles of 16 weight rows per
+// workgroup.
+template <int KM, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -188,6 +265,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 4, "decode shape");
+  constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
   constexpr int PSTR = 20;                         // LDS row stride (floats)
   constexpr int WSTR = 16 * PSTR + 4;              // per-wave block: padded off the bank period
   __shared__ __attribute__((aligned(16))) float part[T][kWaves][WSTR];
@@ -209,15 +287,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t zr =
       rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
+  // byte permute selector: bytes 2 kq + 1, 2 kq of the 8-byte value (low
+  // dword = bytes 0..3) to the high half, zero bytes (0x0C) below
+  const uint32_t sel = ((2u * kq + 1u) << 24) | ((2u * kq) << 16) | 0x0C0Cu;
 
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
-    // ---- scales (and zero points) first: lane row r fetches the wave's 8
-    // groups of row n16 of tile r
-    const int g0 = 4 * c0;
-    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
-    u32x2 zraw = u32x2{0u, 0u};
-    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    // ---- scales (and zero points) first
+    PassScales<SALIGNED, T, ZP> sc;
+    sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- activations (L2 hits after the first CU's request): lane (m, kq)
     // takes elements 8 kq .. 8 kq + 7 of group 4 c + j of row m
     u32x4 xop[kCPW][4];
@@ -226,63 +304,30 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int g = 4 * (c0 + cc) + j;
-        const uint32_t off = (g < G && n16 < M)
-                                 ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u
-                                 : kOOB;
+        const uint32_t off =
+            (FULL || g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
         xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
       }
-    // ---- codes, tile by tile (rows past the end read zero); a row's two
-    // chunks are adjacent requests (one 128-byte line).  Loads return in
-    // issue order, so tile t is processed as soon as its codes are in while
-    // the later tiles' are still on the way.
+    // ---- codes, tile by tile; a row's two chunks are adjacent requests (one
+    // 128-byte line).  Loads return in issue order, so tile t is processed as
+    // soon as its codes are in while the later tiles' are still on the way.
     u32x4 wv[T][kCPW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint32_t nl = (uint32_t)(t * 16 + n16);
-#pragma unroll
-      for (int cc = 0; cc < kCPW; ++cc) {
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
-                                                          0, 0);
-      }
-    }
+    load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
-    uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
-    {
-      const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+    sc.spread();
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t b[4];
-        broadcast_rows(rw[d], b);
-#pragma unroll
-        for (int t = 0; t < T; ++t) sct[t][d] = b[t];
-      }
-    }
-    uint32_t zc[kCPW][T];                // ZP: tile t's zero points of chunk cc's groups
-#pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc) {
-      if constexpr (ZP) {
-        uint32_t b[4];
-        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[cc][t] = b[t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[cc][t] = 0u;
-      }
-    }
+    for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) {
-        const u32x4 u = transpose_rows(wv[t][cc]);
+        const DeqScale dq = sc.consts(t, cc, sel, kq);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const DeqScale dq = group_consts<ZP>(sct[t], zc[cc][t], cc, j);
-          acc = mfma16(xop[cc][j], dequant8<ZP>(word_of(u, j), dq), acc);
-        }
+        for (int j = 0; j < 4; ++j)
+          acc = mfma16(xop[cc][j], dequant8<ZP>(word_of(wv[t][cc], j), dq), acc);
       }
       // lane holds D[m = 4 kq + r][n = n16] of tile t
       *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc;
@@ -315,10 +360,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 
 // 16 < M <= 32 over two 16-row activation halves.  Half 0's X sits in
 // registers as for M <= 16; half 1's X goes straight into this wave's LDS
-// region (direct-to-LDS loads issued with the others) and is read per group
-// where it is used.  Each dequantized word feeds the MFMAs of both halves.
-// The region then takes the wave's partial sums.
-template <bool SALIGNED, int T, bool ZP, bool TL>
+// region (direct-to-LDS loads issued with the others, in the order they
+// arrive in: lane (m, kq) of load 4 cc + j brings elements 8 kq .. of group
+// 4 c + j) and each lane reads its operand of MFMA j from where it landed.
+// Each dequantized word feeds the MFMAs of both halves.  The region then
+// takes the wave's partial sums.
+template <int KM, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -326,6 +373,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 3, "decode shape");
+  constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
   constexpr int PSTR = 36;                         // LDS row stride (floats): 32 rows + pad
   constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
   constexpr int XREG = kCPW * 4 * 256;             // floats: 8 x 1 KB of half-1 activations
@@ -349,22 +397,23 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t zr =
       rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
+  // byte permute selector: bytes 2 kq + 1, 2 kq of the 8-byte value (low
+  // dword = bytes 0..3) to the high half, zero bytes (0x0C) below
+  const uint32_t sel = ((2u * kq + 1u) << 24) | ((2u * kq) << 16) | 0x0C0Cu;
 
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
     // byte offset of lane (n16, kq)'s 16 activation bytes of group 4 c + j
-    // in half hh (rows past M and groups past K read zero)
+    // in half hh (rows past M lie past the buffer and groups past K are sent
+    // past it: both read zero)
     auto x_off = [&](int hh, int cc, int j) {
       const int g = 4 * (c0 + cc) + j;
       const int row = 16 * hh + n16;
-      return (g < G && row < M) ? ((uint32_t)row * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
+      return (FULL || g < G) ? ((uint32_t)row * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
     };
-    // ---- scales (and zero points) first: lane row r fetches the wave's 8
-    // groups of row n16 of tile r
-    const int g0 = 4 * c0;
-    const u32x4 sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
-    u32x2 zraw = u32x2{0u, 0u};
-    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    // ---- scales (and zero points) first
+    PassScales<SALIGNED, T, ZP> sc;
+    sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- half 0's activations into registers, half 1's into this wave's
     // LDS region: load 4 cc + j of lane l lands at byte 1024 (4 cc + j) + 16 l
     u32x4 xop[kCPW][4];
@@ -378,44 +427,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         dma16_to_lds(xr, &lds[wave][(4 * cc + j) * 256], x_off(1, cc, j));
-    // ---- codes, tile by tile (rows past the end read zero); loads return in
-    // issue order, so tile t is processed as soon as its codes are in
+    // ---- codes, tile by tile; loads return in issue order, so tile t is
+    // processed as soon as its codes are in
     u32x4 wv[T][kCPW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint32_t nl = (uint32_t)(t * 16 + n16);
-#pragma unroll
-      for (int cc = 0; cc < kCPW; ++cc) {
-        wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(wr.r, wr.off(nl, 4 * (c0 + cc) + kq, G),
-                                                          0, 0);
-      }
-    }
+    load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
-    uint32_t sct[T][4];                  // [tile][dword]: 8 bf16 scales
-    {
-      const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+    sc.spread();
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t b[4];
-        broadcast_rows(rw[d], b);
-#pragma unroll
-        for (int t = 0; t < T; ++t) sct[t][d] = b[t];
-      }
-    }
-    uint32_t zc[kCPW][T];                // ZP: tile t's zero points of chunk cc's groups
-#pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc) {
-      if constexpr (ZP) {
-        uint32_t b[4];
-        broadcast_rows(cc == 0 ? zraw.x : zraw.y, b);
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[cc][t] = b[t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < T; ++t) zc[cc][t] = 0u;
-      }
-    }
+    for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
 
     f32x4 acc0[T], acc1[T];
 #pragma unroll
@@ -424,12 +444,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) {
-        const u32x4 u = transpose_rows(wv[t][cc]);
+        const DeqScale dq = sc.consts(t, cc, sel, kq);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + j) * 256 + 4 * lane];
-          const DeqScale dq = group_consts<ZP>(sct[t], zc[cc][t], cc, j);
-          const u32x4 w = dequant8<ZP>(word_of(u, j), dq);
+          // elements 8 j .. 8 j + 7 of group 4 c + kq of half-1 row n16 came
+          // with load 4 cc + kq, in lane n16 + 16 j
+          const u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + kq) * 256 + 4 * (n16 + 16 * j)];
+          const u32x4 w = dequant8<ZP>(word_of(wv[t][cc], j), dq);
           acc0[t] = mfma16(xop[cc][j], w, acc0[t]);
           acc1[t] = mfma16(x1, w, acc1[t]);
         }
@@ -484,59 +505,62 @@ int cu_count() {
   return cus[dev];
 }
 
-template <bool SA, int T, bool ZP, bool TL>
+template <int KM, int T, bool ZP, bool TL>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<SA, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((k_decode16<KM, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, bool ZP, bool TL>
+template <int KM, bool ZP, bool TL>
 hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode16_t<SA, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<SA, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<SA, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode16_t<SA, 4, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<KM, 4, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
-template <bool SA, int T, bool ZP, bool TL>
+template <int KM, int T, bool ZP, bool TL>
 hipError_t run_decode32_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode32<SA, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((k_decode32<KM, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <bool SA, bool ZP, bool TL>
+template <int KM, bool ZP, bool TL>
 hipError_t run_decode32(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
                         uint16_t* Y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode32_t<SA, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode32_t<SA, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode32_t<SA, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode32_t<KM, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode32_t<KM, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode32_t<KM, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 template <bool ZP, bool TL>
 hipError_t launch_decode(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                          const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                          hipStream_t st) {
-  const bool sa = ((K >> 5) & 7) == 0;
-  if (M <= 16)
-    return sa ? run_decode16<true, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st)
-              : run_decode16<false, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  return sa ? run_decode32<true, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st)
-            : run_decode32<false, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  const int km = K % kPassK == 0 ? 2 : ((K >> 5) & 7) == 0 ? 1 : 0;
+  if (M <= 16) {
+    if (km == 2) return run_decode16<2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+    if (km == 1) return run_decode16<1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+    return run_decode16<0, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  }
+  if (km == 2) return run_decode32<2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (km == 1) return run_decode32<1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode32<0, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 }  // namespace

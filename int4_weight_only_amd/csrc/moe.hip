@@ -39,6 +39,18 @@ constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
 
+// Inclusive prefix sum over the wave's 64 lanes (DPP row shifts within
+// each 16-lane row, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return v;
+}
+
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
 __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restrict__ ids,
@@ -93,20 +105,20 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   }
   __syncthreads();
 
-  // 2. segment starts (thread e owns expert e), then per-wave positions
+  // 2. segment starts (thread e owns expert e and keeps its 16 wave counts
+  // in registers), then per-wave positions
   int c = 0;
+  int hc[kAlignWaves];
   if (tid < E) {
 #pragma unroll
-    for (int w = 0; w < kAlignWaves; ++w) c += pos[w][tid];
+    for (int w = 0; w < kAlignWaves; ++w) {
+      hc[w] = pos[w][tid];
+      c += hc[w];
+    }
     count[tid] = c;
   }
   const int padded = (tid < E) ? ((c + B - 1) / B) * B : 0;
-  int incl = padded;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_incl_scan(padded);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   int wprefix = 0;
@@ -117,9 +129,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
     int run = s0;
 #pragma unroll
     for (int w = 0; w < kAlignWaves; ++w) {
-      const int n = pos[w][tid];
       pos[w][tid] = run;
-      run += n;
+      run += hc[w];
     }
   }
   if (tid == kAlignThreads - 1) total_sh = wprefix + incl;
