@@ -22,7 +22,8 @@ namespace w4 {
 // thousand to a few tens of thousands, and must be stable and exact).  Wave
 // w owns the contiguous pair range [w*P/16, (w+1)*P/16).
 //  1. per-wave histograms of experts in LDS (atomics on the wave's own
-//     counters: counts do not depend on order);
+//     counters, which the wave clears itself: counts do not depend on
+//     order);
 //  2. exclusive scan of the padded counts -> segment starts; then, per
 //     expert, a scan over the waves in wave order turns the wave's count
 //     into the position where its first pair of that expert goes;
@@ -82,11 +83,12 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
     }
   };
 
-  // the wave's first batch of ids is in flight while the counters are cleared
+  // the wave's first batch of ids is in flight while it clears its own
+  // counters (only this wave touches them until the barrier after step 1,
+  // and its LDS accesses take effect in program order)
   int v0[kBatch];
   load_batch(f_lo, v0);
-  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) pos[i / E][i % E] = 0;
-  __syncthreads();
+  for (int i = lane; i < E; i += 64) pos[wave][i] = 0;
 
   // 1. per-wave histograms; a wave whose range fits one batch keeps its
   // ids in registers for step 3
