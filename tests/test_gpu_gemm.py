@@ -76,10 +76,12 @@ def test_integer_exact(M):
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 32, 33, 130])
-@pytest.mark.parametrize("K", [4640, 8192])
+@pytest.mark.parametrize("K", [4640, 8192, 2048, 6144])
 def test_long_k(M, K):
     """K above one 4096-wide decode pass (the pass partials carry in LDS);
-    4640 also leaves K / 32 off a multiple of 8 (unaligned scale rows)."""
+    4640 also leaves K / 32 off a multiple of 8 (unaligned scale rows);
+    2048 and 6144 have aligned scale rows but a partial decode pass (the
+    range-checked offsets), 8192 whole passes (offsets without checks)."""
     run_case(M, 200, K, 7 * M + K, "long K")
 
 

@@ -65,7 +65,7 @@ def test_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 32, 33, 130])
-@pytest.mark.parametrize("K", [4640, 8192])
+@pytest.mark.parametrize("K", [4640, 8192, 2048, 6144])
 def test_long_k(M, K):
     """K above one decode pass; 4640 also leaves K / 32 off a multiple of 8
     (byte-wise zero-point and scale loads)."""
