@@ -92,6 +92,36 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst
                                            off, 0, 0, 0);
 }
 
+// 16 rows x 256 activations (rows row0 .. row0 + 15 of X, the wave's K
+// slice from chunk c0) into an LDS region of 16 rows x 512 bytes, whole
+// 128-byte lines: load i brings rows 2 i, 2 i + 1; lane l's 16 bytes land in
+// slot l % 32 of row r = 2 i + l / 32 and hold the slice's piece
+// (l % 32) ^ r, so that 16 lanes reading one piece of 16 rows hit 16
+// different slots (no bank conflicts).  Rows past M lie past X's buffer and
+// groups past K are sent past it: both read zero.
+template <bool FULL>
+__device__ __forceinline__ void load_x_lines(__amdgpu_buffer_rsrc_t xr, float* region, int row0,
+                                             int c0, int lane, int K, int G) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const int gp = (lane & 31) ^ r;
+    const int g = 4 * c0 + (gp >> 2);
+    const uint32_t off =
+        (FULL || g < G)
+            ? ((uint32_t)(row0 + r) * (uint32_t)K + 128u * (uint32_t)c0 + 8u * (uint32_t)gp) * 2u
+            : kOOB;
+    dma16_to_lds(xr, region + 256 * i, off);
+  }
+}
+
+// float index of piece 16 cc + 4 kq + j of row r (< 16) in a region written
+// by load_x_lines: the XOR with r leaves bit 4 alone, so chunk cc is a
+// constant offset from the index of chunk 0
+__device__ __forceinline__ int x_slot(int r, int kq, int j, int cc) {
+  return 128 * r + 4 * ((4 * kq + j) ^ r) + 64 * cc;
+}
+
 // Code buffer of a workgroup's rows [n0, n0 + rows) and the byte offset of
 // the 16 bytes of group g of its row nl (kOOB past K).  Canonical: rows of
 // K / 2 bytes from row n0.  Kernel order: the 1 KB blocks of the 32-row
@@ -174,7 +204,7 @@ __device__ __forceinline__ u32x2 load_zp8(__amdgpu_buffer_rsrc_t zr, uint32_t sr
 
 // Copies of v with all four 16-lane rows replaced by row 0, 1, 2, 3.
 __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
-  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // [r0 r1 r0 r1], [r2 r3 r2 r3]
+  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // [r0 r1 r0 r1], [r2 r3 r2 r3]
   auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
   auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
   out[0] = lo[0];
@@ -256,8 +286,12 @@ __device__ __forceinline__ void load_codes(u32x4 (&wv)[T][kCPW], const CodeRows<
 // 4096-element pass as well (no group index is ever past K, so no offset
 // needs a range check).  Activation rows past M need none either: they lie
 // past the end of X's buffer and read zero.  T: tiles of 16 weight rows per
-// workgroup.
-template <int KM, int T, bool ZP, bool TL>
+// workgroup.  XL (for 8 < M <= 16, T <= 3): the activations come through the wave's
+// LDS region in whole 128-byte lines (two rows per load, half the cache-line
+// requests of the 64-byte runs) and each lane reads its operands in MFMA
+// order, with no transpose; for M <= 8 the extra LDS round trip costs more
+// than the lines it saves, and they go to registers.
+template <int KM, int T, bool ZP, bool TL, bool XL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -267,8 +301,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   static_assert(T >= 1 && T <= 4, "decode shape");
   constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
   constexpr int PSTR = 20;                         // LDS row stride (floats)
-  constexpr int WSTR = 16 * PSTR + 4;              // per-wave block: padded off the bank period
-  __shared__ __attribute__((aligned(16))) float part[T][kWaves][WSTR];
+  constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
+  constexpr int XREG = XL ? 2048 : 0;              // floats: the wave's 16 x 256 activations
+  constexpr int REGION = T * WSTR > XREG ? T * WSTR : XREG;
+  __shared__ __attribute__((aligned(16))) float lds[kWaves][REGION];
   __shared__ float ybuf[T][256];                   // partials across K passes
 
   const int tid = threadIdx.x;
@@ -296,18 +332,26 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
     // ---- scales (and zero points) first
     PassScales<SALIGNED, T, ZP> sc;
     sc.load(sr, zr, n16, kq, 4 * c0, G);
-    // ---- activations (L2 hits after the first CU's request): lane (m, kq)
-    // takes elements 8 kq .. 8 kq + 7 of group 4 c + j of row m
+    // ---- activations (L2 hits after the first CU's request)
     u32x4 xop[kCPW][4];
+    if constexpr (XL) {
+      // into this wave's LDS region: load i brings rows 2 i, 2 i + 1 of the
+      // wave's 16 x 256 slice; lane l's 16 bytes land in slot l % 32 of row
+      // 2 i + l / 32 and hold piece (l % 32) ^ row of it
+      load_x_lines<FULL>(xr, &lds[wave][0], 0, c0, lane, K, G);
+    } else {
+      // lane (m, kq) takes elements 8 kq .. 8 kq + 7 of group 4 c + j of row m
 #pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc)
+      for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = 4 * (c0 + cc) + j;
-        const uint32_t off =
-            (FULL || g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
-        xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int g = 4 * (c0 + cc) + j;
+          const uint32_t off =
+              (FULL || g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
+          xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the codes are issued after every activation load
     // ---- codes, tile by tile; a row's two chunks are adjacent requests (one
     // 128-byte line).  Loads return in issue order, so tile t is processed as
     // soon as its codes are in while the later tiles' are still on the way.
@@ -315,9 +359,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
     load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
-    sc.spread();
+    if constexpr (XL) {
+      // the activations have landed once only the codes are in flight; lane
+      // (m, kq)'s operand of MFMA j of chunk cc (elements 8 j .. 8 j + 7 of
+      // group 4 c + kq of row m) is piece 16 cc + 4 kq + j of row m
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T * kCPW) : "memory");
 #pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
+      for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xop[cc][j] = *(const u32x4*)&lds[wave][x_slot(n16, kq, j, cc)];
+    }
+    sc.spread();
+    if constexpr (!XL) {
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
+    }
 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -329,8 +386,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
         for (int j = 0; j < 4; ++j)
           acc = mfma16(xop[cc][j], dequant8<ZP>(word_of(wv[t][cc], j), dq), acc);
       }
-      // lane holds D[m = 4 kq + r][n = n16] of tile t
-      *(f32x4*)&part[t][wave][n16 * PSTR + 4 * kq] = acc;
+      // lane holds D[m = 4 kq + r][n = n16] of tile t; the wave has read all
+      // of its activations (LDS accesses in program order)
+      *(f32x4*)&lds[wave][t * WSTR + n16 * PSTR + 4 * kq] = acc;
       __builtin_amdgcn_sched_barrier(0);   // tile t's work stays ahead of tile t + 1's wait
     }
 
@@ -346,7 +404,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
       const int e = n * PSTR + m;
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += part[t][w][e];
+      for (int w = 0; w < kWaves; ++w) sum += lds[w][t * WSTR + e];
       const int row = t * 16 + n;
       if (npass > 1) {
         sum += (pass == 0) ? 0.0f : ybuf[t][m * 16 + n];
@@ -354,17 +412,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
       }
       if (pass == npass - 1 && row < rows) Y[(size_t)m * N + n0 + row] = to_bf16(sum);
     }
-    if (npass > 1) __syncthreads();   // part is rewritten by the next pass
+    if (npass > 1) __syncthreads();   // the regions are rewritten by the next pass
   }
 }
 
 // 16 < M <= 32 over two 16-row activation halves.  Half 0's X sits in
-// registers as for M <= 16; half 1's X goes straight into this wave's LDS
-// region (direct-to-LDS loads issued with the others, in the order they
-// arrive in: lane (m, kq) of load 4 cc + j brings elements 8 kq .. of group
-// 4 c + j) and each lane reads its operand of MFMA j from where it landed.
-// Each dequantized word feeds the MFMAs of both halves.  The region then
-// takes the wave's partial sums.
+// registers as for M <= 8; half 1's X goes straight into this wave's LDS
+// region in whole lines (load_x_lines, issued with the others) and each lane
+// reads its operand of MFMA j where it landed.  Each dequantized word feeds
+// the MFMAs of both halves.  The region then takes the wave's partial sums.
 template <int KM, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
@@ -415,18 +471,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
     PassScales<SALIGNED, T, ZP> sc;
     sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- half 0's activations into registers, half 1's into this wave's
-    // LDS region: load 4 cc + j of lane l lands at byte 1024 (4 cc + j) + 16 l
+    // LDS region in whole lines
     u32x4 xop[kCPW][4];
 #pragma unroll
     for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(0, cc, j), 0, 0);
-#pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma16_to_lds(xr, &lds[wave][(4 * cc + j) * 256], x_off(1, cc, j));
+    load_x_lines<FULL>(xr, &lds[wave][0], 16, c0, lane, K, G);
     // ---- codes, tile by tile; loads return in issue order, so tile t is
     // processed as soon as its codes are in
     u32x4 wv[T][kCPW];
@@ -447,9 +499,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
         const DeqScale dq = sc.consts(t, cc, sel, kq);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // elements 8 j .. 8 j + 7 of group 4 c + kq of half-1 row n16 came
-          // with load 4 cc + kq, in lane n16 + 16 j
-          const u32x4 x1 = *(const u32x4*)&lds[wave][(4 * cc + kq) * 256 + 4 * (n16 + 16 * j)];
+          // elements 8 j .. 8 j + 7 of group 4 c + kq of half-1 row n16
+          const u32x4 x1 = *(const u32x4*)&lds[wave][x_slot(n16, kq, j, cc)];
           const u32x4 w = dequant8<ZP>(word_of(wv[t][cc], j), dq);
           acc0[t] = mfma16(xop[cc][j], w, acc0[t]);
           acc1[t] = mfma16(x1, w, acc1[t]);
@@ -505,12 +556,12 @@ int cu_count() {
   return cus[dev];
 }
 
-template <int KM, int T, bool ZP, bool TL>
+template <int KM, int T, bool ZP, bool TL, bool XL>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<KM, T, ZP, TL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((k_decode16<KM, T, ZP, TL, XL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -521,10 +572,15 @@ hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode16_t<KM, 4, ZP, TL>(X, Wq, S, Z, Y, M, N, K, st);
+  if (M > 8 && tpw <= 3) {   // (four tiles leave no registers for the LDS path)
+    if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
+    if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
+    return run_decode16_t<KM, 3, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
+  }
+  if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<KM, 4, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 template <int KM, int T, bool ZP, bool TL>
