@@ -14,6 +14,15 @@ and the equality of products on either layout are checked):
   (the canonical row holds its K/32 groups of 4 words each in order);
 * units whose row is >= N or whose group is >= K/32 are zero;
 * E matrices (experts) are stored one after another.
+
+Per-group values (bf16 scales, uint8 zero points, [N, K/32] canonical)
+have a kernel order of their own, read by the same products:
+
+* per matrix, ceil(N/16) x ceil(G/8) blocks of 128 elements (G = K/32),
+  block (r, c) at element 128 (r ceil(G/8) + c);
+* element 8 i + j of a block is the value of row 16 r + i, group 8 c + j
+  (16 rows x 8 groups, row-major);
+* elements whose row is >= N or whose group is >= G are zero.
 """
 
 import numpy as np
@@ -57,3 +66,41 @@ def restore(Wt, N, K):
     out = np.zeros((E, N, K // 32, 4), dtype=np.int32)
     out[:, n[valid], g[valid]] = Wt[:, valid]
     return out.reshape(E, N, K // 8)
+
+
+def repacked_group_elems(N, K):
+    """Elements of one [N, K/32] per-group array in kernel order."""
+    return -(-N // 16) * -(-(K // 32) // 8) * 128
+
+
+def _group_map(N, K):
+    """For every element of the kernel-order buffer: (row n, group g, valid)."""
+    G = K // 32
+    gb = -(-G // 8)
+    idx = np.arange(repacked_group_elems(N, K))
+    b, w = idx // 128, idx % 128
+    n = 16 * (b // gb) + w // 8
+    g = 8 * (b % gb) + w % 8
+    return n, g, (n < N) & (g < G)
+
+
+def repack_groups(A, K):
+    """Per-group values [N, K/32] or [E, N, K/32] -> [E, elements]."""
+    A = np.asarray(A)
+    if A.ndim == 2:
+        A = A[None]
+    E, N, G = A.shape
+    assert G == K // 32
+    n, g, valid = _group_map(N, K)
+    out = np.zeros((E, n.size), dtype=A.dtype)
+    out[:, valid] = A[:, n[valid], g[valid]]
+    return out
+
+
+def restore_groups(At, N, K):
+    """Kernel order [E, elements] -> per-group values [E, N, K/32]."""
+    At = np.asarray(At).reshape(-1, repacked_group_elems(N, K))
+    n, g, valid = _group_map(N, K)
+    out = np.zeros((At.shape[0], N, K // 32), dtype=At.dtype)
+    out[:, n[valid], g[valid]] = At[:, valid]
+    return out

@@ -53,3 +53,36 @@ def test_every_code_lands_where_the_layout_says(E, N, K):
                     + (k % 32) // 8
                 nib = int(Wt[e, w] >> np.uint32(4 * (k % 8))) & 0xF
                 assert (nib - 16 if nib >= 8 else nib) == q[e, n, k], (e, n, k)
+
+
+GROUP_SHAPES = [(1, 1, 32), (1, 15, 64), (1, 16, 256), (3, 17, 288), (2, 100, 4096), (1, 48, 544)]
+
+
+@pytest.mark.parametrize("E,N,K", GROUP_SHAPES)
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint8])
+def test_group_round_trip_and_size(E, N, K, dtype):
+    """Per-group values (bf16 scale bits, zero-point bytes): a lossless
+    permutation with zero padding."""
+    rng = np.random.default_rng(N + K)
+    A = rng.integers(1, 200, size=(E, N, K // 32)).astype(dtype)   # no zero value
+    At = layout.repack_groups(A, K)
+    elems = -(-N // 16) * -(-(K // 32) // 8) * 128
+    assert layout.repacked_group_elems(N, K) == elems
+    assert At.shape == (E, elems) and At.dtype == A.dtype
+    np.testing.assert_array_equal(layout.restore_groups(At, N, K), A)
+    assert np.count_nonzero(At) == E * N * (K // 32)
+
+
+@pytest.mark.parametrize("E,N,K", GROUP_SHAPES[:4])
+def test_every_group_value_lands_where_the_layout_says(E, N, K):
+    """Group g of row n is element 128 (r C + c) + 8 (n % 16) + g % 8 with
+    r = n // 16, c = g // 8, C = ceil(G / 8)."""
+    rng = np.random.default_rng(3 * N + K)
+    G = K // 32
+    A = rng.integers(0, 65535, size=(E, N, G)).astype(np.uint16)
+    At = layout.repack_groups(A, K)
+    C = -(-G // 8)
+    for e in range(E):
+        for n in range(N):
+            for g in range(G):
+                assert At[e, 128 * ((n // 16) * C + g // 8) + 8 * (n % 16) + g % 8] == A[e, n, g]
