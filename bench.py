@@ -5,9 +5,9 @@
 
 Headline line (one JSON object on stdout): the decode W4A16 product over
 packed INT4 weights W[12288 x 4096] (group 32, bf16 scales) against
-M in {1, 8, 16, 32} bf16 activation rows, with the codes in the
-kernel-order layout (w4_repack, converted once before timing, as an
-inference engine converts weights at load).  One step = those four products,
+M in {1, 8, 16, 32} bf16 activation rows, with the codes and the scales in
+the kernel-order layouts (w4_repack, w4_repack_groups, converted once
+before timing, as an inference engine converts weights at load).  One step = those four products,
 each on its own copy of the weights (24 copies rotate, 680 MB in all, so
 the 256 MB last-level cache never holds the step's weights).  ``value`` is
 the algorithmic HBM traffic of the step (packed codes + scales + X + Y)
@@ -165,15 +165,17 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
     del src
     Wqs = [Wq0] + [Wq0.clone() for _ in range(ROTATE - 1)]
     Ss = [S0] + [S0.clone() for _ in range(ROTATE - 1)]
-    # the codes in the kernel-order layout, converted once as at weight load
+    # codes and scales in the kernel-order layouts, converted once as at
+    # weight load
     Wts = [w4.w4_repack(W) for W in Wqs]
+    Sts = [w4.w4_repack_groups(S) for S in Ss]
     Xs = {M: synth.activations(M, DECODE_K, 1, device=dev) for M in DECODE_MS}
     Ys = {M: torch.empty((M, DECODE_N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
 
     def step(i):
         for j, M in enumerate(DECODE_MS):
             r = (4 * i + j) % ROTATE
-            w4.w4a16_gemm_tiled(Xs[M], Wts[r], Ss[r], out=Ys[M])
+            w4.w4a16_gemm_tiled(Xs[M], Wts[r], Sts[r], DECODE_N, out=Ys[M])
 
     timer.run(step, warmup)
     timer.settle(step)
@@ -183,7 +185,8 @@ def bench_decode(w4, synth, torch, steps, warmup, timer):
         torch, timer, steps, lambda M, r: w4.w4a16_gemm(Xs[M], Wqs[r], Ss[r], out=Ys[M]),
         lambda M: decode_bytes(M))
     per_m_tiled = graph_per_m(
-        torch, timer, steps, lambda M, r: w4.w4a16_gemm_tiled(Xs[M], Wts[r], Ss[r], out=Ys[M]),
+        torch, timer, steps,
+        lambda M, r: w4.w4a16_gemm_tiled(Xs[M], Wts[r], Sts[r], DECODE_N, out=Ys[M]),
         lambda M: decode_bytes(M))
     launches = steps * len(DECODE_MS)
     return dict(ms_step=ms / steps, step_bytes=step_bytes, launches=launches, total_ms=ms,
@@ -250,8 +253,8 @@ def bench_prefill(w4, synth, torch, iters, timer):
     timer.settle(f)
     t = timer.run(f, iters) / iters
     tf = gemm_flops(M, N, K) / (t * 1e-3) / 1e12
-    Wt = w4.w4_repack(Wq)
-    ft = lambda i: w4.w4a16_gemm_tiled(X, Wt, S, out=Y)
+    Wt, St = w4.w4_repack(Wq), w4.w4_repack_groups(S)
+    ft = lambda i: w4.w4a16_gemm_tiled(X, Wt, St, N, out=Y)
     timer.settle(ft, SETTLE_MS / 3)
     tt = timer.run(ft, iters) / iters
     tft = gemm_flops(M, N, K) / (tt * 1e-3) / 1e12
@@ -276,11 +279,14 @@ def bench_quant(w4, synth, torch, iters, timer):
     Wt = w4.w4_repack(Wq)
     Wr = torch.empty_like(Wq)
     rp_bytes = 2 * (N * K // 2)
+    St = w4.w4_repack_groups(S)
+    rg_bytes = 2 * (2 * N * (K // 32))
     for name, fn, nbytes in (("quantize_pack", lambda i: w4.w4_quantize_pack(W, Wq, S), qp_bytes),
                              ("fake_quant", lambda i: w4.w4_fake_quant(W, Wf), fq_bytes),
                              ("dequant", lambda i: w4.w4_dequant(Wq, S, Wf), qp_bytes),
                              ("repack", lambda i: w4.w4_repack(Wq, Wt), rp_bytes),
-                             ("restore", lambda i: w4.w4_restore(Wt, N, K, Wr), rp_bytes)):
+                             ("restore", lambda i: w4.w4_restore(Wt, N, K, Wr), rp_bytes),
+                             ("repack_scales", lambda i: w4.w4_repack_groups(S, St), rg_bytes)):
         timer.settle(fn, SETTLE_MS / 3)
         t = timer.run(fn, iters) / iters
         gbs = nbytes / (t * 1e-3) / 1e9
@@ -684,7 +690,8 @@ def main():
             "config": {"workload": "decode W4A16 GEMV sweep: packed int4 W[12288x4096] group 32 "
                                    "bf16 scales, X[M,4096] bf16, M in {1,8,16,32}",
                        "rotating_weight_copies": ROTATE,
-                       "code_layout": "kernel order (w4_repack, converted once at load)"}}
+                       "code_layout": "kernel order (w4_repack and w4_repack_groups, "
+                                      "converted once at load)"}}
     if dec is not None:
         value = dec["step_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
         per_launch_bytes = dec["step_bytes"] / len(DECODE_MS)
@@ -696,7 +703,7 @@ def main():
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(achieved / PEAK_HBM_GBS, 4),
                             "traffic": traffic,
-                            "kernel": "k_decode16 / k_decode32 on kernel-order codes",
+                            "kernel": "k_decode16 / k_decode32 on kernel-order codes and scales",
                             "algorithmic_bytes_per_launch": per_launch_bytes,
                             "avg_launch_us": round(per_launch_us, 3)}
     else:

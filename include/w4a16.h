@@ -209,10 +209,34 @@ int w4_restore(const int32_t* Wt, int64_t E, int64_t N, int64_t K, int32_t* Wq,
                void* stream);
 
 /*
+ * w4_repacked_group_elems -- elements of one [N, K/32] per-group array
+ *   (scales or zero points) in kernel order: ceil(N/16) * ceil(K/256) * 128.
+ *   -1 on invalid sizes.
+ *
+ * w4_repack_groups -- per-group values A [E, N, K/32] (elem_bytes = 2: bf16
+ * scales; 1: uint8 zero points) -> kernel order At
+ * [E * w4_repacked_group_elems(N, K)]: per matrix, ceil(N/16) x ceil(K/256)
+ * blocks of 128 elements, block (r, c) at element 128 (r ceil(K/256) + c),
+ * element 8 i + j of a block = row 16 r + i, group 8 c + j; elements past N
+ * or K/32 are written as zero.  The products then read a wave's eight
+ * values of 16 consecutive rows as one contiguous piece.
+ * w4_restore_groups -- the inverse (padding ignored).  Pure permutations:
+ * w4_restore_groups(w4_repack_groups(A)) equals A bit for bit.  Buffers
+ * aligned to elem_bytes, not overlapping; K % 32 == 0; elem_bytes other
+ * than 1 or 2 is unsupported; E, N or K == 0 is a no-op.
+ */
+int64_t w4_repacked_group_elems(int64_t N, int64_t K);
+int w4_repack_groups(const void* A, int32_t elem_bytes, int64_t E, int64_t N, int64_t K, void* At,
+                     void* stream);
+int w4_restore_groups(const void* At, int32_t elem_bytes, int64_t E, int64_t N, int64_t K, void* A,
+                      void* stream);
+
+/*
  * w4a16_gemm_tiled -- w4a16_gemm (Z == NULL) or w4a16_gemm_asym (Z given)
- * with the codes in kernel order (Wt from w4_repack, E = 1).  Same
- * definition, arguments, limits and dispatch; the results equal those of
- * the canonical-layout call bit for bit.
+ * with the codes, the scales and the zero points in kernel order (Wt from
+ * w4_repack, St and Zt from w4_repack_groups, E = 1).  Same definition,
+ * arguments, limits and dispatch; the results equal those of the
+ * canonical-layout call bit for bit.
  */
 int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
                      const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
@@ -220,11 +244,11 @@ int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
 
 /*
  * w4a16_moe_gemm_tiled, w4a16_moe_gemm_swiglu_tiled -- the grouped
- * products (symmetric with Z == NULL, zero-point with Z [E, N, K/32]) with
- * every expert's codes in kernel order (Wt from w4_repack with E experts).
- * Definitions, arguments and limits as w4a16_moe_gemm(_asym) and
- * w4a16_moe_gemm_swiglu(_asym); results equal the canonical-layout calls
- * bit for bit.
+ * products (symmetric with Z == NULL, zero-point with Z given) with every
+ * expert's codes, scales and zero points in kernel order (Wt from w4_repack,
+ * St and Zt from w4_repack_groups, E experts each).  Definitions, arguments
+ * and limits as w4a16_moe_gemm(_asym) and w4a16_moe_gemm_swiglu(_asym);
+ * results equal the canonical-layout calls bit for bit.
  */
 int w4a16_moe_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
                          const uint8_t* Z, const int32_t* sorted_token_ids,

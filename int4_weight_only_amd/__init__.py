@@ -14,7 +14,10 @@ Layouts (all row-major, contiguous, on one GPU):
   Z       uint8 [N, K/32]     zero points (the asymmetric variants)
   experts stacked on a leading axis: Wq [E, N, K/8], S [E, N, K/32], Z [E, N, K/32]
   Wt      int32 [E, w4_repacked_words(N, K)]  codes in the kernel-order layout
-          (w4_repack / w4_restore); the *_tiled products read it
+          (w4_repack / w4_restore)
+  St, Zt  bf16 / uint8 [E, w4_repacked_group_elems(N, K)]  scales and zero
+          points in kernel order (w4_repack_groups / w4_restore_groups);
+          the *_tiled products read Wt, St and Zt and take N explicitly
 """
 
 import torch
@@ -28,7 +31,8 @@ __all__ = [
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
-    "w4_repacked_words", "w4_repack", "w4_restore", "w4a16_gemm_tiled",
+    "w4_repacked_words", "w4_repack", "w4_restore", "w4_repacked_group_elems",
+    "w4_repack_groups", "w4_restore_groups", "w4a16_gemm_tiled",
     "w4a16_moe_gemm_tiled", "w4a16_moe_gemm_swiglu_tiled",
 ]
 
@@ -505,21 +509,88 @@ def w4_restore(Wt, N, K, out=None):
     return out
 
 
-def w4a16_gemm_tiled(X, Wt, S, Z=None, out=None):
-    """w4a16_gemm (Z None) / w4a16_gemm_asym (Z uint8 [N, K/32]) on
-    kernel-order codes Wt [1, w4_repacked_words(N, K)]; N and K from S."""
+def w4_repacked_group_elems(N, K):
+    """Elements of one [N, K/32] per-group array in the kernel-order layout."""
+    n = int(_lib.load().w4_repacked_group_elems(N, K))
+    if n < 0:
+        raise ValueError("invalid N or K")
+    return n
+
+
+_GROUP_DTYPES = {torch.bfloat16: 2, torch.uint8: 1}
+
+
+def w4_repack_groups(A, out=None):
+    """Per-group scales (bf16) or zero points (uint8) A [N, K/32] (or
+    [E, N, K/32]) -> kernel order [E, w4_repacked_group_elems(N, K)]."""
+    if not isinstance(A, torch.Tensor) or A.dtype not in _GROUP_DTYPES:
+        raise TypeError("A must be a bf16 or uint8 tensor")
+    _need(A, "A", A.dtype)
+    if A.dim() not in (2, 3):
+        raise ValueError("A must be [N, K/32] or [E, N, K/32]")
+    E, N, G = (1,) + tuple(A.shape) if A.dim() == 2 else tuple(A.shape)
+    K = 32 * G
+    elems = w4_repacked_group_elems(N, K)
+    if out is None:
+        out = torch.empty((E, elems), dtype=A.dtype, device=A.device)
+    _need(out, "out", A.dtype)
+    if out.numel() != E * elems:
+        raise ValueError(f"out needs {E * elems} elements")
+    lib = _lib.load()
+    _lib.check("w4_repack_groups", lib.w4_repack_groups(
+        _ptr(A), _GROUP_DTYPES[A.dtype], E, N, K, _ptr(out), _stream(A)))
+    return out
+
+
+def w4_restore_groups(At, N, K, out=None):
+    """Kernel-order per-group values At [E, elems] -> canonical [E, N, K/32]
+    (the inverse of w4_repack_groups; [N, K/32] when E = 1 and ``out`` is not
+    given)."""
+    if not isinstance(At, torch.Tensor) or At.dtype not in _GROUP_DTYPES:
+        raise TypeError("At must be a bf16 or uint8 tensor")
+    _need(At, "At", At.dtype)
+    elems = w4_repacked_group_elems(N, K)
+    if At.numel() % max(elems, 1) != 0:
+        raise ValueError("At size is not a whole number of matrices")
+    E = At.numel() // max(elems, 1)
+    if out is None:
+        shape = (N, K // 32) if E == 1 else (E, N, K // 32)
+        out = torch.empty(shape, dtype=At.dtype, device=At.device)
+    _need(out, "out", At.dtype)
+    if out.numel() != E * N * (K // 32):
+        raise ValueError("out size does not match [E, N, K/32]")
+    lib = _lib.load()
+    _lib.check("w4_restore_groups", lib.w4_restore_groups(
+        _ptr(At), _GROUP_DTYPES[At.dtype], E, N, K, _ptr(out), _stream(At)))
+    return out
+
+
+def _tiled_experts(X, Wt, St, Z, N, E=None):
+    """E (from Wt unless given) and K of kernel-order operands, checking
+    their sizes."""
     _need(X, "X", torch.bfloat16, 2)
     _need(Wt, "Wt", torch.int32)
-    _need(S, "S", torch.bfloat16, 2)
-    M, K = X.shape
-    N = S.shape[0]
-    if S.shape[1] * 32 != K or Wt.numel() != w4_repacked_words(N, K):
+    _need(St, "St", torch.bfloat16)
+    K = X.shape[1]
+    words, elems = w4_repacked_words(N, K), w4_repacked_group_elems(N, K)
+    if E is None:
+        E = Wt.numel() // max(words, 1)
+    if E < 1 or Wt.numel() != E * words or St.numel() != E * elems:
         raise ValueError(f"shape mismatch: X {tuple(X.shape)} Wt {tuple(Wt.shape)} "
-                         f"S {tuple(S.shape)}")
+                         f"St {tuple(St.shape)} for N={N}")
     if Z is not None:
-        _need(Z, "Z", torch.uint8, 2)
-        if tuple(Z.shape) != tuple(S.shape):
-            raise ValueError("Z must be [N, K/32]")
+        _need(Z, "Z", torch.uint8)
+        if Z.numel() != E * elems:
+            raise ValueError("Z must hold w4_repacked_group_elems(N, K) values per matrix")
+    return E, K
+
+
+def w4a16_gemm_tiled(X, Wt, St, N, Z=None, out=None):
+    """w4a16_gemm (Z None) / w4a16_gemm_asym on kernel-order operands: codes
+    Wt [1, w4_repacked_words(N, K)], scales St and zero points Z
+    [1, w4_repacked_group_elems(N, K)]; K from X."""
+    _, K = _tiled_experts(X, Wt, St, Z, N, E=1)
+    M = X.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     _need(out, "out", torch.bfloat16)
@@ -527,32 +598,23 @@ def w4a16_gemm_tiled(X, Wt, S, Z=None, out=None):
         raise ValueError("out size does not match [M, N]")
     lib = _lib.load()
     _lib.check("w4a16_gemm_tiled", lib.w4a16_gemm_tiled(
-        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(out), M, N, K, _stream(X)))
+        _ptr(X), _ptr(Wt), _ptr(St), _ptr(Z), _ptr(out), M, N, K, _stream(X)))
     return out
 
 
-def _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div):
-    _need(X, "X", torch.bfloat16, 2)
-    _need(Wt, "Wt", torch.int32)
-    _need(S, "S", torch.bfloat16, 3)
-    E, N, G = S.shape
-    K = 32 * G
-    if X.shape[1] != K or Wt.numel() != E * w4_repacked_words(N, K):
-        raise ValueError("shape mismatch between X, Wt and S")
-    if Z is not None:
-        _need(Z, "Z", torch.uint8, 3)
-        if tuple(Z.shape) != (E, N, G):
-            raise ValueError("Z must be [E, N, K/32]")
+def _moe_tiled_args(X, Wt, St, Z, N, T, k, x_row_div):
+    E, K = _tiled_experts(X, Wt, St, Z, N)
     if X.shape[0] != (T * k) // x_row_div:
         raise ValueError("X must have T*k / x_row_div rows")
-    return E, N, K
+    return E, K
 
 
-def w4a16_moe_gemm_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+def w4a16_moe_gemm_tiled(X, Wt, St, N, sorted_token_ids, expert_ids, num_tokens_post_padded,
                          T, k, B, x_row_div, Z=None, topk_weights=None, out=None):
     """``w4a16_moe_gemm`` (Z None) / ``w4a16_moe_gemm_asym`` on kernel-order
-    expert codes Wt [E, w4_repacked_words(N, K)]; E, N, K from S."""
-    E, N, K = _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div)
+    expert operands: Wt [E, w4_repacked_words(N, K)], St and Z
+    [E, w4_repacked_group_elems(N, K)]; E from Wt, K from X."""
+    E, K = _moe_tiled_args(X, Wt, St, Z, N, T, k, x_row_div)
     for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
                  (num_tokens_post_padded, "num_tokens_post_padded")):
         _need(t, n, torch.int32)
@@ -567,17 +629,17 @@ def w4a16_moe_gemm_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_tokens_post
         raise ValueError("out must be [T*k, N]")
     lib = _lib.load()
     _lib.check("w4a16_moe_gemm_tiled", lib.w4a16_moe_gemm_tiled(
-        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(X), _ptr(Wt), _ptr(St), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, k, E, N, K, B,
         x_row_div, _stream(X)))
     return out
 
 
-def w4a16_moe_gemm_swiglu_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                                T, k, B, x_row_div, Z=None, out=None):
+def w4a16_moe_gemm_swiglu_tiled(X, Wt, St, N, sorted_token_ids, expert_ids,
+                                num_tokens_post_padded, T, k, B, x_row_div, Z=None, out=None):
     """``w4a16_moe_gemm_swiglu`` (Z None) / ``..._asym`` on kernel-order
-    expert codes Wt [E, w4_repacked_words(2I, K)]."""
-    E, N, K = _moe_tiled_args(X, Wt, S, Z, T, k, x_row_div)
+    expert operands of N = 2I rows (Wt, St, Z as ``w4a16_moe_gemm_tiled``)."""
+    E, K = _moe_tiled_args(X, Wt, St, Z, N, T, k, x_row_div)
     for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
                  (num_tokens_post_padded, "num_tokens_post_padded")):
         _need(t, n, torch.int32)
@@ -591,6 +653,6 @@ def w4a16_moe_gemm_swiglu_tiled(X, Wt, S, sorted_token_ids, expert_ids, num_toke
         raise ValueError("out must be [T*k, I]")
     lib = _lib.load()
     _lib.check("w4a16_moe_gemm_swiglu_tiled", lib.w4a16_moe_gemm_swiglu_tiled(
-        _ptr(X), _ptr(Wt), _ptr(S), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(X), _ptr(Wt), _ptr(St), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
     return out

@@ -205,6 +205,41 @@ int w4_restore(const int32_t* Wt, int64_t E, int64_t N, int64_t K, int32_t* Wq, 
   return relayout_checked(Wt, Wq, E, N, K, true, stream);
 }
 
+int64_t w4_repacked_group_elems(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K % 32 != 0 || N > kMaxI32 || K > kMaxI32) return -1;
+  return w4::tiled_group_elems(N, K);
+}
+
+namespace {
+int relayout_groups_checked(const void* src, void* dst, int32_t elem_bytes, int64_t E, int64_t N,
+                            int64_t K, bool restore, void* stream) {
+  if (E < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2) return W4_ERR_UNSUPPORTED;
+  if (E == 0 || N == 0 || K == 0) return W4_OK;
+  if (N > kMaxI32 || K > kMaxI32 || E * w4::tiled_group_elems(N, K) > ((int64_t)1 << 40))
+    return W4_ERR_UNSUPPORTED;
+  if (!src || !dst) return W4_ERR_NULL;
+  if (!aligned(src, elem_bytes) || !aligned(dst, elem_bytes)) return W4_ERR_MISALIGNED;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  const int64_t tiled = E * w4::tiled_group_elems(N, K), canon = E * N * (K / 32);
+  const uintptr_t la = (uintptr_t)(restore ? tiled : canon) * elem_bytes;
+  const uintptr_t lb = (uintptr_t)(restore ? canon : tiled) * elem_bytes;
+  if (a < b + lb && b < a + la) return W4_ERR_UNSUPPORTED;
+  return hip_status(
+      w4::launch_relayout_groups(src, dst, elem_bytes, E, N, K, restore, as_stream(stream)));
+}
+}  // namespace
+
+int w4_repack_groups(const void* A, int32_t elem_bytes, int64_t E, int64_t N, int64_t K, void* At,
+                     void* stream) {
+  return relayout_groups_checked(A, At, elem_bytes, E, N, K, false, stream);
+}
+
+int w4_restore_groups(const void* At, int32_t elem_bytes, int64_t E, int64_t N, int64_t K, void* A,
+                      void* stream) {
+  return relayout_groups_checked(At, A, elem_bytes, E, N, K, true, stream);
+}
+
 int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S, const uint8_t* Z,
                      uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return W4_ERR_SHAPE;

@@ -173,6 +173,10 @@ hipError_t launch_zero_bf16(uint16_t* Y, int64_t n, hipStream_t st);
 int64_t tiled_words(int64_t N, int64_t K);
 hipError_t launch_relayout(const int32_t* src, int32_t* dst, int64_t E, int64_t N, int64_t K,
                            bool restore, hipStream_t st);
+// kernel-order layout of per-group values (scales: 2 bytes, zero points: 1)
+int64_t tiled_group_elems(int64_t N, int64_t K);
+hipError_t launch_relayout_groups(const void* src, void* dst, int elem_bytes, int64_t E,
+                                  int64_t N, int64_t K, bool restore, hipStream_t st);
 // QAT input gradient: transposed dequant W'^T [K, N], and a bf16 NT GEMM
 hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, uint16_t* WT,
                             int64_t N, int64_t K, hipStream_t st);

@@ -26,8 +26,11 @@
 // order in which the lanes of one load read them, so each load instruction
 // reads 1 KB of contiguous memory and a run of steps is one contiguous
 // stream (the weight-layout conversion the RL write-up's section 4 applies
-// before its inference kernel).  Nothing else changes: scales and zero
-// points keep their [N, K/32] layout, and the arithmetic is identical.
+// before its inference kernel).  Scales and zero points come in kernel
+// order too (w4_repack_groups): 16-row x 8-group blocks of 128 values, so
+// the 8 values of a window that lanes n .. n + 15 load are 256 contiguous
+// bytes (128 for zero points) instead of 16 pieces one row apart.  The
+// arithmetic is identical.
 //
 // Pipeline: activations go straight from HBM into LDS (16-byte
 // buffer_load ... lds, four stages: three steps ahead, no staging
@@ -284,16 +287,21 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   // tiled: each expert holds ceil(N/32) x ceil(K/64) blocks of 1 KB
   const int64_t tl_words = (int64_t)((N + 31) >> 5) * ((K + kStepK - 1) / kStepK) * 256;
   const uint32_t* Wbase = Wq + (int64_t)expert * (TL ? tl_words : (int64_t)N * kw);
-  const uint16_t* Sbase = S + (int64_t)expert * N * G;
+  // kernel-order scales and zero points: each expert holds ceil(N/16) x
+  // ceil(G/8) blocks of 128 values (value 8 i + j of block (r, c) = row
+  // 16 r + i, group 8 c + j)
+  const uint32_t gblk = (uint32_t)(G + 7) >> 3;
+  const int64_t grp_elems = TL ? (int64_t)((N + 15) >> 4) * gblk * 128 : (int64_t)N * G;
+  const uint16_t* Sbase = S + (int64_t)expert * grp_elems;
   const int nsteps = (K + kStepK - 1) / kStepK;
   const int nstepsp = (nsteps + kU - 1) / kU * kU;  // padded to the unroll; pad steps load zeros, skip MFMAs
   const int x_rows = MOE ? n_pairs / x_row_div : M;
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)x_rows * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t wr =
       rsrc(Wbase, TL ? (uint32_t)tl_words * 4u : (uint32_t)N * (uint32_t)kw * 4u);
-  const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)N * (uint32_t)G * 2u);
-  const uint8_t* Zbase = ZP ? Z + (int64_t)expert * N * G : nullptr;
-  const __amdgpu_buffer_rsrc_t zr = rsrc(Zbase, ZP ? (uint32_t)N * (uint32_t)G : 0u);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)grp_elems * 2u);
+  const uint8_t* Zbase = ZP ? Z + (int64_t)expert * grp_elems : nullptr;
+  const __amdgpu_buffer_rsrc_t zr = rsrc(Zbase, ZP ? (uint32_t)grp_elems : 0u);
 
   {
     // ---- row tables (thread r < BM fills row r)
@@ -378,7 +386,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
-        if constexpr (SA) {
+        if constexpr (TL) {
+          // rows past N fall in the zero padding or past the expert's blocks
+          const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (g0 < G) ? e * 2u : kOOB, 0, 0);
+        } else if constexpr (SA) {
           const uint32_t soff = (g0 < G) ? (n * (uint32_t)G + (uint32_t)g0) * 2u : kOOB;
           raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, soff, 0, 0);
         } else {
@@ -402,7 +414,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
-        if constexpr (SA) {
+        if constexpr (TL) {
+          const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, (g0 < G) ? e : kOOB, 0, 0);
+        } else if constexpr (SA) {
           const uint32_t zoff = (g0 < G) ? n * (uint32_t)G + (uint32_t)g0 : kOOB;
           raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, zoff, 0, 0);
         } else {

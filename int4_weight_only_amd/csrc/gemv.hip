@@ -39,7 +39,9 @@
 // Kernel-order codes (TL, written by w4_repack): the 16 bytes of group g of
 // row n sit in the 1 KB block (n / 32, g / 2) at unit 32 (g % 2) + n % 32,
 // so one load instruction reads four 256-byte runs instead of 16 rows'
-// 64-byte pieces; the arithmetic is unchanged.
+// 64-byte pieces.  Its scales and zero points then come in kernel order
+// too (w4_repack_groups): a tile's 8 values of a wave's slice are one
+// 256-byte piece (128 for zero points); the arithmetic is unchanged.
 //
 // Zero-point weights (ZP; "Quantization basics: from FP32 to INT4" §2.1 and
 // §2.3, w' = bf16((q - z) s) with unsigned q): the same step with the
@@ -202,6 +204,24 @@ __device__ __forceinline__ u32x2 load_zp8(__amdgpu_buffer_rsrc_t zr, uint32_t sr
   }
 }
 
+// Per-group values (scales, zero points) of a workgroup's rows [n0, n0 +
+// rows), n0 a multiple of 16: the first element and the element count.
+// Canonical: rows of G values.  Kernel order (w4_repack_groups): the
+// ceil(G / 8) blocks of 128 values of each of the workgroup's 16-row
+// blocks; value 8 i + j of block (r, c) is row 16 r + i, group 8 c + j.
+template <bool TL>
+__device__ __forceinline__ void group_span(int n0, int rows, int G, size_t& first,
+                                           uint32_t& count) {
+  if constexpr (TL) {
+    const uint32_t gblk = (uint32_t)(G + 7) >> 3;
+    first = (size_t)(n0 >> 4) * gblk * 128u;
+    count = (((uint32_t)rows + 15u) >> 4) * gblk * 128u;
+  } else {
+    first = (size_t)n0 * G;
+    count = (uint32_t)rows * (uint32_t)G;
+  }
+}
+
 // Copies of v with all four 16-lane rows replaced by row 0, 1, 2, 3.
 __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
   auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // [r0 r1 r0 r1], [r2 r3 r2 r3]
@@ -218,17 +238,28 @@ __device__ __forceinline__ void broadcast_rows(uint32_t v, uint32_t out[4]) {
 // bytes of zero points) and permlane swaps broadcast them, so every lane
 // holds its row's 8 scales of every tile; lane (n16, kq) then takes group
 // 4 cc + kq of chunk cc (a dword select and a byte permute).
-template <bool SALIGNED, int T, bool ZP>
+template <int KM, int T, bool ZP, bool TL>
 struct PassScales {
+  static constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
   uint32_t sct[T][4];      // [tile][dword]: 8 bf16 scales
   uint32_t zc[kCPW][T];    // [chunk][tile]: the 4 zero points of the chunk's groups
   u32x4 sraw;
   u32x2 zraw;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t zr,
                                        int n16, int kq, int g0, int G) {
-    sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
     zraw = u32x2{0u, 0u};
-    if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    if constexpr (TL) {
+      // one piece of block (tile kq, g0 / 8); g0 is a multiple of 8 and the
+      // blocks are zero-padded, so no clamp (tiles past the rows read zero)
+      const uint32_t e =
+          ((uint32_t)kq * ((uint32_t)(G + 7) >> 3) + ((uint32_t)g0 >> 3)) * 128u + 8u * n16;
+      const bool in = FULL || g0 < G;
+      sraw = __builtin_amdgcn_raw_buffer_load_b128(sr, in ? e * 2u : kOOB, 0, 0);
+      if constexpr (ZP) zraw = __builtin_amdgcn_raw_buffer_load_b64(zr, in ? e : kOOB, 0, 0);
+    } else {
+      sraw = load_scale8<SALIGNED>(sr, (uint32_t)(kq * 16 + n16), g0, G);
+      if constexpr (ZP) zraw = load_zp8<SALIGNED>(zr, (uint32_t)(kq * 16 + n16), g0, G);
+    }
   }
   __device__ __forceinline__ void spread() {
     const uint32_t rw[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 4, "decode shape");
-  constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
+  constexpr bool FULL = KM == 2;
   constexpr int PSTR = 20;                         // LDS row stride (floats)
   constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
   constexpr int XREG = XL ? 2048 : 0;              // floats: the wave's 16 x 256 activations
@@ -319,9 +350,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const CodeRows<TL> wr(Wq, n0, rows, K);
-  const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
-  const __amdgpu_buffer_rsrc_t zr =
-      rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
+  size_t gfirst;
+  uint32_t gcount;
+  group_span<TL>(n0, rows, G, gfirst, gcount);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(S + gfirst, gcount * 2u);
+  const __amdgpu_buffer_rsrc_t zr = rsrc(ZP ? Z + gfirst : nullptr, ZP ? gcount : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
   // byte permute selector: bytes 2 kq + 1, 2 kq of the 8-byte value (low
   // dword = bytes 0..3) to the high half, zero bytes (0x0C) below
@@ -330,7 +363,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
     // ---- scales (and zero points) first
-    PassScales<SALIGNED, T, ZP> sc;
+    PassScales<KM, T, ZP, TL> sc;
     sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- activations (L2 hits after the first CU's request)
     u32x4 xop[kCPW][4];
@@ -429,7 +462,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
                                                           uint16_t* __restrict__ Y, int M, int N,
                                                           int K) {
   static_assert(T >= 1 && T <= 3, "decode shape");
-  constexpr bool SALIGNED = KM >= 1, FULL = KM == 2;
+  constexpr bool FULL = KM == 2;
   constexpr int PSTR = 36;                         // LDS row stride (floats): 32 rows + pad
   constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
   constexpr int XREG = kCPW * 4 * 256;             // floats: 8 x 1 KB of half-1 activations
@@ -449,9 +482,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
 
   const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const CodeRows<TL> wr(Wq, n0, rows, K);
-  const __amdgpu_buffer_rsrc_t sr = rsrc(S + (size_t)n0 * G, (uint32_t)rows * (uint32_t)G * 2u);
-  const __amdgpu_buffer_rsrc_t zr =
-      rsrc(ZP ? Z + (size_t)n0 * G : nullptr, ZP ? (uint32_t)rows * (uint32_t)G : 0u);
+  size_t gfirst;
+  uint32_t gcount;
+  group_span<TL>(n0, rows, G, gfirst, gcount);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(S + gfirst, gcount * 2u);
+  const __amdgpu_buffer_rsrc_t zr = rsrc(ZP ? Z + gfirst : nullptr, ZP ? gcount : 0u);
   const int npass = (K + kPassK - 1) / kPassK;
   // byte permute selector: bytes 2 kq + 1, 2 kq of the 8-byte value (low
   // dword = bytes 0..3) to the high half, zero bytes (0x0C) below
@@ -468,7 +503,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       return (FULL || g < G) ? ((uint32_t)row * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
     };
     // ---- scales (and zero points) first
-    PassScales<SALIGNED, T, ZP> sc;
+    PassScales<KM, T, ZP, TL> sc;
     sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- half 0's activations into registers, half 1's into this wave's
     // LDS region in whole lines

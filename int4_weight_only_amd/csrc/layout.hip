@@ -14,6 +14,14 @@
 //
 // One lane per 16-byte unit of the kernel-order buffer: a 64-lane wave
 // writes one whole block (1 KB, coalesced) and reads 32 rows x 32 bytes.
+//
+// Per-group values (bf16 scales, uint8 zero points; canonical [N, K/32]):
+// per matrix, ceil(N/16) x ceil(G/8) blocks of 128 elements (G = K/32),
+// block (r, c) at element 128 (r ceil(G/8) + c), and element 8 i + j of a
+// block is row 16 r + i, group 8 c + j.  Elements naming a row past N or a
+// group past G are zero.  The products read a wave's eight values of 16
+// consecutive rows as one contiguous piece instead of 16 pieces one row
+// apart.  One thread per 8-element row piece of a block (16 or 8 bytes).
 #include "common.h"
 
 namespace w4 {
@@ -43,6 +51,64 @@ __global__ __launch_bounds__(256) void k_relayout(const u32x4* __restrict__ src,
 }
 
 int64_t tiled_words(int64_t N, int64_t K) { return ((N + 31) / 32) * ((K + 63) / 64) * 256; }
+
+int64_t tiled_group_elems(int64_t N, int64_t K) {
+  return ((N + 15) / 16) * ((K / 32 + 7) / 8) * 128;
+}
+
+template <bool RESTORE, typename V>
+__global__ __launch_bounds__(256) void k_relayout_groups(const V* __restrict__ src,
+                                                         V* __restrict__ dst, int64_t N,
+                                                         int64_t G, int64_t gb, int64_t pieces,
+                                                         int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t e = i / pieces;           // matrix
+    const int64_t p = i - e * pieces;       // row piece inside the matrix's blocks
+    const int64_t blk = p >> 4;
+    const int64_t r = blk / gb, c = blk - r * gb;
+    const int64_t n = 16 * r + (p & 15);
+    const V* s = src;
+    V* d = dst;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t g = 8 * c + j;
+      const bool valid = n < N && g < G;
+      const int64_t canon = (e * N + n) * G + g;
+      const int64_t tiled = 8 * i + j;
+      if constexpr (RESTORE) {
+        if (valid) d[canon] = s[tiled];
+      } else {
+        d[tiled] = valid ? s[canon] : (V)0;
+      }
+    }
+  }
+}
+
+hipError_t launch_relayout_groups(const void* src, void* dst, int elem_bytes, int64_t E,
+                                  int64_t N, int64_t K, bool restore, hipStream_t st) {
+  const int64_t pieces = tiled_group_elems(N, K) / 8;
+  const int64_t total = E * pieces;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const int64_t G = K / 32, gb = (G + 7) / 8;
+  if (elem_bytes == 2) {
+    if (restore)
+      hipLaunchKernelGGL((k_relayout_groups<true, uint16_t>), dim3((unsigned)blocks), dim3(256),
+                         0, st, (const uint16_t*)src, (uint16_t*)dst, N, G, gb, pieces, total);
+    else
+      hipLaunchKernelGGL((k_relayout_groups<false, uint16_t>), dim3((unsigned)blocks), dim3(256),
+                         0, st, (const uint16_t*)src, (uint16_t*)dst, N, G, gb, pieces, total);
+  } else {
+    if (restore)
+      hipLaunchKernelGGL((k_relayout_groups<true, uint8_t>), dim3((unsigned)blocks), dim3(256),
+                         0, st, (const uint8_t*)src, (uint8_t*)dst, N, G, gb, pieces, total);
+    else
+      hipLaunchKernelGGL((k_relayout_groups<false, uint8_t>), dim3((unsigned)blocks), dim3(256),
+                         0, st, (const uint8_t*)src, (uint8_t*)dst, N, G, gb, pieces, total);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_relayout(const int32_t* src, int32_t* dst, int64_t E, int64_t N, int64_t K,
                            bool restore, hipStream_t st) {

@@ -16,8 +16,8 @@ the combine (weights applied after the down projection) are readings: the
 pages name the gate_up / down pair but give no formula.  Experts quantized
 with zero points ("Quantization basics: from FP32 to INT4" §2.3) run the
 ``_asym`` forms of the two grouped products; experts converted to the
-kernel-order code layout (``repack_experts``, §4's weight-layout conversion)
-run the ``_tiled`` forms.
+kernel-order layouts (``repack_experts``, §4's weight-layout conversion,
+codes and per-group values alike) run the ``_tiled`` forms.
 """
 
 from dataclasses import dataclass
@@ -26,7 +26,7 @@ import torch
 
 from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
                w4_pick_block_size, w4_quantize_pack, w4_quantize_pack_asym, w4_repack,
-               w4_silu_mul, w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
+               w4_repack_groups, w4_silu_mul, w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
                w4a16_moe_gemm_swiglu_asym, w4a16_moe_gemm_swiglu_tiled, w4a16_moe_gemm_tiled)
 
 
@@ -34,38 +34,56 @@ from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe
 class ExpertWeights:
     """Stacked packed weights of E experts: Wq int32 [E, N, K/8], S bf16 [E, N, K/32],
     and for zero-point experts Z uint8 [E, N, K/32] (None: symmetric codes).
-    Wt: the same codes in the kernel-order layout ([E, w4_repacked_words(N, K)],
-    from ``repack_experts``); when present the products read it and Wq may be
-    None."""
+    Wt, St, Zt: the same codes, scales and zero points in the kernel-order
+    layouts ([E, w4_repacked_words(N, K)], [E, w4_repacked_group_elems(N, K)],
+    from ``repack_experts``); when Wt is present the products read Wt, St and
+    Zt, and the canonical arrays may be None.  dims = (E, N, K), taken from S
+    when not given."""
     Wq: torch.Tensor
     S: torch.Tensor
     Z: torch.Tensor = None
     Wt: torch.Tensor = None
+    St: torch.Tensor = None
+    Zt: torch.Tensor = None
+    dims: tuple = None
+
+    def __post_init__(self):
+        if self.dims is None:
+            E, N, G = self.S.shape
+            self.dims = (E, N, 32 * G)
 
     @property
     def E(self):
-        return self.S.shape[0]
+        return self.dims[0]
 
     @property
     def N(self):
-        return self.S.shape[1]
+        return self.dims[1]
 
     @property
     def K(self):
-        return self.S.shape[2] * 32
+        return self.dims[2]
 
     def nbytes(self):
-        z = 0 if self.Z is None else self.Z.numel()
-        codes = self.Wt if self.Wt is not None else self.Wq
-        return codes.numel() * 4 + self.S.numel() * 2 + z
+        """Bytes of the arrays the products read."""
+        if self.Wt is not None:
+            arrays = (self.Wt, self.St, self.Zt)
+        else:
+            arrays = (self.Wq, self.S, self.Z)
+        return sum(a.numel() * a.element_size() for a in arrays if a is not None)
 
 
 def repack_experts(w, keep_canonical=False):
-    """The experts with their codes converted to the kernel-order layout
-    (``w4_repack``); the canonical codes are dropped unless asked for
-    (``w4_restore`` brings them back)."""
+    """The experts with codes, scales and zero points converted to the
+    kernel-order layouts (``w4_repack``, ``w4_repack_groups``); the canonical
+    arrays are dropped unless asked for (``w4_restore`` and
+    ``w4_restore_groups`` bring them back)."""
     Wt = w4_repack(w.Wq)
-    return ExpertWeights(w.Wq if keep_canonical else None, w.S, w.Z, Wt)
+    St = w4_repack_groups(w.S)
+    Zt = w4_repack_groups(w.Z) if w.Z is not None else None
+    if keep_canonical:
+        return ExpertWeights(w.Wq, w.S, w.Z, Wt, St, Zt, w.dims)
+    return ExpertWeights(None, None, None, Wt, St, Zt, w.dims)
 
 
 def quantize_experts(E, N, K, source, device, asym=False):
@@ -93,8 +111,8 @@ def grouped_gemm(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row_div,
     """``w4a16_moe_gemm``, its zero-point form or their kernel-order forms,
     as the experts ``w`` need."""
     if w.Wt is not None:
-        return w4a16_moe_gemm_tiled(X, w.Wt, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
-                                    x_row_div, Z=w.Z, topk_weights=topk_weights, out=out)
+        return w4a16_moe_gemm_tiled(X, w.Wt, w.St, w.N, sorted_token_ids, expert_ids, ntpp, T, k,
+                                    B, x_row_div, Z=w.Zt, topk_weights=topk_weights, out=out)
     if w.Z is None:
         return w4a16_moe_gemm(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
                               x_row_div, topk_weights, out)
@@ -106,8 +124,8 @@ def grouped_gemm_swiglu(X, w, sorted_token_ids, expert_ids, ntpp, T, k, B, x_row
     """``w4a16_moe_gemm_swiglu``, its zero-point form or their kernel-order
     forms, as the experts ``w`` need."""
     if w.Wt is not None:
-        return w4a16_moe_gemm_swiglu_tiled(X, w.Wt, w.S, sorted_token_ids, expert_ids, ntpp, T,
-                                           k, B, x_row_div, Z=w.Z, out=out)
+        return w4a16_moe_gemm_swiglu_tiled(X, w.Wt, w.St, w.N, sorted_token_ids, expert_ids, ntpp,
+                                           T, k, B, x_row_div, Z=w.Zt, out=out)
     if w.Z is None:
         return w4a16_moe_gemm_swiglu(X, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, T, k, B,
                                      x_row_div, out)

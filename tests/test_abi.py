@@ -357,6 +357,33 @@ def test_repack_restore_validation(lib):
         assert f(A16, 1, 4, 32, A16, None) == UNSUPPORTED      # overlapping buffers
 
 
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 256), (17, 288), (12288, 4096), (45, 96),
+                                 (3072, 2048), (100, 0)])
+def test_repacked_group_elems_matches_oracle(lib, N, K):
+    from oracle import layout
+    assert lib.w4_repacked_group_elems(N, K) == layout.repacked_group_elems(N, K)
+
+
+def test_repacked_group_elems_bad_args(lib):
+    assert lib.w4_repacked_group_elems(-1, 32) == -1
+    assert lib.w4_repacked_group_elems(4, 33) == -1
+    assert lib.w4_repacked_group_elems(4, -32) == -1
+
+
+def test_repack_restore_groups_validation(lib):
+    for f in (lib.w4_repack_groups, lib.w4_restore_groups):
+        assert f(A16, 2, 1, 4, 33, D16, None) == SHAPE
+        assert f(A16, 2, -1, 4, 32, D16, None) == SHAPE
+        assert f(A16, 4, 1, 4, 32, D16, None) == UNSUPPORTED    # 1- or 2-byte values only
+        assert f(A16, 0, 1, 4, 32, D16, None) == UNSUPPORTED
+        assert f(None, 2, 0, 4, 32, None, None) == OK           # empty: no-op
+        assert f(None, 2, 1, 4, 32, D16, None) == NULL
+        assert f(A16, 1, 1, 4, 32, None, None) == NULL
+        assert f(A1, 2, 1, 4, 32, D16, None) == MISALIGNED
+        assert f(A16, 2, 1, 4, 32, A1, None) == MISALIGNED
+        assert f(A16, 2, 1, 4, 32, A16, None) == UNSUPPORTED    # overlapping buffers
+
+
 def test_gemm_tiled_validation(lib):
     f = lib.w4a16_gemm_tiled
     assert f(A16, A16, A2, None, A4, 4, 8, 33, None) == SHAPE

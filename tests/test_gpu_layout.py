@@ -1,10 +1,11 @@
-"""GPU parity: the kernel-order code layout (w4_repack / w4_restore) and the
-products that read it.
+"""GPU parity: the kernel-order layouts of the codes (w4_repack /
+w4_restore) and of the per-group scales and zero points (w4_repack_groups /
+w4_restore_groups), and the products that read them.
 
-* w4_repack is bit-exact against the oracle's layout (oracle/layout.py),
-  padding included; w4_restore(w4_repack(Wq)) == Wq bit for bit.
+* w4_repack and w4_repack_groups are bit-exact against the oracle's layouts
+  (oracle/layout.py), padding included; restore(repack(x)) == x bit for bit.
 * Every *_tiled product equals the canonical-layout call bit for bit (the
-  same arithmetic in the same order; only the code addresses differ): the
+  same arithmetic in the same order; only the addresses differ): the
   decode kernels (M <= 32), the tiled product, the grouped products of both
   tile shapes with and without the fused SwiGLU, symmetric and zero-point
   codes, ragged N and K (K % 64 == 32 leaves half of the last 64-wide step
@@ -71,6 +72,48 @@ def test_restore_ignores_padding_and_leaves_other_memory():
     assert np.all(o[0] == 0x77) and np.all(o[N + 1] == 0x77)
 
 
+def down_raw(t):
+    """The tensor's bits as numpy (bf16 as int16)."""
+    return down(t.view(torch.int16) if t.dtype == torch.bfloat16 else t)
+
+
+def tiled(S, Z):
+    """Scales and zero points in kernel order."""
+    return w4.w4_repack_groups(S), (None if Z is None else w4.w4_repack_groups(Z))
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 1, 32), (1, 31, 96), (1, 33, 288), (3, 100, 544),
+                                   (2, 64, 4096), (1, 12288, 4096), (128, 3072, 2048),
+                                   (1, 17, 8192)])
+def test_repack_groups_bit_exact_and_restore(E, N, K):
+    say(f"repack groups E={E} N={N} K={K}")
+    _, S, Z = codes(N, K, E + N + K + 1, asym=True, E=E)
+    for A in (S, Z):
+        At = w4.w4_repack_groups(A)
+        assert tuple(At.shape) == (E, layout.repacked_group_elems(N, K))
+        ref = layout.repack_groups(down_raw(A).reshape(E, N, K // 32), K)
+        np.testing.assert_array_equal(down_raw(At), ref)
+        back = w4.w4_restore_groups(At, N, K)
+        np.testing.assert_array_equal(down_raw(back).reshape(E, N, K // 32), down_raw(A))
+
+
+def test_restore_groups_ignores_padding_and_leaves_other_memory():
+    """Padding elements of the kernel-order scales (rows past N, groups past
+    K) are never read back: poison them and restore still gives S."""
+    N, K = 45, 96 + 32 * 8
+    say("restore groups with poisoned padding")
+    _, S, _ = codes(N, K, 4)
+    St = w4.w4_repack_groups(S)
+    _, _, valid = layout._group_map(N, K)
+    St.view(torch.int16).view(-1)[up(np.nonzero(~valid)[0].astype(np.int64))] = 0x5A5A
+    out = torch.full((N + 2, K // 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4_restore_groups(St, N, K, out=out[1:N + 1])
+    o = down_raw(out)
+    np.testing.assert_array_equal(o[1:N + 1], down_raw(S))
+    seven = down_raw(torch.full((1,), 7.0, dtype=torch.bfloat16, device="cuda"))[0]
+    assert np.all(o[0] == seven) and np.all(o[N + 1] == seven)
+
+
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (8, 12288, 4096), (16, 12288, 4096),
                                    (32, 12288, 4096), (17, 45, 544), (5, 300, 96), (33, 300, 96),
@@ -82,7 +125,8 @@ def test_dense_tiled_equals_canonical(asym, M, N, K):
     X = synth.activations(M, K, M + 1).cuda()
     ref = w4.w4a16_gemm_asym(X, Wq, S, Z) if asym else w4.w4a16_gemm(X, Wq, S)
     Wt = w4.w4_repack(Wq)
-    y = w4.w4a16_gemm_tiled(X, Wt, S, Z)
+    St, Zt = tiled(S, Z)
+    y = w4.w4a16_gemm_tiled(X, Wt, St, N, Z=Zt)
     np.testing.assert_array_equal(down_bits(y), down_bits(ref))
 
 
@@ -95,7 +139,8 @@ def test_dense_tiled_against_oracle(M):
     Wq_ref, S_ref = quant.quantize_pack(Wb)
     Wt = w4.w4_repack(up(Wq_ref))
     np.testing.assert_array_equal(down(Wt), layout.repack(Wq_ref))
-    y = down_bits(w4.w4a16_gemm_tiled(up_bits(Xb), Wt, up_bits(S_ref)))
+    St = up_bits(layout.repack_groups(S_ref, K))
+    y = down_bits(w4.w4a16_gemm_tiled(up_bits(Xb), Wt, St, N))
     ok, a, r = gemm.within_tolerance(y, gemm.w4a16_gemm(Xb, Wq_ref, S_ref), ATOL, RTOL)
     assert ok, (a, r)
 
@@ -111,6 +156,7 @@ def test_grouped_tiled_equals_canonical(asym, T, E, k, N, K, B):
     s, e, n = w4.moe_align_block_size(ids, E, B)
     tw = torch.rand(T * k, generator=torch.Generator().manual_seed(5)).cuda()
     Wt = w4.w4_repack(Wq)
+    St, Zt = tiled(S, Z)
     X = synth.activations(T, K, 7).cuda()
     X1 = synth.activations(T * k, K, 8).cuda()
     valid = down(ids).reshape(-1)
@@ -121,8 +167,8 @@ def test_grouped_tiled_equals_canonical(asym, T, E, k, N, K, B):
     else:
         ref_gu = w4.w4a16_moe_gemm(X, Wq, S, s, e, n, T, k, B, k)
         ref_dn = w4.w4a16_moe_gemm(X1, Wq, S, s, e, n, T, k, B, 1, topk_weights=tw)
-    gu = w4.w4a16_moe_gemm_tiled(X, Wt, S, s, e, n, T, k, B, k, Z=Z)
-    dn = w4.w4a16_moe_gemm_tiled(X1, Wt, S, s, e, n, T, k, B, 1, Z=Z, topk_weights=tw)
+    gu = w4.w4a16_moe_gemm_tiled(X, Wt, St, N, s, e, n, T, k, B, k, Z=Zt)
+    dn = w4.w4a16_moe_gemm_tiled(X1, Wt, St, N, s, e, n, T, k, B, 1, Z=Zt, topk_weights=tw)
     np.testing.assert_array_equal(down_bits(gu)[rows], down_bits(ref_gu)[rows])
     np.testing.assert_array_equal(down_bits(dn)[rows], down_bits(ref_dn)[rows])
     if N % 2 == 0:
@@ -130,7 +176,7 @@ def test_grouped_tiled_equals_canonical(asym, T, E, k, N, K, B):
             ref_a = w4.w4a16_moe_gemm_swiglu_asym(X, Wq, S, Z, s, e, n, T, k, B, k)
         else:
             ref_a = w4.w4a16_moe_gemm_swiglu(X, Wq, S, s, e, n, T, k, B, k)
-        a = w4.w4a16_moe_gemm_swiglu_tiled(X, Wt, S, s, e, n, T, k, B, k, Z=Z)
+        a = w4.w4a16_moe_gemm_swiglu_tiled(X, Wt, St, N, s, e, n, T, k, B, k, Z=Zt)
         np.testing.assert_array_equal(down_bits(a)[rows], down_bits(ref_a)[rows])
 
 
@@ -140,12 +186,12 @@ def test_grouped_tiled_against_oracle():
     srcs = [synth.bits(synth.weights(N, K, 70, stream=60 + e)) for e in range(E)]
     ref = [quant.quantize_pack(b) for b in srcs]
     Wt = up(layout.repack(np.stack([r[0] for r in ref])))
-    S = up_bits(np.stack([r[1] for r in ref]))
+    St = up_bits(layout.repack_groups(np.stack([r[1] for r in ref]), K))
     ids = synth.random_ids(T, k, E, 71).numpy()
     s_ref, e_ref, n_ref = omoe.align(ids, E, B)
     Xb = synth.bits(synth.activations(T, K, 72))
     s, e, n = w4.moe_align_block_size(up(ids), E, B)
-    y = down_bits(w4.w4a16_moe_gemm_tiled(up_bits(Xb), Wt, S, s, e, n, T, k, B, k))
+    y = down_bits(w4.w4a16_moe_gemm_tiled(up_bits(Xb), Wt, St, N, s, e, n, T, k, B, k))
     rows = omoe.grouped_gemm(Xb, lambda x: ref[x], s_ref, e_ref, n_ref, B, k, T * k)
     fs = sorted(rows)
     ok, a, r = gemm.within_tolerance(y[fs], np.stack([rows[f] for f in fs]), ATOL, RTOL)
@@ -168,11 +214,15 @@ def test_full_layers_tiled_equal_canonical(name):
     s, e, n = w4.moe_align_block_size(ids, E, B)
     A = w4.w4a16_moe_gemm_swiglu(X, gu.Wq, gu.S, s, e, n, T, k, B, k)
     H2 = w4.w4a16_moe_gemm(A, dn.Wq, dn.S, s, e, n, T, k, B, 1)
-    gu_t, dn_t = w4.w4_repack(gu.Wq), w4.w4_repack(dn.Wq)
-    A_t = w4.w4a16_moe_gemm_swiglu_tiled(X, gu_t, gu.S, s, e, n, T, k, B, k)
+    gu_t = wmoe.repack_experts(gu, keep_canonical=True)
+    dn_t = wmoe.repack_experts(dn)
+    A_t = wmoe.grouped_gemm_swiglu(X, gu_t, s, e, n, T, k, B, k)
     np.testing.assert_array_equal(down_bits(A_t), down_bits(A))
-    H2_t = w4.w4a16_moe_gemm_tiled(A, dn_t, dn.S, s, e, n, T, k, B, 1)
+    H2_t = wmoe.grouped_gemm(A, dn_t, s, e, n, T, k, B, 1)
     np.testing.assert_array_equal(down_bits(H2_t), down_bits(H2))
     # and back: restore gives the canonical experts
-    np.testing.assert_array_equal(down(w4.w4_restore(gu_t, 2 * I, H)).reshape(E, 2 * I, H // 8),
-                                  down(gu.Wq))
+    np.testing.assert_array_equal(
+        down(w4.w4_restore(gu_t.Wt, 2 * I, H)).reshape(E, 2 * I, H // 8), down(gu.Wq))
+    np.testing.assert_array_equal(
+        down_raw(w4.w4_restore_groups(gu_t.St, 2 * I, H)).reshape(E, 2 * I, H // 32),
+        down_raw(gu.S))
