@@ -69,7 +69,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // row r of the run is pair f = sorted_ids[row0 + r] (valid if f < n_pairs),
 // activation row f / x_row_div, output row f.
 // SA: K is a multiple of 256, so a row's scales start 16-byte aligned and
-// eight of them are one 16-byte load.
+// eight of them are one 16-byte load, and every step lies inside K: loads
+// carry no range checks.  Loads issued ahead past the last step then read
+// the next row's bytes or, past the buffer, zero; nothing uses them.
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
 // take gate rows [c, c + 2 WN) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform, so the LDS addresses of the direct-to-LDS loads are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
   // Tile of this workgroup.  MoE: a slot of at most BM rows (an alignment
@@ -353,7 +356,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const int col = step * kStepK + 8 * ((lane & 7) ^ (((8 * (wave * XPW + i) + (lane >> 3)) >> 1) & 7));
-        const uint32_t off = (xoff[i] != kOOB && col < K) ? xoff[i] + (uint32_t)step * (kStepK * 2) : kOOB;
+        // (an OOB row's offset stays past the buffer: X is below 2 GiB)
+        const uint32_t off = (SA || (xoff[i] != kOOB && col < K))
+                                 ? xoff[i] + (uint32_t)step * (kStepK * 2)
+                                 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xr, (__attribute__((address_space(3))) void*)(st + (wave * XPW + i) * 512), 16, off, 0,
             0, 0);
@@ -369,11 +375,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         // the last 32-row block); a group past K reads zero
         uint32_t woff;
         if constexpr (TL)
-          woff = (g < G) ? (((n >> 5) * (uint32_t)nsteps + (uint32_t)step) * 64u + (uint32_t)h * 32u +
+          woff = (SA || g < G) ? (((n >> 5) * (uint32_t)nsteps + (uint32_t)step) * 64u + (uint32_t)h * 32u +
                             (n & 31u)) * 16u
                          : kOOB;
         else
-          woff = (g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
+          woff = (SA || g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
         wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
       }
     };
@@ -389,10 +395,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         if constexpr (TL) {
           // rows past N fall in the zero padding or past the expert's blocks
           const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (g0 < G) ? e * 2u : kOOB, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (SA || g0 < G) ? e * 2u : kOOB, 0, 0);
         } else if constexpr (SA) {
-          const uint32_t soff = (g0 < G) ? (n * (uint32_t)G + (uint32_t)g0) * 2u : kOOB;
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, soff, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (n * (uint32_t)G + (uint32_t)g0) * 2u,
+                                                          0, 0);
         } else {
           uint32_t hw[8];
 #pragma unroll
@@ -416,10 +422,9 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
         if constexpr (TL) {
           const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, (g0 < G) ? e : kOOB, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, (SA || g0 < G) ? e : kOOB, 0, 0);
         } else if constexpr (SA) {
-          const uint32_t zoff = (g0 < G) ? n * (uint32_t)G + (uint32_t)g0 : kOOB;
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, zoff, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, n * (uint32_t)G + (uint32_t)g0, 0, 0);
         } else {
           uint32_t b[8];
 #pragma unroll
@@ -515,7 +520,8 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
           load_z((step >> 3) + 1, zraw);
         }
       }
-      if (step < nsteps) {
+      // (SA with a 4-step unroll: K/64 steps, a multiple of the unroll)
+      if ((SA && kU == 4) || step < nsteps) {
         // step t of the window uses the bf16 in half (t >= 4) of dword t % 4:
         // one v_perm with a uniform selector moves it into the top half
         const uint32_t hsel = (step & 4) ? 0x03020C0Cu : 0x01000C0Cu;
