@@ -69,9 +69,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // row r of the run is pair f = sorted_ids[row0 + r] (valid if f < n_pairs),
 // activation row f / x_row_div, output row f.
 // SA: K is a multiple of 256, so a row's scales start 16-byte aligned and
-// eight of them are one 16-byte load, and every step lies inside K: loads
-// carry no range checks.  Loads issued ahead past the last step then read
-// the next row's bytes or, past the buffer, zero; nothing uses them.
+// eight of them are one 16-byte load, and every step lies inside K: the
+// loads carry no per-lane range checks.  Loads issued ahead past the last
+// step read the next rows' bytes, which no step uses; the 32-row tile,
+// which issues codes up to eight steps ahead, sends them to an empty buffer
+// instead (a uniform choice: they read zero without touching memory).
 // SWI (MoE only): N = 2I weight rows, gate [0, I) and up [I, 2I); waves 0, 1
 // take gate rows [c, c + 2 WN) and waves 2, 3 the matching up rows, and the
 // epilogue writes A = bf16(silu(bf16(gate)) * bf16(up)) [rows, I].
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   constexpr int kWS = kGroupW ? 8 : 2;   // code register sets (steps ahead)
   constexpr int kU = kWS > kXS ? kWS : kXS;   // K-loop unroll: stage and set named statically
   constexpr bool kRunSlots = MOE && BM <= 32;  // grouped product: slots index runs
+  constexpr bool kNullPast = SA && kGroupW;      // loads past the last step read the empty buffer
   static_assert(kU % kXS == 0 && kU % kWS == 0, "unroll");
   static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   const __amdgpu_buffer_rsrc_t sr = rsrc(Sbase, (uint32_t)grp_elems * 2u);
   const uint8_t* Zbase = ZP ? Z + (int64_t)expert * grp_elems : nullptr;
   const __amdgpu_buffer_rsrc_t zr = rsrc(Zbase, ZP ? (uint32_t)grp_elems : 0u);
+  const __amdgpu_buffer_rsrc_t rnull = rsrc(nullptr, 0u);   // every load reads zero
 
   {
     // ---- row tables (thread r < BM fills row r)
@@ -361,8 +365,9 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
                                  ? xoff[i] + (uint32_t)step * (kStepK * 2)
                                  : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xr, (__attribute__((address_space(3))) void*)(st + (wave * XPW + i) * 512), 16, off, 0,
-            0, 0);
+            (kNullPast && step >= nsteps) ? rnull : xr,
+            (__attribute__((address_space(3))) void*)(st + (wave * XPW + i) * 512), 16, off, 0, 0,
+            0);
       }
     };
     // codes of one step into a register set
@@ -380,24 +385,28 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
                          : kOOB;
         else
           woff = (SA || g < G) ? (n * (uint32_t)kw + 4u * (uint32_t)g) * 4u : kOOB;
-        wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, 0, 0);
+        wreg[ns] = __builtin_amdgcn_raw_buffer_load_b128((kNullPast && step >= nsteps) ? rnull : wr, woff,
+                                                         0, 0);
       }
     };
     // Scales come in windows of 8 steps (16 groups): lane (n, h) loads the
     // 8 scales of groups 16 u + 8 h .. + 7 of its row, so a scale row is
     // read in 32-byte pieces, each once (scattered 2-byte loads per step
     // would need each 128-byte scale line to stay in L2 for 32 steps).
+    // SA: windows past K read the next rows' values, which no step uses
+    // (the 32-row tile sends a window wholly past K to the empty buffer).
     auto load_s = [&](int u, u32x4 (&raw)[NS]) __attribute__((always_inline)) {
       const int g0 = 16 * u + 8 * h;
+      const __amdgpu_buffer_rsrc_t srs = (kNullPast && 16 * u >= G) ? rnull : sr;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
         if constexpr (TL) {
           // rows past N fall in the zero padding or past the expert's blocks
           const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (SA || g0 < G) ? e * 2u : kOOB, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(srs, (SA || g0 < G) ? e * 2u : kOOB, 0, 0);
         } else if constexpr (SA) {
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, (n * (uint32_t)G + (uint32_t)g0) * 2u,
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b128(srs, (n * (uint32_t)G + (uint32_t)g0) * 2u,
                                                           0, 0);
         } else {
           uint32_t hw[8];
@@ -417,14 +426,15 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     // aligned, K % 256 == 0).
     auto load_z = [&](int u, u32x2 (&raw)[NS]) __attribute__((always_inline)) {
       const int g0 = 16 * u + 8 * h;
+      const __amdgpu_buffer_rsrc_t zrs = (kNullPast && 16 * u >= G) ? rnull : zr;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const uint32_t n = (uint32_t)(n_base + ns * 32 + l32);
         if constexpr (TL) {
           const uint32_t e = ((n >> 4) * gblk + ((uint32_t)g0 >> 3)) * 128u + 8u * (n & 15u);
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, (SA || g0 < G) ? e : kOOB, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zrs, (SA || g0 < G) ? e : kOOB, 0, 0);
         } else if constexpr (SA) {
-          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zr, n * (uint32_t)G + (uint32_t)g0, 0, 0);
+          raw[ns] = __builtin_amdgcn_raw_buffer_load_b64(zrs, n * (uint32_t)G + (uint32_t)g0, 0, 0);
         } else {
           uint32_t b[8];
 #pragma unroll
