@@ -457,6 +457,16 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
         by_B[str(B2)] = round(timer.run(layer_b, iters) / iters * 1e3, 1)
         del b2
     q = torch.quantile(counts.float(), torch.tensor([0.1, 0.5, 0.9], device=counts.device))
+
+    def gemm_rates(us):
+        """The two grouped products (fused gate_up + SwiGLU, down) taking us
+        microseconds together: weight stream and MFMA rates."""
+        return {"us": round(us, 1),
+                "weight_GB/s": round(wbytes / (us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                "TFLOP/s": round((fl_gu + fl_dn) / (us * 1e-6) / 1e12, 1),
+                "frac_mfma_bf16": round((fl_gu + fl_dn) / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
     res = {
         "T": T, "E": E, "k": k, "H": H, "I": I, "B": B,
         "layer_us": round(t_layer * 1e3, 1),
@@ -472,6 +482,8 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
                                       / 1e12 / PEAK_BF16_TFLOPS, 4),
         "frac_hbm_gemms": round(wbytes / ((per["gate_up"] + per["down"]) * 1e-6) / 1e9
                                 / PEAK_HBM_GBS, 4),
+        "gemms_kernel_order": gemm_rates(per["gate_up_swiglu_kernel_order"]
+                                         + per["down_kernel_order"]),
         "layer_us_by_B": by_B,
         "rows_per_expert_max": int(counts.max().item()),
         "rows_per_expert_min": int(counts.min().item()),

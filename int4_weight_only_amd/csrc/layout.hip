@@ -85,6 +85,43 @@ __global__ __launch_bounds__(256) void k_relayout_groups(const V* __restrict__ s
   }
 }
 
+// K/32 a multiple of 8 and both buffers aligned to a whole piece: a piece
+// (8 values of one row) is contiguous on both sides, one vector load and
+// one vector store (P: 16 bytes of bf16 or 8 bytes of uint8)
+template <bool RESTORE, typename P, typename I>
+__global__ __launch_bounds__(256) void k_relayout_groups_vec(const P* __restrict__ src,
+                                                             P* __restrict__ dst, I N, I gb,
+                                                             I pieces, I total) {
+  // I: 32-bit index arithmetic whenever every index fits (the divisions
+  // dominate otherwise)
+  for (I i = (I)blockIdx.x * 256 + threadIdx.x; i < total; i += (I)gridDim.x * 256) {
+    const I e = i / pieces;
+    const I p = i - e * pieces;
+    const I blk = p >> 4;
+    const I r = blk / gb, c = blk - r * gb;
+    const I n = 16 * r + (p & 15);
+    const I canon = (e * N + n) * gb + c;   // in pieces: rows of gb pieces
+    if constexpr (RESTORE) {
+      if (n < N) dst[canon] = src[i];
+    } else {
+      P v{};
+      if (n < N) v = src[canon];
+      dst[i] = v;
+    }
+  }
+}
+
+template <typename P, typename I>
+void launch_groups_vec(const void* src, void* dst, bool restore, I N, I gb, I pieces, I total,
+                       unsigned blocks, hipStream_t st) {
+  if (restore)
+    hipLaunchKernelGGL((k_relayout_groups_vec<true, P, I>), dim3(blocks), dim3(256), 0, st,
+                       (const P*)src, (P*)dst, N, gb, pieces, total);
+  else
+    hipLaunchKernelGGL((k_relayout_groups_vec<false, P, I>), dim3(blocks), dim3(256), 0, st,
+                       (const P*)src, (P*)dst, N, gb, pieces, total);
+}
+
 hipError_t launch_relayout_groups(const void* src, void* dst, int elem_bytes, int64_t E,
                                   int64_t N, int64_t K, bool restore, hipStream_t st) {
   const int64_t pieces = tiled_group_elems(N, K) / 8;
@@ -92,6 +129,27 @@ hipError_t launch_relayout_groups(const void* src, void* dst, int elem_bytes, in
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   const int64_t G = K / 32, gb = (G + 7) / 8;
+  const uintptr_t piece_bytes = 8u * (uintptr_t)elem_bytes;
+  if (G % 8 == 0 && (uintptr_t)src % piece_bytes == 0 && (uintptr_t)dst % piece_bytes == 0) {
+    // the largest index: the tiled piece count (canonical indexes are smaller)
+    const bool small = total + (int64_t)blocks * 256 < ((int64_t)1 << 31);
+    if (elem_bytes == 2) {
+      if (small)
+        launch_groups_vec<u32x4, uint32_t>(src, dst, restore, (uint32_t)N, (uint32_t)gb,
+                                           (uint32_t)pieces, (uint32_t)total, (unsigned)blocks, st);
+      else
+        launch_groups_vec<u32x4, int64_t>(src, dst, restore, N, gb, pieces, total,
+                                          (unsigned)blocks, st);
+    } else {
+      if (small)
+        launch_groups_vec<u32x2, uint32_t>(src, dst, restore, (uint32_t)N, (uint32_t)gb,
+                                           (uint32_t)pieces, (uint32_t)total, (unsigned)blocks, st);
+      else
+        launch_groups_vec<u32x2, int64_t>(src, dst, restore, N, gb, pieces, total,
+                                          (unsigned)blocks, st);
+    }
+    return hipGetLastError();
+  }
   if (elem_bytes == 2) {
     if (restore)
       hipLaunchKernelGGL((k_relayout_groups<true, uint16_t>), dim3((unsigned)blocks), dim3(256),

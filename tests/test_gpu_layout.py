@@ -97,6 +97,27 @@ def test_repack_groups_bit_exact_and_restore(E, N, K):
         np.testing.assert_array_equal(down_raw(back).reshape(E, N, K // 32), down_raw(A))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.uint8])
+def test_repack_groups_any_alignment(dtype):
+    """Buffers one element off a whole piece take the element-wise kernel;
+    the result is the same bits as from aligned buffers (K/32 % 8 == 0, so
+    aligned buffers take the vector kernel)."""
+    E, N, K = 2, 37, 512
+    say(f"repack groups unaligned {dtype}")
+    _, S, Z = codes(N, K, 9, asym=True, E=E)
+    A = S if dtype == torch.bfloat16 else Z
+    ref = down_raw(w4.w4_repack_groups(A))
+    flat = torch.zeros(A.numel() + 1, dtype=dtype, device="cuda")
+    src = flat[1:].view(E, N, K // 32)
+    src.copy_(A)
+    out = torch.zeros(E * layout.repacked_group_elems(N, K) + 1, dtype=dtype, device="cuda")
+    w4.w4_repack_groups(src, out=out[1:])
+    np.testing.assert_array_equal(down_raw(out[1:]).reshape(ref.shape), ref)
+    back = torch.zeros(A.numel() + 1, dtype=dtype, device="cuda")
+    w4.w4_restore_groups(out[1:], N, K, out=back[1:])
+    np.testing.assert_array_equal(down_raw(back[1:]), down_raw(A).reshape(-1))
+
+
 def test_restore_groups_ignores_padding_and_leaves_other_memory():
     """Padding elements of the kernel-order scales (rows past N, groups past
     K) are never read back: poison them and restore still gives S."""
