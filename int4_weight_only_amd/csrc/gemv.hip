@@ -454,6 +454,16 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
 // region in whole lines (load_x_lines, issued with the others) and each lane
 // reads its operand of MFMA j where it landed.  Each dequantized word feeds
 // the MFMAs of both halves.  The region then takes the wave's partial sums.
+// The same for tile t alone.
+template <bool FULL, int T, bool TL>
+__device__ __forceinline__ void load_codes_tile(u32x4 (&wv)[T][kCPW], int t, const CodeRows<TL>& wr,
+                                                int c0, int n16, int kq, int G) {
+#pragma unroll
+  for (int cc = 0; cc < kCPW; ++cc)
+    wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(
+        wr.r, wr.template off<FULL>((uint32_t)(t * 16 + n16), 4 * (c0 + cc) + kq, G), 0, 0);
+}
+
 template <int KM, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
@@ -494,35 +504,62 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
 
   for (int pass = 0; pass < npass; ++pass) {
     const int c0 = pass * (kWaves * kCPW) + wave * kCPW;   // first chunk of this wave
-    // byte offset of lane (n16, kq)'s 16 activation bytes of group 4 c + j
-    // in half hh (rows past M lie past the buffer and groups past K are sent
-    // past it: both read zero)
-    auto x_off = [&](int hh, int cc, int j) {
-      const int g = 4 * (c0 + cc) + j;
-      const int row = 16 * hh + n16;
-      return (FULL || g < G) ? ((uint32_t)row * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
-    };
     // ---- scales (and zero points) first
     PassScales<KM, T, ZP, TL> sc;
     sc.load(sr, zr, n16, kq, 4 * c0, G);
-    // ---- half 0's activations into registers, half 1's into this wave's
-    // LDS region in whole lines
     u32x4 xop[kCPW][4];
-#pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(0, cc, j), 0, 0);
-    load_x_lines<FULL>(xr, &lds[wave][0], 16, c0, lane, K, G);
-    // ---- codes, tile by tile; loads return in issue order, so tile t is
-    // processed as soon as its codes are in
     u32x4 wv[T][kCPW];
-    load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
-    __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
-
-    sc.spread();
+    if constexpr (FULL) {
+      // ---- both halves' activations go through this wave's LDS region in
+      // whole lines, one after the other: half 0, then tile 0's codes; once
+      // half 0 has landed it is read into registers in operand order and
+      // half 1 takes its place, followed by the other tiles' codes.  Loads
+      // return in issue order, so tile t is processed as soon as its codes
+      // are in.
+      __builtin_amdgcn_sched_barrier(0);   // the waits below count loads in issue order
+      load_x_lines<FULL>(xr, &lds[wave][0], 0, c0, lane, K, G);
+      __builtin_amdgcn_sched_barrier(0);
+      load_codes_tile<FULL, T, TL>(wv, 0, wr, c0, n16, kq, G);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCPW) : "memory");   // half 0 has landed
 #pragma unroll
-    for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
+      for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xop[cc][j] = *(const u32x4*)&lds[wave][x_slot(n16, kq, j, cc)];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the region is refilled
+      __builtin_amdgcn_sched_barrier(0);
+      load_x_lines<FULL>(xr, &lds[wave][0], 16, c0, lane, K, G);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 1; t < T; ++t) load_codes_tile<FULL, T, TL>(wv, t, wr, c0, n16, kq, G);
+      __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the next wait
+      sc.spread();
+      // half 1 has landed once only the later tiles' codes are in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((T - 1) * kCPW) : "memory");
+    } else {
+      // ---- K not a whole number of passes (range checks on every load;
+      // the staging above would spill): half 0's activations into
+      // registers, 64-byte runs per row, transposed to operand order; half
+      // 1's into this wave's LDS region in whole lines
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int g = 4 * (c0 + cc) + j;
+          const uint32_t off =
+              (g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
+          xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        }
+      load_x_lines<FULL>(xr, &lds[wave][0], 16, c0, lane, K, G);
+      load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
+      __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
+      sc.spread();
+#pragma unroll
+      for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
+      // half 1 has landed once only the codes are in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T * kCPW) : "memory");
+    }
 
     f32x4 acc0[T], acc1[T];
 #pragma unroll
