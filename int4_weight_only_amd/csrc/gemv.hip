@@ -473,6 +473,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
                                                           int K) {
   static_assert(T >= 1 && T <= 3, "decode shape");
   constexpr bool FULL = KM == 2;
+  // tiles whose codes go out before half 1 (two measured slightly faster
+  // than one at M = 32)
+  constexpr int kEarly = T < 2 ? 1 : 2;
+  static_assert(kEarly <= 2, "early code tiles");
   constexpr int PSTR = 36;                         // LDS row stride (floats): 32 rows + pad
   constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
   constexpr int XREG = kCPW * 4 * 256;             // floats: 8 x 1 KB of half-1 activations
@@ -520,8 +524,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       load_x_lines<FULL>(xr, &lds[wave][0], 0, c0, lane, K, G);
       __builtin_amdgcn_sched_barrier(0);
       load_codes_tile<FULL, T, TL>(wv, 0, wr, c0, n16, kq, G);
+      if constexpr (kEarly > 1) load_codes_tile<FULL, T, TL>(wv, 1, wr, c0, n16, kq, G);
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCPW) : "memory");   // half 0 has landed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly * kCPW) : "memory");   // half 0 has landed
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
@@ -532,11 +537,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
       load_x_lines<FULL>(xr, &lds[wave][0], 16, c0, lane, K, G);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 1; t < T; ++t) load_codes_tile<FULL, T, TL>(wv, t, wr, c0, n16, kq, G);
+      for (int t = kEarly; t < T; ++t) load_codes_tile<FULL, T, TL>(wv, t, wr, c0, n16, kq, G);
       __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the next wait
       sc.spread();
       // half 1 has landed once only the later tiles' codes are in flight
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((T - 1) * kCPW) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((T - kEarly) * kCPW) : "memory");
     } else {
       // ---- K not a whole number of passes (range checks on every load;
       // the staging above would spill): half 0's activations into
