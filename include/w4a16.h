@@ -233,10 +233,10 @@ int w4_restore_groups(const void* At, int32_t elem_bytes, int64_t E, int64_t N, 
 
 /*
  * w4a16_gemm_tiled -- w4a16_gemm (Z == NULL) or w4a16_gemm_asym (Z given)
- * with the codes, the scales and the zero points in kernel order (Wt from
- * w4_repack, St and Zt from w4_repack_groups, E = 1).  Same definition,
- * arguments, limits and dispatch; the results equal those of the
- * canonical-layout call bit for bit.
+ * with the codes, the scales and the zero points in kernel order: Wt from
+ * w4_repack, S and Z from w4_repack_groups (E = 1; w4_repacked_group_elems
+ * values each).  Same definition, arguments, limits and dispatch; the
+ * results equal those of the canonical-layout call bit for bit.
  */
 int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
                      const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
@@ -246,7 +246,7 @@ int w4a16_gemm_tiled(const uint16_t* X, const int32_t* Wt, const uint16_t* S,
  * w4a16_moe_gemm_tiled, w4a16_moe_gemm_swiglu_tiled -- the grouped
  * products (symmetric with Z == NULL, zero-point with Z given) with every
  * expert's codes, scales and zero points in kernel order (Wt from w4_repack,
- * St and Zt from w4_repack_groups, E experts each).  Definitions, arguments
+ * S and Z from w4_repack_groups, E experts each).  Definitions, arguments
  * and limits as w4a16_moe_gemm(_asym) and w4a16_moe_gemm_swiglu(_asym);
  * results equal the canonical-layout calls bit for bit.
  */
