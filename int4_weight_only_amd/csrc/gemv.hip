@@ -22,12 +22,14 @@
 // behind a branch.  Word j of those 16 bytes is the lane's B operand of
 // MFMA j (v_mfma_f32_16x16x32_bf16: A = X rows, B = weight rows), whose 32
 // k values are elements 8 j .. 8 j + 7 of the four groups of the chunk, so
-// a lane dequantizes all four words of one group with one scale.  The
-// activations come in as contiguous 64-byte runs per row (lane (m, kq):
-// elements 8 kq .. 8 kq + 7 of group 4 c + j, one load per j) and a 4 x 4
-// transpose of 16-byte pieces across the four 16-lane rows (v_permlane32_swap
-// + v_permlane16_swap), done once per wave, gives lane (m, kq) its A
-// operands: elements 8 j .. 8 j + 7 of group 4 c + kq of row m.  A wave's
+// a lane dequantizes all four words of one group with one scale.  Lane
+// (m, kq)'s A operand of MFMA j is elements 8 j .. 8 j + 7 of group
+// 4 c + kq of row m: for M <= 8 each lane loads those 16 bytes itself; for
+// more rows the activations come in whole lines through LDS (below) or, with
+// four tiles, as contiguous 64-byte runs per row (lane (m, kq): elements
+// 8 kq .. 8 kq + 7 of group 4 c + j, one load per j) followed by a 4 x 4
+// transpose of 16-byte pieces across the four 16-lane rows
+// (v_permlane32_swap + v_permlane16_swap), done once per wave.  A wave's
 // eight scales of a row are one 16-byte load: lane row r fetches tile r's,
 // permlane swaps broadcast them, and each lane picks its group's.
 //   Each wave issues all of its loads at once (scales and activations first,
@@ -317,12 +319,19 @@ __device__ __forceinline__ void load_codes(u32x4 (&wv)[T][kCPW], const CodeRows<
 // 4096-element pass as well (no group index is ever past K, so no offset
 // needs a range check).  Activation rows past M need none either: they lie
 // past the end of X's buffer and read zero.  T: tiles of 16 weight rows per
-// workgroup.  XL (for 8 < M <= 16, T <= 3): the activations come through the wave's
-// LDS region in whole 128-byte lines (two rows per load, half the cache-line
-// requests of the 64-byte runs) and each lane reads its operands in MFMA
-// order, with no transpose; for M <= 8 the extra LDS round trip costs more
-// than the lines it saves, and they go to registers.
-template <int KM, int T, bool ZP, bool TL, bool XL>
+// workgroup.  XM, how the activations arrive:
+//   kXLines (8 < M <= 16, T <= 3): through the wave's LDS region in whole
+//     128-byte lines (two rows per load, half the cache-line requests of the
+//     64-byte runs); each lane reads its operands in MFMA order.
+//   kXOperand (M <= 8): each lane loads its own operands into registers in
+//     MFMA order (16 bytes per MFMA, spread over two lines per row): with at
+//     most 8 rows in the buffer the requests stay few, and neither the LDS
+//     round trip nor a transpose is needed.
+//   kXRuns (8 < M <= 16, T = 4, where the LDS path has no registers left):
+//     64-byte runs per row into registers, then the transpose to operand
+//     order (one cache line per row and load).
+enum XMode { kXRuns = 0, kXLines = 1, kXOperand = 2 };
+template <int KM, int T, bool ZP, bool TL, int XM>
 __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
                                                           const uint16_t* __restrict__ S,
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   constexpr bool FULL = KM == 2;
   constexpr int PSTR = 20;                         // LDS row stride (floats)
   constexpr int WSTR = 16 * PSTR + 4;              // per-tile block: padded off the bank period
-  constexpr int XREG = XL ? 2048 : 0;              // floats: the wave's 16 x 256 activations
+  constexpr int XREG = XM == kXLines ? 2048 : 0;   // floats: the wave's 16 x 256 activations
   constexpr int REGION = T * WSTR > XREG ? T * WSTR : XREG;
   __shared__ __attribute__((aligned(16))) float lds[kWaves][REGION];
   __shared__ float ybuf[T][256];                   // partials across K passes
@@ -367,20 +376,23 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
     sc.load(sr, zr, n16, kq, 4 * c0, G);
     // ---- activations (L2 hits after the first CU's request)
     u32x4 xop[kCPW][4];
-    if constexpr (XL) {
+    if constexpr (XM == kXLines) {
       // into this wave's LDS region: load i brings rows 2 i, 2 i + 1 of the
       // wave's 16 x 256 slice; lane l's 16 bytes land in slot l % 32 of row
       // 2 i + l / 32 and hold piece (l % 32) ^ row of it
       load_x_lines<FULL>(xr, &lds[wave][0], 0, c0, lane, K, G);
     } else {
-      // lane (m, kq) takes elements 8 kq .. 8 kq + 7 of group 4 c + j of row m
+      // kXRuns: lane (m, kq) takes elements 8 kq .. 8 kq + 7 of group
+      // 4 c + j of row m; kXOperand: elements 8 j .. 8 j + 7 of group
+      // 4 c + kq, its operand of MFMA j
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int g = 4 * (c0 + cc) + j;
+          const int g = 4 * (c0 + cc) + (XM == kXOperand ? kq : j);
+          const uint32_t e = XM == kXOperand ? 8u * j : 8u * kq;
           const uint32_t off =
-              (FULL || g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + 8u * kq) * 2u : kOOB;
+              (FULL || g < G) ? ((uint32_t)n16 * (uint32_t)K + 32u * g + e) * 2u : kOOB;
           xop[cc][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
         }
     }
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
     load_codes<FULL, T, TL>(wv, wr, c0, n16, kq, G);
     __builtin_amdgcn_sched_barrier(0);   // keep every load above ahead of the first wait
 
-    if constexpr (XL) {
+    if constexpr (XM == kXLines) {
       // the activations have landed once only the codes are in flight; lane
       // (m, kq)'s operand of MFMA j of chunk cc (elements 8 j .. 8 j + 7 of
       // group 4 c + kq of row m) is piece 16 cc + 4 kq + j of row m
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
           xop[cc][j] = *(const u32x4*)&lds[wave][x_slot(n16, kq, j, cc)];
     }
     sc.spread();
-    if constexpr (!XL) {
+    if constexpr (XM == kXRuns) {
 #pragma unroll
       for (int cc = 0; cc < kCPW; ++cc) transpose_pieces(xop[cc]);
     }
@@ -633,12 +645,12 @@ int cu_count() {
   return cus[dev];
 }
 
-template <int KM, int T, bool ZP, bool TL, bool XL>
+template <int KM, int T, bool ZP, bool TL, int XM>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                           hipStream_t st) {
   const int64_t blocks = (N + T * 16 - 1) / (T * 16);
-  hipLaunchKernelGGL((k_decode16<KM, T, ZP, TL, XL>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((k_decode16<KM, T, ZP, TL, XM>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
                      st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -649,15 +661,17 @@ hipError_t run_decode16(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
   const int64_t tiles = (N + 15) / 16;
   const int64_t cus = cu_count();
   const int64_t tpw = (tiles + cus - 1) / cus;
-  if (M > 8 && tpw <= 3) {   // (four tiles leave no registers for the LDS path)
-    if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
-    if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
-    return run_decode16_t<KM, 3, ZP, TL, true>(X, Wq, S, Z, Y, M, N, K, st);
+  if (M > 8) {
+    // (four tiles leave no registers for the LDS path)
+    if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, kXLines>(X, Wq, S, Z, Y, M, N, K, st);
+    if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, kXLines>(X, Wq, S, Z, Y, M, N, K, st);
+    if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL, kXLines>(X, Wq, S, Z, Y, M, N, K, st);
+    return run_decode16_t<KM, 4, ZP, TL, kXRuns>(X, Wq, S, Z, Y, M, N, K, st);
   }
-  if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
-  if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
-  return run_decode16_t<KM, 4, ZP, TL, false>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw <= 1) return run_decode16_t<KM, 1, ZP, TL, kXOperand>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 2) return run_decode16_t<KM, 2, ZP, TL, kXOperand>(X, Wq, S, Z, Y, M, N, K, st);
+  if (tpw == 3) return run_decode16_t<KM, 3, ZP, TL, kXOperand>(X, Wq, S, Z, Y, M, N, K, st);
+  return run_decode16_t<KM, 4, ZP, TL, kXOperand>(X, Wq, S, Z, Y, M, N, K, st);
 }
 
 template <int KM, int T, bool ZP, bool TL>

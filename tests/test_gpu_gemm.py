@@ -110,6 +110,14 @@ def test_decode_full(M):
     run_case(M, wl["N"], wl["K"], wl["seed"], "decode")
 
 
+@pytest.mark.parametrize("M", [1, 8, 9, 16])
+def test_decode_four_tiles(M):
+    """N = 14336 gives each CU four 16-row tiles: M <= 8 loads its operands
+    directly, 8 < M <= 16 takes the 64-byte runs and the register transpose
+    (the LDS path has no registers left at four tiles)."""
+    run_case(M, 14336, 4096, 77 + M, "four tiles")
+
+
 @pytest.fixture(scope="module")
 def decode_weights():
     """The decode workload's W [12288, 4096], packed by the GPU (asserted
