@@ -312,6 +312,16 @@ __device__ __forceinline__ void load_codes(u32x4 (&wv)[T][kCPW], const CodeRows<
           wr.r, wr.template off<FULL>((uint32_t)(t * 16 + n16), 4 * (c0 + cc) + kq, G), 0, 0);
 }
 
+// The same for tile t alone.
+template <bool FULL, int T, bool TL>
+__device__ __forceinline__ void load_codes_tile(u32x4 (&wv)[T][kCPW], int t, const CodeRows<TL>& wr,
+                                                int c0, int n16, int kq, int G) {
+#pragma unroll
+  for (int cc = 0; cc < kCPW; ++cc)
+    wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(
+        wr.r, wr.template off<FULL>((uint32_t)(t * 16 + n16), 4 * (c0 + cc) + kq, G), 0, 0);
+}
+
 }  // namespace
 
 // M <= 16.  KM: 0 = any K; 1 = K / 32 is a multiple of 8 (a wave's eight
@@ -461,21 +471,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode16(const uint16_t* __rest
   }
 }
 
-// 16 < M <= 32 over two 16-row activation halves.  Half 0's X sits in
-// registers as for M <= 8; half 1's X goes straight into this wave's LDS
-// region in whole lines (load_x_lines, issued with the others) and each lane
-// reads its operand of MFMA j where it landed.  Each dequantized word feeds
-// the MFMAs of both halves.  The region then takes the wave's partial sums.
-// The same for tile t alone.
-template <bool FULL, int T, bool TL>
-__device__ __forceinline__ void load_codes_tile(u32x4 (&wv)[T][kCPW], int t, const CodeRows<TL>& wr,
-                                                int c0, int n16, int kq, int G) {
-#pragma unroll
-  for (int cc = 0; cc < kCPW; ++cc)
-    wv[t][cc] = __builtin_amdgcn_raw_buffer_load_b128(
-        wr.r, wr.template off<FULL>((uint32_t)(t * 16 + n16), 4 * (c0 + cc) + kq, G), 0, 0);
-}
-
+// 16 < M <= 32 over two 16-row activation halves.  K a whole number of
+// passes: both halves come through this wave's LDS region in whole lines,
+// one after the other (half 0 is read into registers in operand order once
+// it has landed, and half 1 takes its place); otherwise half 0 comes into
+// registers as 64-byte runs per row and is transposed.  Each lane reads its
+// half-1 operand of MFMA j where it landed.  Each dequantized word feeds the
+// MFMAs of both halves.  The region then takes the wave's partial sums.
 template <int KM, int T, bool ZP, bool TL>
 __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __restrict__ X,
                                                           const uint32_t* __restrict__ Wq,
