@@ -118,6 +118,15 @@ def test_decode_four_tiles(M):
     run_case(M, 14336, 4096, 77 + M, "four tiles")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 12288, 4096), (24, 6000, 4096), (32, 8192, 8192),
+                                   (20, 700, 4096), (32, 6000, 4608)])
+def test_decode32_tiles(M, N, K):
+    """16 < M <= 32 at one, two and three tiles per workgroup, one and two
+    K passes (activation halves staged through LDS), and a K that is not a
+    whole number of passes (half 0 through registers)."""
+    run_case(M, N, K, 31 * M + N + K, "decode32 tiles")
+
+
 @pytest.fixture(scope="module")
 def decode_weights():
     """The decode workload's W [12288, 4096], packed by the GPU (asserted
