@@ -301,6 +301,24 @@ def bench_quant(w4, synth, torch, iters, timer):
         timer.settle(fn, SETTLE_MS / 3)
         qat[str(M)] = round(timer.run(fn, iters) / iters * 1e3, 1)
     out["qat_linear_forward_us_by_M"] = qat
+    # the QAT linear's input gradient at the prefill rows: W_fq^T from the
+    # codes (w4_dequant_t), then dX = dY W_fq (w4_bf16_gemm_nt)
+    M = wl["M"][0]
+    dY = synth.activations(M, N, wl["seed"] + 1, device=dev)
+    WT = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    fn = lambda i: w4.w4_dequant_t(Wq, S, out=WT)
+    timer.settle(fn, SETTLE_MS / 3)
+    t_dq = timer.run(fn, iters) / iters
+    fn = lambda i: w4.w4_bf16_gemm_nt(dY, WT, out=dX)
+    timer.settle(fn, SETTLE_MS / 3)
+    t_mm = timer.run(fn, iters) / iters
+    tf = gemm_flops(M, K, N) / (t_mm * 1e-3) / 1e12
+    out["qat_input_gradient"] = {
+        "M": M, "N": N, "K": K, "dequant_t_us": round(t_dq * 1e3, 1),
+        "dequant_t_GB/s": round(qp_bytes / (t_dq * 1e-3) / 1e9, 1),
+        "gemm_nt_us": round(t_mm * 1e3, 1), "gemm_nt_TFLOP/s": round(tf, 1),
+        "gemm_nt_frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
     return out
 
 

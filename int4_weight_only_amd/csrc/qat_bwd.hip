@@ -107,88 +107,169 @@ hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t*
 
 // --------------------------------------------------------- bf16 NT GEMM --
 // C[M, N] = bf16( sum_k A[m, k] B[n, k] ), fp32 accumulation in a fixed
-// order (k ascending in 16-wide MFMA slices).  A workgroup of 4 waves takes
-// 128 x 128 of C; wave (wm, wn) 64 x 64 as 2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16.  Lane (r = l % 32, h = l / 32) loads the 16
-// bytes k = 16 s + 8 h .. + 7 of its A row and B row straight into the
-// operand registers (raw buffer loads; rows past the end and k past K read
-// zero), the next 32-wide step's operands in flight while the MFMAs of the
-// current one run.  K % 8 == 0 (16-byte rows pieces).
-__global__ __launch_bounds__(256, 2) void k_bf16_gemm_nt(const uint16_t* __restrict__ A,
+// order.  Tile (MI355X): a workgroup of 4 waves takes 128 rows of A x 256
+// rows of B (one workgroup per CU); wave w owns B rows [64 w, 64 w + 64)
+// and all 128 A rows, as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128
+// accumulator registers), so every operand read from LDS feeds 2 or 4
+// MFMAs.  K advances 64 per step; both operands go straight from memory into
+// LDS (16-byte buffer_load ... lds, three stages: two steps ahead, no staging
+// registers), each 64-element row stored as eight 16-byte pieces
+// XOR-swizzled by (row / 2) % 8 so that the MFMA operand reads of 32 rows
+// spread over the banks.  Lane (r = l % 32, h = l / 32) reads elements
+// 32 h + 8 j .. + 7 of its row for MFMA j of a step -- the same k
+// permutation for A and B, which leaves each dot product's terms unchanged;
+// the fp32 additions run step by step, MFMA j in order.  Rows past M or N
+// and k past K read zero.  K % 8 == 0 (16-byte row pieces).
+namespace {
+constexpr int kNtBM = 128, kNtBN = 256, kNtK = 64, kNtStages = 3;
+constexpr int kNtXA = kNtBM / 8 / 4;    // 1 KB loads per A stage per wave
+constexpr int kNtXB = kNtBN / 8 / 4;    // ... per B stage per wave
+}  // namespace
+
+__global__ __launch_bounds__(256, 1) void k_bf16_gemm_nt(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ B,
                                                          uint16_t* __restrict__ C, int M, int N,
                                                          int K) {
+  // separately declared stages: each DMA target and each operand read names
+  // one object
+  __shared__ __attribute__((aligned(16))) uint16_t as0[kNtBM * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t as1[kNtBM * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t as2[kNtBM * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t bs0[kNtBN * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t bs1[kNtBN * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[kNtBN * kNtK];
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int ntn = (N + 127) / 128;
-  const int tm = blockIdx.x / ntn, tn = blockIdx.x % ntn;
-  const int m0 = tm * 128 + (wave >> 1) * 64;
-  const int n0 = tn * 128 + (wave & 1) * 64;
+  // tile order: the 1-D grid is dispatched round-robin over the 8 XCDs;
+  // XCD x walks the contiguous tile range [x per, (x + 1) per) in groups of
+  // 8 A row-blocks, so co-running workgroups share rows in its L2
+  const int mt = (M + kNtBM - 1) / kNtBM, nt = (N + kNtBN - 1) / kNtBN;
+  const int tiles = mt * nt;
+  const int per = (tiles + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= tiles) return;
+  const int group = t / (8 * nt);
+  const int gm = min(8, mt - group * 8);
+  const int in_group = t - group * (8 * nt);
+  const int m0 = (group * 8 + in_group % gm) * kNtBM;
+  const int n0 = (in_group / gm) * kNtBN;
+
   const __amdgpu_buffer_rsrc_t ar = rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
-  uint32_t arow[2], brow[2];
+  // Load i of this wave fills stage rows 8 (wave X + i) .. + 7: lane l
+  // writes the 16 bytes at slot l, row r = 8 I + l / 8, stored piece l % 8,
+  // which holds the row's piece (l % 8) ^ ((r / 2) % 8).  Byte offset of the
+  // lane's piece at step 0, or OOB for rows past the end.
+  auto row_off = [&](int first, int lim, int i) {
+    const int r = 8 * i + (lane >> 3);
+    const int pg = (lane & 7) ^ ((r >> 1) & 7);
+    const int row = first + r;
+    return row < lim ? ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)pg) * 2u : kOOB;
+  };
+  uint32_t aoff[kNtXA], boff[kNtXB];
+  int acol[kNtXA], bcol[kNtXB];   // k of the lane's piece within a step
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + 32 * i + l32, n = n0 + 32 * i + l32;
-    arow[i] = m < M ? (uint32_t)m * (uint32_t)K * 2u : kOOB;
-    brow[i] = n < N ? (uint32_t)n * (uint32_t)K * 2u : kOOB;
+  for (int i = 0; i < kNtXA; ++i) {
+    const int I = wave * kNtXA + i;
+    aoff[i] = row_off(m0, M, I);
+    acol[i] = 8 * ((lane & 7) ^ (((8 * I + (lane >> 3)) >> 1) & 7));
   }
-  auto off = [&](uint32_t row, int k) { return (row != kOOB && k < K) ? row + 2u * k : kOOB; };
-  auto load = [&](int step, u32x4 (&a)[2][2], u32x4 (&b)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int k = 32 * step + 16 * s + 8 * h;
+  for (int i = 0; i < kNtXB; ++i) {
+    const int I = wave * kNtXB + i;
+    boff[i] = row_off(n0, N, I);
+    bcol[i] = 8 * ((lane & 7) ^ (((8 * I + (lane >> 3)) >> 1) & 7));
+  }
+  auto load_stage = [&](int step, uint16_t* sa, uint16_t* sb) __attribute__((always_inline)) {
+    const int k0 = step * kNtK;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[s][i] = __builtin_amdgcn_raw_buffer_load_b128(ar, off(arow[i], k), 0, 0);
-        b[s][i] = __builtin_amdgcn_raw_buffer_load_b128(br, off(brow[i], k), 0, 0);
+    for (int i = 0; i < kNtXA; ++i) {
+      const uint32_t off =
+          (aoff[i] != kOOB && k0 + acol[i] < K) ? aoff[i] + (uint32_t)k0 * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ar, (__attribute__((address_space(3))) void*)(sa + (wave * kNtXA + i) * 512), 16, off,
+          0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kNtXB; ++i) {
+      const uint32_t off =
+          (boff[i] != kOOB && k0 + bcol[i] < K) ? boff[i] + (uint32_t)k0 * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          br, (__attribute__((address_space(3))) void*)(sb + (wave * kNtXB + i) * 512), 16, off,
+          0, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
+
+  const int nsteps = (K + kNtK - 1) / kNtK;
+  // One step: wait until this wave's loads of this step's stage have landed
+  // (the next stage's loads may stay in flight), a bare s_barrier so that
+  // every wave's part is visible and every wave is done with the stage the
+  // new loads overwrite, start the stage two steps ahead, multiply.
+  auto step_body = [&](int step, const uint16_t* sa, const uint16_t* sb, uint16_t* na,
+                       uint16_t* nb) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kNtXA + kNtXB) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_stage(step + 2, na, nb);   // past K: reads zero
+    if (step < nsteps) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 a[4], b[2];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          const int R = ms * 32 + l32;
+          a[ms] = *(const u32x4*)(sa + R * kNtK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+        }
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          const int R = wave * 64 + ns * 32 + l32;
+          b[ns] = *(const u32x4*)(sb + R * kNtK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+        }
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+          for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma32(a[ms], b[ns], acc[ms][ns]);
       }
     }
   };
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  auto mma = [&](const u32x4 (&a)[2][2], const u32x4 (&b)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[s][i], b[s][j], acc[i][j]);
-  };
-  const int nsteps = (K + 31) / 32;
-  u32x4 a0[2][2], b0[2][2], a1[2][2], b1[2][2];
-  load(0, a0, b0);
-  for (int step = 0; step < nsteps; step += 2) {
-    load(step + 1, a1, b1);            // past K: reads zero
-    mma(a0, b0);
-    if (step + 1 >= nsteps) break;
-    load(step + 2, a0, b0);
-    mma(a1, b1);
+  load_stage(0, as0, bs0);
+  load_stage(1, as1, bs1);
+  for (int step = 0; step < nsteps; step += kNtStages) {
+    step_body(step + 0, as0, bs0, as2, bs2);
+    step_body(step + 1, as1, bs1, as0, bs0);
+    step_body(step + 2, as2, bs2, as1, bs1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end drained
+
   // lane holds D[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ns = 0; ns < 2; ++ns) {
+    const int n = n0 + wave * 64 + ns * 32 + l32;
+    if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 32 * j + l32;
-      if (n >= N) continue;
+    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < M) C[(int64_t)m * N + n] = to_bf16(acc[i][j][v]);
+        const int m = m0 + ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m < M) C[(int64_t)m * N + n] = to_bf16(acc[ms][ns][v]);
       }
-    }
+  }
 }
 
 hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
                                int64_t N, int64_t K, hipStream_t st) {
-  const int64_t blocks = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t tiles = ((M + kNtBM - 1) / kNtBM) * ((N + kNtBN - 1) / kNtBN);
+  const int64_t blocks = (tiles + 7) / 8 * 8;   // whole rounds over the 8 XCDs
   hipLaunchKernelGGL(k_bf16_gemm_nt, dim3((unsigned)blocks), dim3(256), 0, st, A, B, C, (int)M,
                      (int)N, (int)K);
   return hipGetLastError();
