@@ -40,6 +40,26 @@ inline bool gemm_fits(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+namespace w4 {
+
+// The launchers size their grids by it (decode tiles per workgroup, the
+// bf16 product's tile shape).
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace w4
+
 extern "C" {
 
 const char* w4_status_string(int status) {

@@ -128,6 +128,8 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
 // --------------------------------------------------- host-side launchers ----
 // Implemented in the .hip files; called by api.hip after validation.
 namespace w4 {
+// compute units of the current device (cached per device; 256 if unknown)
+int cu_count();
 hipError_t launch_quantize(const uint16_t* W, int64_t words, int32_t* Wq, uint16_t* S,
                            uint8_t* Z, uint16_t* Wfq, bool fake, bool asym, hipStream_t st);
 // packed codes -> bf16 weights (Z == nullptr: symmetric codes)

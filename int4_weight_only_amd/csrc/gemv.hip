@@ -633,20 +633,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_decode32(const uint16_t* __rest
 
 namespace {
 
-int cu_count() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        v <= 0)
-      v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 template <int KM, int T, bool ZP, bool TL, int XM>
 hipError_t run_decode16_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, uint16_t* Y, int64_t M, int64_t N, int64_t K,

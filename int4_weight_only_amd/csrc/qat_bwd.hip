@@ -120,32 +120,38 @@ hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t*
 // permutation for A and B, which leaves each dot product's terms unchanged;
 // the fp32 additions run step by step, MFMA j in order.  Rows past M or N
 // and k past K read zero.  K % 8 == 0 (16-byte row pieces).
-namespace {
-constexpr int kNtBM = 128, kNtBN = 256, kNtK = 64, kNtStages = 3;
-constexpr int kNtXA = kNtBM / 8 / 4;    // 1 KB loads per A stage per wave
-constexpr int kNtXB = kNtBN / 8 / 4;    // ... per B stage per wave
-}  // namespace
-
-__global__ __launch_bounds__(256, 1) void k_bf16_gemm_nt(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ B,
-                                                         uint16_t* __restrict__ C, int M, int N,
-                                                         int K) {
+// BM rows of A per workgroup, NWV waves as (BM / 128) x (NWV / (BM / 128))
+// waves of 128 A rows x 64 B rows each, NST LDS stages.
+template <int BM, int NWV, int NST>
+__global__ __launch_bounds__(NWV * 64, 1) void k_bf16_gemm_nt(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B,
+                                                              uint16_t* __restrict__ C, int M,
+                                                              int N, int K) {
+  constexpr int KS = 64;                 // K per step
+  constexpr int WA = BM / 128;           // waves along A
+  constexpr int WB = NWV / WA;           // waves along B
+  constexpr int BN = 64 * WB;
+  constexpr int XA = BM / 8 / NWV;       // 1 KB loads per A stage per wave
+  constexpr int XB = BN / 8 / NWV;       // ... per B stage per wave
+  static_assert(NST == 2 || NST == 3, "stages");
+  static_assert(XA * NWV * 8 == BM && XB * NWV * 8 == BN, "tile shape");
   // separately declared stages: each DMA target and each operand read names
   // one object
-  __shared__ __attribute__((aligned(16))) uint16_t as0[kNtBM * kNtK];
-  __shared__ __attribute__((aligned(16))) uint16_t as1[kNtBM * kNtK];
-  __shared__ __attribute__((aligned(16))) uint16_t as2[kNtBM * kNtK];
-  __shared__ __attribute__((aligned(16))) uint16_t bs0[kNtBN * kNtK];
-  __shared__ __attribute__((aligned(16))) uint16_t bs1[kNtBN * kNtK];
-  __shared__ __attribute__((aligned(16))) uint16_t bs2[kNtBN * kNtK];
+  __shared__ __attribute__((aligned(16))) uint16_t as0[BM * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t as1[BM * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t as2[NST > 2 ? BM * KS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t bs0[BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t bs1[BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[NST > 2 ? BN * KS : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wa = wave / WB, wb = wave % WB;
   const int l32 = lane & 31, h = lane >> 5;
   // tile order: the 1-D grid is dispatched round-robin over the 8 XCDs;
   // XCD x walks the contiguous tile range [x per, (x + 1) per) in groups of
   // 8 A row-blocks, so co-running workgroups share rows in its L2
-  const int mt = (M + kNtBM - 1) / kNtBM, nt = (N + kNtBN - 1) / kNtBN;
+  const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   const int tiles = mt * nt;
   const int per = (tiles + 7) / 8;
   const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -153,52 +159,46 @@ __global__ __launch_bounds__(256, 1) void k_bf16_gemm_nt(const uint16_t* __restr
   const int group = t / (8 * nt);
   const int gm = min(8, mt - group * 8);
   const int in_group = t - group * (8 * nt);
-  const int m0 = (group * 8 + in_group % gm) * kNtBM;
-  const int n0 = (in_group / gm) * kNtBN;
+  const int m0 = (group * 8 + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
 
   const __amdgpu_buffer_rsrc_t ar = rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
-  // Load i of this wave fills stage rows 8 (wave X + i) .. + 7: lane l
-  // writes the 16 bytes at slot l, row r = 8 I + l / 8, stored piece l % 8,
-  // which holds the row's piece (l % 8) ^ ((r / 2) % 8).  Byte offset of the
-  // lane's piece at step 0, or OOB for rows past the end.
-  auto row_off = [&](int first, int lim, int i) {
-    const int r = 8 * i + (lane >> 3);
+  // Load I of a stage fills stage rows 8 I .. 8 I + 7: lane l writes the 16
+  // bytes at slot l, row r = 8 I + l / 8, stored piece l % 8, which holds
+  // the row's piece (l % 8) ^ ((r / 2) % 8).  Byte offset of the lane's
+  // piece at step 0 (OOB for rows past the end) and its k within a step.
+  auto row_off = [&](int first, int lim, int I) {
+    const int r = 8 * I + (lane >> 3);
     const int pg = (lane & 7) ^ ((r >> 1) & 7);
     const int row = first + r;
     return row < lim ? ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)pg) * 2u : kOOB;
   };
-  uint32_t aoff[kNtXA], boff[kNtXB];
-  int acol[kNtXA], bcol[kNtXB];   // k of the lane's piece within a step
+  auto piece_k = [&](int I) { return 8 * ((lane & 7) ^ (((8 * I + (lane >> 3)) >> 1) & 7)); };
+  uint32_t aoff[XA], boff[XB];
 #pragma unroll
-  for (int i = 0; i < kNtXA; ++i) {
-    const int I = wave * kNtXA + i;
-    aoff[i] = row_off(m0, M, I);
-    acol[i] = 8 * ((lane & 7) ^ (((8 * I + (lane >> 3)) >> 1) & 7));
-  }
+  for (int i = 0; i < XA; ++i) aoff[i] = row_off(m0, M, wave * XA + i);
 #pragma unroll
-  for (int i = 0; i < kNtXB; ++i) {
-    const int I = wave * kNtXB + i;
-    boff[i] = row_off(n0, N, I);
-    bcol[i] = 8 * ((lane & 7) ^ (((8 * I + (lane >> 3)) >> 1) & 7));
-  }
+  for (int i = 0; i < XB; ++i) boff[i] = row_off(n0, N, wave * XB + i);
   auto load_stage = [&](int step, uint16_t* sa, uint16_t* sb) __attribute__((always_inline)) {
-    const int k0 = step * kNtK;
+    const int k0 = step * KS;
 #pragma unroll
-    for (int i = 0; i < kNtXA; ++i) {
-      const uint32_t off =
-          (aoff[i] != kOOB && k0 + acol[i] < K) ? aoff[i] + (uint32_t)k0 * 2u : kOOB;
+    for (int i = 0; i < XA; ++i) {
+      const uint32_t off = (aoff[i] != kOOB && k0 + piece_k(wave * XA + i) < K)
+                               ? aoff[i] + (uint32_t)k0 * 2u
+                               : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ar, (__attribute__((address_space(3))) void*)(sa + (wave * kNtXA + i) * 512), 16, off,
-          0, 0, 0);
+          ar, (__attribute__((address_space(3))) void*)(sa + (wave * XA + i) * 512), 16, off, 0,
+          0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kNtXB; ++i) {
-      const uint32_t off =
-          (boff[i] != kOOB && k0 + bcol[i] < K) ? boff[i] + (uint32_t)k0 * 2u : kOOB;
+    for (int i = 0; i < XB; ++i) {
+      const uint32_t off = (boff[i] != kOOB && k0 + piece_k(wave * XB + i) < K)
+                               ? boff[i] + (uint32_t)k0 * 2u
+                               : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          br, (__attribute__((address_space(3))) void*)(sb + (wave * kNtXB + i) * 512), 16, off,
-          0, 0, 0);
+          br, (__attribute__((address_space(3))) void*)(sb + (wave * XB + i) * 512), 16, off, 0,
+          0, 0);
     }
   };
 
@@ -210,30 +210,30 @@ __global__ __launch_bounds__(256, 1) void k_bf16_gemm_nt(const uint16_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ms][ns][v] = 0.0f;
 
-  const int nsteps = (K + kNtK - 1) / kNtK;
+  const int nsteps = (K + KS - 1) / KS;
   // One step: wait until this wave's loads of this step's stage have landed
-  // (the next stage's loads may stay in flight), a bare s_barrier so that
+  // (the later stages' loads may stay in flight), a bare s_barrier so that
   // every wave's part is visible and every wave is done with the stage the
-  // new loads overwrite, start the stage two steps ahead, multiply.
+  // new loads overwrite, start the stage NST - 1 steps ahead, multiply.
   auto step_body = [&](int step, const uint16_t* sa, const uint16_t* sb, uint16_t* na,
                        uint16_t* nb) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kNtXA + kNtXB) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NST - 2) * (XA + XB)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    load_stage(step + 2, na, nb);   // past K: reads zero
+    load_stage(step + NST - 1, na, nb);   // past K: reads zero
     if (step < nsteps) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x4 a[4], b[2];
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
-          const int R = ms * 32 + l32;
-          a[ms] = *(const u32x4*)(sa + R * kNtK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+          const int R = wa * 128 + ms * 32 + l32;
+          a[ms] = *(const u32x4*)(sa + R * KS + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
         }
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-          const int R = wave * 64 + ns * 32 + l32;
-          b[ns] = *(const u32x4*)(sb + R * kNtK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+          const int R = wb * 64 + ns * 32 + l32;
+          b[ns] = *(const u32x4*)(sb + R * KS + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
         }
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms)
@@ -243,36 +243,59 @@ __global__ __launch_bounds__(256, 1) void k_bf16_gemm_nt(const uint16_t* __restr
     }
   };
   load_stage(0, as0, bs0);
-  load_stage(1, as1, bs1);
-  for (int step = 0; step < nsteps; step += kNtStages) {
-    step_body(step + 0, as0, bs0, as2, bs2);
-    step_body(step + 1, as1, bs1, as0, bs0);
-    step_body(step + 2, as2, bs2, as1, bs1);
+  if constexpr (NST == 3) {
+    load_stage(1, as1, bs1);
+    for (int step = 0; step < nsteps; step += 3) {
+      step_body(step + 0, as0, bs0, as2, bs2);
+      step_body(step + 1, as1, bs1, as0, bs0);
+      step_body(step + 2, as2, bs2, as1, bs1);
+    }
+  } else {
+    for (int step = 0; step < nsteps; step += 2) {
+      step_body(step + 0, as0, bs0, as1, bs1);
+      step_body(step + 1, as1, bs1, as0, bs0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end drained
 
   // lane holds D[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
 #pragma unroll
   for (int ns = 0; ns < 2; ++ns) {
-    const int n = n0 + wave * 64 + ns * 32 + l32;
+    const int n = n0 + wb * 64 + ns * 32 + l32;
     if (n >= N) continue;
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int m = m0 + wa * 128 + ms * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         if (m < M) C[(int64_t)m * N + n] = to_bf16(acc[ms][ns][v]);
       }
   }
 }
 
+namespace {
+template <int BM, int NWV, int NST>
+hipError_t launch_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N,
+                     int64_t K, hipStream_t st) {
+  constexpr int BN = 64 * (NWV / (BM / 128));
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t blocks = (tiles + 7) / 8 * 8;   // whole rounds over the 8 XCDs
+  hipLaunchKernelGGL((k_bf16_gemm_nt<BM, NWV, NST>), dim3((unsigned)blocks), dim3(NWV * 64), 0,
+                     st, A, B, C, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+}  // namespace
+
+// 256 x 256 tiles of 8 waves (two per SIMD, two stages) when they fill
+// every CU at least once: 440 -> 382 us on dY [4096, 14336] x W'^T
+// [4096, 14336]; smaller products keep the 128 x 256 tile of 4 waves
+// (three stages), which spreads them over more CUs.  Both sum each output
+// in the same order, so the choice does not change a bit.
 hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
                                int64_t N, int64_t K, hipStream_t st) {
-  const int64_t tiles = ((M + kNtBM - 1) / kNtBM) * ((N + kNtBN - 1) / kNtBN);
-  const int64_t blocks = (tiles + 7) / 8 * 8;   // whole rounds over the 8 XCDs
-  hipLaunchKernelGGL(k_bf16_gemm_nt, dim3((unsigned)blocks), dim3(256), 0, st, A, B, C, (int)M,
-                     (int)N, (int)K);
-  return hipGetLastError();
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= cu_count()) return launch_nt<256, 8, 2>(A, B, C, M, N, K, st);
+  return launch_nt<128, 4, 3>(A, B, C, M, N, K, st);
 }
 
 }  // namespace w4
