@@ -319,6 +319,23 @@ def bench_quant(w4, synth, torch, iters, timer):
         "dequant_t_GB/s": round(qp_bytes / (t_dq * 1e-3) / 1e9, 1),
         "gemm_nt_us": round(t_mm * 1e3, 1), "gemm_nt_TFLOP/s": round(tf, 1),
         "gemm_nt_frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
+    # and its weight gradient dW = dY^T X: both operands transposed (the
+    # token dimension contiguous), then the same product
+    X = synth.activations(M, K, wl["seed"], device=dev)
+    dYT = torch.empty((N, M), dtype=torch.bfloat16, device=dev)
+    XT = torch.empty((K, M), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+
+    def weight_grad(i):
+        w4.w4_bf16_transpose(dY, M, out=dYT)
+        w4.w4_bf16_transpose(X, M, out=XT)
+        w4.w4_bf16_gemm_nt(dYT, XT, out=dW)
+    timer.settle(weight_grad, SETTLE_MS / 3)
+    t_wg = timer.run(weight_grad, iters) / iters
+    tf = gemm_flops(N, K, M) / (t_wg * 1e-3) / 1e12
+    out["qat_weight_gradient"] = {"M": M, "N": N, "K": K, "us": round(t_wg * 1e3, 1),
+                                  "TFLOP/s": round(tf, 1),
+                                  "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
     return out
 
 

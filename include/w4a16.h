@@ -290,6 +290,18 @@ int w4_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M
                     int64_t N, int64_t K, void* stream);
 
 /*
+ * w4_bf16_transpose -- AT = A^T with zero rows appended ([RL] §2.1: the QAT
+ * weight gradient dW = dY^T X is w4_bf16_gemm_nt(dY^T, X^T), whose operands
+ * need their shared dimension contiguous and a multiple of 8):
+ *   AT[c, r] = A[r, c]  (r < R),   AT[c, r] = 0  (R <= r < RP)
+ * A bf16 [R, C], AT bf16 [C, RP] output, both 2-byte aligned and not
+ * overlapping.  RP >= R (W4_ERR_SHAPE otherwise); C == 0 or RP == 0 is a
+ * no-op.  Bit-exact (a copy).
+ */
+int w4_bf16_transpose(const uint16_t* A, int64_t R, int64_t C, int64_t RP, uint16_t* AT,
+                      void* stream);
+
+/*
  * w4_pick_block_size -- alignment block size from the token count and the
  * expert count ([TAG] [35]):  B = min(64, max(16, next_pow2(ceil(T*k/E)))).
  * Returns 0 if T < 0, k < 1 or E < 1.

@@ -26,7 +26,7 @@ from . import _lib
 
 __all__ = [
     "w4_quantize_pack", "w4_fake_quant", "w4_quantize_pack_asym", "w4_fake_quant_asym",
-    "w4_dequant", "w4_dequant_asym", "w4_dequant_t", "w4_bf16_gemm_nt",
+    "w4_dequant", "w4_dequant_asym", "w4_dequant_t", "w4_bf16_gemm_nt", "w4_bf16_transpose",
     "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
@@ -196,6 +196,25 @@ def w4_dequant_t(Wq, S, Z=None, out=None):
     lib = _lib.load()
     _lib.check("w4_dequant_t", lib.w4_dequant_t(_ptr(Wq), _ptr(S), _ptr(Z), N, K, _ptr(out),
                                                 _stream(Wq)))
+    return out
+
+
+def w4_bf16_transpose(A, rows_padded=None, out=None):
+    """A bf16 [R, C] -> A^T [C, RP] with RP = rows_padded (>= R, default R)
+    and zero columns R .. RP - 1."""
+    _need(A, "A", torch.bfloat16, 2)
+    R, C = A.shape
+    RP = R if rows_padded is None else int(rows_padded)
+    if RP < R:
+        raise ValueError("rows_padded must be >= the rows of A")
+    if out is None:
+        out = torch.empty((C, RP), dtype=torch.bfloat16, device=A.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != C * RP:
+        raise ValueError(f"out must hold [{C}, {RP}]")
+    lib = _lib.load()
+    _lib.check("w4_bf16_transpose", lib.w4_bf16_transpose(_ptr(A), R, C, RP, _ptr(out),
+                                                          _stream(A)))
     return out
 
 

@@ -45,6 +45,7 @@ SIGNATURES = {
     "w4_repacked_words": (_i64, [_i64, _i64]),
     "w4_repack": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p]),
     "w4_restore": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p]),
+    "w4_bf16_transpose": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p]),
     "w4_repacked_group_elems": (_i64, [_i64, _i64]),
     "w4_repack_groups": (ctypes.c_int, [_p, _i32, _i64, _i64, _i64, _p, _p]),
     "w4_restore_groups": (ctypes.c_int, [_p, _i32, _i64, _i64, _i64, _p, _p]),

@@ -308,6 +308,21 @@ int w4_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M
   return hip_status(w4::launch_bf16_gemm_nt(A, B, C, M, N, K, as_stream(stream)));
 }
 
+int w4_bf16_transpose(const uint16_t* A, int64_t R, int64_t C, int64_t RP, uint16_t* AT,
+                      void* stream) {
+  if (R < 0 || C < 0 || RP < R) return W4_ERR_SHAPE;
+  if (RP == 0 || C == 0) return W4_OK;
+  if (!AT || (R > 0 && !A)) return W4_ERR_NULL;
+  if (!aligned(A, 2) || !aligned(AT, 2)) return W4_ERR_MISALIGNED;
+  if (R > ((int64_t)1 << 40) / (C > 0 ? C : 1) || RP > ((int64_t)1 << 40) / C ||
+      ((RP + 63) / 64) * ((C + 63) / 64) >= kMaxI32)
+    return W4_ERR_UNSUPPORTED;
+  const uintptr_t a = (uintptr_t)A, b = (uintptr_t)AT;
+  const uintptr_t la = (uintptr_t)(R * C) * 2u, lb = (uintptr_t)(RP * C) * 2u;
+  if (R > 0 && a < b + lb && b < a + la) return W4_ERR_UNSUPPORTED;   // overlapping buffers
+  return hip_status(w4::launch_transpose_bf16(A, AT, R, C, RP, as_stream(stream)));
+}
+
 int32_t w4_pick_block_size(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   const int64_t mean = (T * k + E - 1) / E;

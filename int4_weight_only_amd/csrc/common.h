@@ -182,6 +182,9 @@ hipError_t launch_relayout_groups(const void* src, void* dst, int elem_bytes, in
 // QAT input gradient: transposed dequant W'^T [K, N], and a bf16 NT GEMM
 hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t* Z, uint16_t* WT,
                             int64_t N, int64_t K, hipStream_t st);
+// AT [C, RP] = A [R, C]^T, rows R .. RP - 1 of AT's columns zero
+hipError_t launch_transpose_bf16(const uint16_t* A, uint16_t* AT, int64_t R, int64_t C,
+                                 int64_t RP, hipStream_t st);
 hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
                                int64_t N, int64_t K, hipStream_t st);
 // products on either layout (Z == nullptr: symmetric codes)

@@ -1,4 +1,4 @@
-// Kernels of the QAT linear layer's input gradient.
+// Kernels of the QAT linear layer's gradients.
 //
 // Method: "INT4 QAT end-to-end for RL" §2.1 -- the forward multiplies the
 // fake-quantized weight W' = bf16(q s) and the straight-through estimator
@@ -102,6 +102,67 @@ hipError_t launch_dequant_t(const int32_t* Wq, const uint16_t* S, const uint8_t*
   else
     hipLaunchKernelGGL(k_dequant_t<false>, dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint32_t*)Wq, S, nullptr, WT, N, K);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ transpose --
+// AT[c, r] = A[r, c] for r < R, zero for R <= r < RP (A [R, C], AT [C, RP]).
+// A workgroup of 256 threads moves a 64 x 64 tile through LDS (rows padded
+// by 8 elements off the bank period).  VEC (C and RP multiples of 8, both
+// buffers 16-byte aligned): 16-byte loads along A's rows and 16-byte stores
+// along AT's rows; otherwise 2-byte accesses.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ A,
+                                                        uint16_t* __restrict__ AT, int64_t R,
+                                                        int64_t C, int64_t RP) {
+  constexpr int TS = 64, PAD = 8;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TS][TS + PAD];
+  const int tid = threadIdx.x;
+  const int64_t ntc = (C + TS - 1) / TS;
+  const int64_t r0 = (int64_t)(blockIdx.x / ntc) * TS;
+  const int64_t c0 = (int64_t)(blockIdx.x % ntc) * TS;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 32 * p + tid / 8, c = 8 * (tid % 8);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r0 + r < R && c0 + c < C) v = *(const u32x4*)(A + (r0 + r) * C + c0 + c);
+      *(u32x4*)&tile[r][c] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = 32 * p + tid / 8, r = 8 * (tid % 8);
+      if (c0 + c >= C || r0 + r >= RP) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)tile[r + 2 * i][c] | ((uint32_t)tile[r + 2 * i + 1][c] << 16);
+      *(u32x4*)(AT + (c0 + c) * RP + r0 + r) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  } else {
+    for (int e = tid; e < TS * TS; e += 256) {
+      const int r = e / TS, c = e % TS;
+      tile[r][c] = (r0 + r < R && c0 + c < C) ? A[(r0 + r) * C + c0 + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int e = tid; e < TS * TS; e += 256) {
+      const int c = e / TS, r = e % TS;
+      if (c0 + c < C && r0 + r < RP) AT[(c0 + c) * RP + r0 + r] = tile[r][c];
+    }
+  }
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* A, uint16_t* AT, int64_t R, int64_t C,
+                                 int64_t RP, hipStream_t st) {
+  const int64_t blocks = ((RP + 63) / 64) * ((C + 63) / 64);
+  const bool vec = C % 8 == 0 && RP % 8 == 0 && (uintptr_t)A % 16 == 0 && (uintptr_t)AT % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(k_transpose_bf16<true>, dim3((unsigned)blocks), dim3(256), 0, st, A, AT, R,
+                       C, RP);
+  else
+    hipLaunchKernelGGL(k_transpose_bf16<false>, dim3((unsigned)blocks), dim3(256), 0, st, A, AT,
+                       R, C, RP);
   return hipGetLastError();
 }
 

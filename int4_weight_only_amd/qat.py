@@ -24,13 +24,15 @@ W_fq).  The backward is the straight-through estimator.  The input
 gradient dX = dY * W_fq runs in the library: ``w4_dequant_t`` writes W_fq^T
 from the packed codes the forward made (bit-exact with fake quant) and
 ``w4_bf16_gemm_nt`` multiplies (N % 8 == 0).  The weight gradient
-dW = dY^T * X involves no quantized operand: it is a plain bf16 product of
-two activations and stays torch's matrix product.
+dW = dY^T * X runs in the library too: ``w4_bf16_transpose`` writes dY^T and
+X^T with the token dimension padded to a multiple of 8 (zeros), and
+``w4_bf16_gemm_nt`` contracts over it.
 """
 
 import torch
 
-from . import w4_bf16_gemm_nt, w4_dequant_t, w4_fake_quant, w4_quantize_pack, w4a16_gemm
+from . import (w4_bf16_gemm_nt, w4_bf16_transpose, w4_dequant_t, w4_fake_quant, w4_quantize_pack,
+               w4a16_gemm)
 
 __all__ = ["FakeInt4STE", "fake_quant_ste", "Int4QATLinear", "qat_linear"]
 
@@ -81,7 +83,8 @@ class Int4QATLinear(torch.autograd.Function):
                 raise ValueError(f"the QAT input gradient needs N % 8 == 0 (N = {N})")
             dX = w4_bf16_gemm_nt(dY, w4_dequant_t(Wq, S)).reshape(ctx.x_shape)
         if ctx.needs_input_grad[1]:
-            dW = torch.mm(dY.t().contiguous(), X2)
+            Mp = (dY.shape[0] + 7) // 8 * 8
+            dW = w4_bf16_gemm_nt(w4_bf16_transpose(dY, Mp), w4_bf16_transpose(X2, Mp))
         return dX, dW
 
 

@@ -384,6 +384,19 @@ def test_repack_restore_groups_validation(lib):
         assert f(A16, 2, 1, 4, 32, A16, None) == UNSUPPORTED    # overlapping buffers
 
 
+def test_bf16_transpose_validation(lib):
+    f = lib.w4_bf16_transpose
+    assert f(A16, -1, 8, 8, D16, None) == SHAPE
+    assert f(A16, 8, -1, 8, D16, None) == SHAPE
+    assert f(A16, 8, 8, 7, D16, None) == SHAPE          # padded rows below the rows
+    assert f(None, 8, 0, 8, None, None) == OK           # no columns: no-op
+    assert f(None, 0, 8, 0, None, None) == OK           # no rows at all: no-op
+    assert f(None, 8, 8, 8, D16, None) == NULL
+    assert f(A16, 8, 8, 8, None, None) == NULL
+    assert f(A1, 8, 8, 8, D16, None) == MISALIGNED
+    assert f(A16, 8, 8, 8, A16, None) == UNSUPPORTED    # overlapping buffers
+
+
 def test_gemm_tiled_validation(lib):
     f = lib.w4a16_gemm_tiled
     assert f(A16, A16, A2, None, A4, 4, 8, 33, None) == SHAPE

@@ -87,12 +87,14 @@ def test_qat_linear_forward_matches_oracle(shape, N, K):
     assert ok, (a, r)
 
 
-def test_qat_linear_backward_is_straight_through():
+@pytest.mark.parametrize("M", [40, 37, 300])
+def test_qat_linear_backward_is_straight_through(M):
     """dX = dY * fake_quant(W) and dW = dY^T * X (the estimator passes the
-    gradient of the quantized weight to the master weight)."""
+    gradient of the quantized weight to the master weight); M = 37 pads the
+    token dimension of the weight gradient's transposed operands."""
     from int4_weight_only_amd.qat import qat_linear
-    say("qat_linear backward")
-    M, N, K = 40, 64, 128
+    say(f"qat_linear backward M={M}")
+    N, K = 64, 128
     Wb = synth.bits(synth.weights(N, K, 41))
     Xb = synth.bits(synth.activations(M, K, 42))
     Gb = synth.bits(synth.activations(M, N, 43))
@@ -147,6 +149,28 @@ def test_bf16_gemm_nt_matches_oracle(M, N, K):
     ref = bf16.to_f32(Ab).astype(np.float64) @ bf16.to_f32(Bb).astype(np.float64).T
     ok, a, r = gemm.within_tolerance(C, ref, ATOL, RTOL)
     assert ok, (a, r)
+
+
+@pytest.mark.parametrize("R,C,RP,offset", [(1, 1, 1, 0), (37, 64, 40, 0), (64, 64, 64, 0),
+                                          (130, 200, 136, 0), (4096, 4096, 4096, 0),
+                                          (45, 19, 45, 0), (33, 40, 48, 1), (0, 16, 8, 0)])
+def test_bf16_transpose_bit_exact(R, C, RP, offset):
+    """AT[c, r] = A[r, c], zero columns r >= R; 16-byte paths (C and RP
+    multiples of 8, aligned buffers) and the element-wise path (ragged C, or
+    buffers one element off)."""
+    import int4_weight_only_amd as w4
+    say(f"transpose R={R} C={C} RP={RP} offset={offset}")
+    Ab = synth.bits(synth.activations(max(R, 1), C, 62))[:R]
+    flat = torch.zeros(R * C + offset, dtype=torch.bfloat16, device=dev())
+    A = flat[offset:].view(R, C)
+    if R:
+        A.copy_(up_bits(np.ascontiguousarray(Ab)).view(R, C))
+    out = torch.full((C * RP + offset,), 3.0, dtype=torch.bfloat16, device=dev())
+    w4.w4_bf16_transpose(A, RP, out=out[offset:])
+    got = down_bits(out[offset:]).reshape(C, RP)
+    ref = np.zeros((C, RP), dtype=np.uint16)
+    ref[:, :R] = np.asarray(Ab).reshape(R, C).T
+    np.testing.assert_array_equal(got, ref)
 
 
 def test_qat_linear_input_gradient_needs_n_multiple_of_8():
