@@ -105,6 +105,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
   constexpr int kU = kWS > kXS ? kWS : kXS;   // K-loop unroll: stage and set named statically
   constexpr bool kRunSlots = MOE && BM <= 32;  // grouped product: slots index runs
   constexpr bool kNullPast = SA && kGroupW;      // loads past the last step read the empty buffer
+  constexpr bool kPipe = !MOE;                   // dequant of slice j + 1 under slice j's MFMAs
   static_assert(kU % kXS == 0 && kU % kWS == 0, "unroll");
   static_assert(BM % 32 == 0 && WN % 32 == 0 && XI % NW == 0 && BM <= NT, "tile shape");
 
@@ -546,15 +547,61 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
             d[ns] = deq_scale(sc);
           }
         }
+        auto word = [&](int ns, int j) __attribute__((always_inline)) {
+          return j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z : wreg[ns].w;
+        };
+        if constexpr (kPipe) {
+          // Software pipeline: slice j's MFMAs run while the next slice's
+          // words are dequantized, one MFMA issued between every four VALU
+          // instructions (a 32x32x16 MFMA occupies the matrix unit for
+          // about as long as four wave64 VALU issues take twice over).
+          // The activation operands of slice j + 1 are read from LDS
+          // during slice j as well (slice 0's at the top of the step).
+          auto read_a = [&](int j, u32x4 (&a)[MSE]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ms = 0; ms < MSE; ++ms) {
+              const int R = ms * 32 + l32;
+              a[ms] = *(const u32x4*)(st + R * kStepK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+            }
+          };
+          u32x4 bcur[NS], bnext[NS], acur[MSE], anext[MSE];
+          read_a(0, acur);
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) bcur[ns] = dequant8<ZP>(word(ns, 0), d[ns]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < 3) {
+              read_a(j + 1, anext);
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) bnext[ns] = dequant8<ZP>(word(ns, j + 1), d[ns]);
+            }
+#pragma unroll
+            for (int ms = 0; ms < MSE; ++ms)
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(acur[ms], bcur[ns], acc[ms][ns]);
+            if (j < 3) {
+              __builtin_amdgcn_sched_group_barrier(0x100, MSE, 0);   // the next operand reads
+              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+              for (int i = 0; i < MSE * NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) bcur[ns] = bnext[ns];
+#pragma unroll
+            for (int ms = 0; ms < MSE; ++ms) acur[ms] = anext[ms];
+          }
+        } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // word j of each code register feeds MFMA slice j
           u32x4 bop[NS];
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            bop[ns] = dequant8<ZP>(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
-                                                                                : wreg[ns].w,
-                               d[ns]);
+          for (int ns = 0; ns < NS; ++ns) bop[ns] = dequant8<ZP>(word(ns, j), d[ns]);
           u32x4 a[MSE];
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms) {
@@ -565,6 +612,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
           for (int ms = 0; ms < MSE; ++ms)
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
+        }
         }
       }
       if constexpr (kGroupW) {
