@@ -601,7 +601,10 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
           // word j of each code register feeds MFMA slice j
           u32x4 bop[NS];
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) bop[ns] = dequant8<ZP>(word(ns, j), d[ns]);
+          for (int ns = 0; ns < NS; ++ns)
+            bop[ns] = dequant8<ZP>(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
+                                                                                : wreg[ns].w,
+                               d[ns]);
           u32x4 a[MSE];
 #pragma unroll
           for (int ms = 0; ms < MSE; ++ms) {
