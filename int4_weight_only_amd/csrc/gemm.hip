@@ -553,10 +553,11 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
         if constexpr (kPipe) {
           // Software pipeline: slice j's MFMAs run while the next slice's
           // words are dequantized, one MFMA issued between every four VALU
-          // instructions (a 32x32x16 MFMA occupies the matrix unit for
-          // about as long as four wave64 VALU issues take twice over).
-          // The activation operands of slice j + 1 are read from LDS
-          // during slice j as well (slice 0's at the top of the step).
+          // instructions (a 32x32x16 MFMA holds the matrix unit for about
+          // eight wave64 VALU issue slots, so four leave room for the other
+          // wave on the SIMD).  The activation operands of slice j + 1 are
+          // read from LDS during slice j as well (slice 0's at the top of
+          // the step).
           auto read_a = [&](int j, u32x4 (&a)[MSE]) __attribute__((always_inline)) {
 #pragma unroll
             for (int ms = 0; ms < MSE; ++ms) {
@@ -597,25 +598,25 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
           }
         } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // word j of each code register feeds MFMA slice j
-          u32x4 bop[NS];
+          for (int j = 0; j < 4; ++j) {
+            // word j of each code register feeds MFMA slice j
+            u32x4 bop[NS];
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            bop[ns] = dequant8<ZP>(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y : j == 2 ? wreg[ns].z
-                                                                                : wreg[ns].w,
-                               d[ns]);
-          u32x4 a[MSE];
+            for (int ns = 0; ns < NS; ++ns)
+              bop[ns] = dequant8<ZP>(j == 0 ? wreg[ns].x : j == 1 ? wreg[ns].y
+                                                       : j == 2 ? wreg[ns].z : wreg[ns].w,
+                                     d[ns]);
+            u32x4 a[MSE];
 #pragma unroll
-          for (int ms = 0; ms < MSE; ++ms) {
-            const int R = ms * 32 + l32;
-            a[ms] = *(const u32x4*)(st + R * kStepK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+            for (int ms = 0; ms < MSE; ++ms) {
+              const int R = ms * 32 + l32;
+              a[ms] = *(const u32x4*)(st + R * kStepK + 8 * ((4 * h + j) ^ ((R >> 1) & 7)));
+            }
+#pragma unroll
+            for (int ms = 0; ms < MSE; ++ms)
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
           }
-#pragma unroll
-          for (int ms = 0; ms < MSE; ++ms)
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma32(a[ms], bop[ns], acc[ms][ns]);
-        }
         }
       }
       if constexpr (kGroupW) {
