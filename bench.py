@@ -454,6 +454,10 @@ def bench_moe_layer(name, w4, wmoe, synth, torch, iters, timer, block_sweep=True
         X, gu_t, buf.sorted_token_ids, buf.expert_ids, buf.ntpp, T, k, B, k, out=buf.A)
     stages["down_kernel_order"] = lambda: wmoe.grouped_gemm(
         buf.A, dn_t, buf.sorted_token_ids, buf.expert_ids, buf.ntpp, T, k, B, 1, out=buf.H2)
+    # the down product with the top-k combine fused (w4a16_moe_gemm_combine),
+    # against down_kernel_order + combine
+    stages["down_combine_kernel_order"] = lambda: wmoe.down_combine(
+        buf.A, dn_t, buf.sorted_token_ids, buf.expert_ids, buf.ntpp, ids, tw, B, buf)
 
     def layer_t(i):
         for sname in ("route", "align", "gate_up_swiglu_kernel_order", "down_kernel_order",

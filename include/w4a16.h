@@ -436,6 +436,52 @@ int w4_moe_sum(const uint16_t* H2, const float* topk_weights, uint16_t* Out,
 int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
                  int32_t* topk_ids, float* topk_weights, void* stream);
 
+/*
+ * w4_moe_combine_workspace_words -- int32 words of the arrival counters
+ * that w4a16_moe_gemm_combine needs for T tokens, top-k, E experts, N
+ * output columns and block size B: one per token and weight-row tile of the
+ * grouped product (T * ceil(N / 128) or T * ceil(N / 256), as the tile the
+ * product picks).  -1 on invalid arguments.
+ */
+int64_t w4_moe_combine_workspace_words(int64_t T, int32_t k, int32_t E, int64_t N,
+                                       int32_t B);
+
+/*
+ * w4a16_moe_gemm_combine -- the grouped down product with the top-k
+ * combine fused ([RL] §4, deep fusion of the MoE operators; [TAG] [35]).
+ * In one launch:
+ *   H2 = w4a16_moe_gemm(A, Wq, S, ..., x_row_div = 1, topk_weights = NULL)
+ *   Out[t, :] = bf16( sum over j = 0..k-1 in order, fp32 fused multiply-add,
+ *                     of topk_weights[t, j] * H2[t*k + j, :] )
+ * -- bit for bit what w4a16_moe_gemm followed by w4_moe_sum give.  Pairs
+ * whose topk_ids entry lies outside [0, E) take no part in the sum; a token
+ * none of whose pairs lies in [0, E) is not written.
+ * A bf16 [T*k, K] (the SwiGLU output); Wq / S the experts' codes and scales
+ * as w4a16_moe_gemm (tiled == 0) or in the kernel-order layouts of
+ * w4_repack / w4_repack_groups (tiled != 0); sorted_token_ids, expert_ids,
+ * num_tokens_post_padded from moe_align_block_size over topk_ids int32
+ * [T, k]; topk_weights float32 [T, k]; H2 bf16 [T*k, N] (written: the
+ * unweighted rows); Out bf16 [T, N].
+ * workspace: int32 [w4_moe_combine_workspace_words(T, k, E, N, B)],
+ * caller-owned device memory, 4-byte aligned, all zero before the call;
+ * the call leaves it all zero.  Each workgroup counts its rows' tokens in
+ * once its rows are stored, and the one that completes a token's count
+ * writes that token's columns, so the result does not depend
+ * on the order in which workgroups run.  Calls that share a workspace must
+ * not overlap in time.  The rows of H2 are written and read back with
+ * agent-coherent accesses (through the L2 of each XCD), so no cache
+ * write-back or invalidate is needed between workgroups.  Limits and errors
+ * as w4a16_moe_gemm (symmetric codes), plus k <= 16 (W4_ERR_UNSUPPORTED)
+ * and NULL topk_ids / topk_weights / Out / workspace: W4_ERR_NULL.
+ */
+int w4a16_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                           const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded,
+                           const int32_t* topk_ids, const float* topk_weights,
+                           uint16_t* H2, uint16_t* Out, int64_t T, int32_t k,
+                           int32_t E, int64_t N, int64_t K, int32_t B, int32_t tiled,
+                           int32_t* workspace, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemm_asym", "w4_pick_block_size",
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
-    "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "library_path",
+    "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "w4_moe_combine_workspace_words",
+    "w4a16_moe_gemm_combine", "library_path",
     "w4_repacked_words", "w4_repack", "w4_restore", "w4_repacked_group_elems",
     "w4_repack_groups", "w4_restore_groups", "w4a16_gemm_tiled",
     "w4a16_moe_gemm_tiled", "w4a16_moe_gemm_swiglu_tiled",
@@ -675,3 +676,61 @@ def w4a16_moe_gemm_swiglu_tiled(X, Wt, St, N, sorted_token_ids, expert_ids,
         _ptr(X), _ptr(Wt), _ptr(St), _ptr(Z), _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(out), T, k, E, I, K, B, x_row_div, _stream(X)))
     return out
+
+
+# ---------------------------------------------- down product + top-k combine --
+
+def w4_moe_combine_workspace_words(T, k, E, N, B):
+    """int32 arrival counters ``w4a16_moe_gemm_combine`` needs."""
+    n = int(_lib.load().w4_moe_combine_workspace_words(T, k, E, N, B))
+    if n < 0:
+        raise ValueError("invalid T, k, E, N or B")
+    return n
+
+
+def w4a16_moe_gemm_combine(A, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                           topk_ids, topk_weights, B, N=None, tiled=False, H2=None, out=None,
+                           workspace=None):
+    """The grouped down product with the top-k combine fused.
+
+    A bf16 [T*k, K]; canonical experts Wq [E, N, K/8], S [E, N, K/32], or
+    (``tiled``) kernel-order Wt / St with N given.  Returns (Out [T, N],
+    H2 [T*k, N]); ``workspace`` int32 [w4_moe_combine_workspace_words(...)]
+    holding zeros (allocated zeroed when omitted; every call leaves it zero).
+    """
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    if tiled:
+        if N is None:
+            raise ValueError("kernel-order experts need N")
+        E, K = _moe_tiled_args(A, Wq, S, None, N, T, k, 1)
+        for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                     (num_tokens_post_padded, "num_tokens_post_padded")):
+            _need(t, n, torch.int32)
+    else:
+        E, N, K = _moe_args(A, Wq, S, None, sorted_token_ids, expert_ids,
+                            num_tokens_post_padded, T, k, B, 1)
+    _need(topk_weights, "topk_weights", torch.float32)
+    if topk_weights.numel() != T * k:
+        raise ValueError("topk_weights must be [T, k]")
+    dev = A.device
+    if H2 is None:
+        H2 = torch.empty((T * k, N), dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    _need(H2, "H2", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    if H2.numel() != T * k * N or out.numel() != T * N:
+        raise ValueError("H2 must be [T*k, N] and out [T, N]")
+    words = w4_moe_combine_workspace_words(T, k, E, N, B)
+    if workspace is None:
+        workspace = torch.zeros(words, dtype=torch.int32, device=dev)
+    _need(workspace, "workspace", torch.int32)
+    if workspace.numel() < words:
+        raise ValueError(f"workspace needs {words} int32 words")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm_combine", lib.w4a16_moe_gemm_combine(
+        _ptr(A), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(topk_ids), _ptr(topk_weights), _ptr(H2), _ptr(out),
+        T, k, E, N, K, B, 1 if tiled else 0, _ptr(workspace), _stream(A)))
+    return out, H2

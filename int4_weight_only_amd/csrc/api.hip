@@ -361,11 +361,13 @@ namespace {
 
 // Shared validation and dispatch of the grouped products (Z == nullptr:
 // symmetric codes).  N is the weight rows per expert (2I with the SwiGLU).
-int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
-                     bool asym, const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                     const int32_t* num_tokens_post_padded, const float* topk_weights,
-                     uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
-                     int32_t B, int32_t x_row_div, bool swiglu, bool tiled, void* stream) {
+// Checks shared by the grouped products; W4_OK, or -1 for a valid call with
+// nothing to do (T == 0), or an error status.
+int moe_gemm_validate(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                      bool asym, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, const float* topk_weights,
+                      uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                      int32_t B, int32_t x_row_div, bool swiglu, bool tiled) {
   if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32 != 0 || B < 1) return W4_ERR_SHAPE;
   if (x_row_div != 1 && x_row_div != k) return W4_ERR_SHAPE;
   if (B > 1024 || E > 1024) return W4_ERR_UNSUPPORTED;
@@ -376,7 +378,7 @@ int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, co
   if (!fits_buffer((T * k / x_row_div) * K * 2) ||
       !fits_buffer(tiled ? w4::tiled_words(N, K) * 4 : N * (K / 2)))
     return W4_ERR_UNSUPPORTED;
-  if (T == 0) return W4_OK;
+  if (T == 0) return -1;
   if (!X || !Wq || !S || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !Y ||
       (asym && !Z))
     return W4_ERR_NULL;
@@ -385,6 +387,20 @@ int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, co
       !aligned(num_tokens_post_padded, 4) || !aligned(topk_weights, 4))
     return W4_ERR_MISALIGNED;
   if (w4::moe_gemm_workgroups(T, k, E, N, B, swiglu) >= kMaxI32) return W4_ERR_UNSUPPORTED;
+  return W4_OK;
+}
+
+// Shared validation and dispatch of the grouped products (Z == nullptr:
+// symmetric codes).  N is the weight rows per expert (2I with the SwiGLU).
+int moe_gemm_checked(const uint16_t* X, const int32_t* Wq, const uint16_t* S, const uint8_t* Z,
+                     bool asym, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_padded, const float* topk_weights,
+                     uint16_t* Y, int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                     int32_t B, int32_t x_row_div, bool swiglu, bool tiled, void* stream) {
+  const int v = moe_gemm_validate(X, Wq, S, Z, asym, sorted_token_ids, expert_ids,
+                                  num_tokens_post_padded, topk_weights, Y, T, k, E, N, K, B,
+                                  x_row_div, swiglu, tiled);
+  if (v != W4_OK) return v < 0 ? W4_OK : v;
   if (swiglu)
     return hip_status(w4::launch_moe_gemm_swiglu(X, Wq, S, asym ? Z : nullptr, sorted_token_ids,
                                                  expert_ids, num_tokens_post_padded, Y, T, k, E,
@@ -492,6 +508,32 @@ int w4_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* 
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
     return W4_ERR_MISALIGNED;
   return hip_status(w4::launch_route(logits, T, E, k, topk_ids, topk_weights, as_stream(stream)));
+}
+
+int64_t w4_moe_combine_workspace_words(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B) {
+  if (T < 0 || k < 1 || E < 1 || N < 1 || B < 1) return -1;
+  return w4::moe_combine_counters(T, k, E, N, B);
+}
+
+int w4a16_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                           const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, const int32_t* topk_ids,
+                           const float* topk_weights, uint16_t* H2, uint16_t* Out, int64_t T,
+                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B, int32_t tiled,
+                           int32_t* workspace, void* stream) {
+  const int v = moe_gemm_validate(A, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
+                                  num_tokens_post_padded, topk_weights, H2, T, k, E, N, K, B, 1,
+                                  false, tiled != 0);
+  if (v < 0) return W4_OK;
+  if (v != W4_OK) return v;
+  if (T * N >= ((int64_t)1 << 40) || k > 16) return W4_ERR_UNSUPPORTED;
+  if (!topk_ids || !topk_weights || !Out || !workspace) return W4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(Out, 2) || !aligned(workspace, 4))
+    return W4_ERR_MISALIGNED;
+  return hip_status(w4::launch_moe_gemm_combine(A, Wq, S, sorted_token_ids, expert_ids,
+                                                num_tokens_post_padded, topk_ids, topk_weights,
+                                                H2, Out, workspace, T, k, E, N, K, B, tiled != 0,
+                                                as_stream(stream)));
 }
 
 }  // extern "C"

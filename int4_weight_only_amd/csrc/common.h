@@ -161,6 +161,13 @@ hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const ui
 // Slots of the grouped GEMM, and its workgroups (N-tiles x slots, a 1-D grid).
 int64_t moe_gemm_slots(int64_t T, int32_t k, int32_t E, int32_t B);
 int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B, bool swiglu);
+hipError_t launch_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                                   const int32_t* sorted_ids, const int32_t* expert_ids,
+                                   const int32_t* ntpp, const int32_t* topk_ids,
+                                   const float* topk_w, uint16_t* H2, uint16_t* Out, int32_t* cnt,
+                                   int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                                   int32_t B, bool tiled, hipStream_t st);
+int64_t moe_combine_counters(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B);
 hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t B,
                         int64_t cap, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
                         hipStream_t st);

@@ -84,13 +84,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // in four back-to-back loads instead of across four steps, when L2 may have
 // dropped it) and four workgroups per CU keep weight bytes in flight, and
 // workgroups index runs rather than blocks.
-template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false, bool TL = false>
+// CMB (grouped down product only): the workgroup stores its rows of Y (the
+// unweighted bf16 products) with agent-coherent stores (written through the
+// XCD's L2), waits until they are done, and counts each row's token in on
+// cnt[token * ntn + tile_n] (one counter per token and weight-row tile,
+// device-scope atomics); the workgroup whose count completes a token (its
+// pairs routed to experts in [0, E) all stored) reads those rows back with
+// agent-coherent loads and writes Out[token, tile columns] = bf16(sum over j
+// in order of cw[t k + j] * Y[t k + j, column]) -- the same fp32 operations
+// in the same order as the separate combine -- and sets the counter back
+// to 0.  Coherent accesses replace an L2 write-back per workgroup and an L2
+// invalidate per completing workgroup, which measured 2.5x slower.  Pairs
+// whose expert lies outside [0, E) take no part.
+template <int BM, int WN, int NW, bool MOE, bool SA, bool SWI, bool ZP = false, bool TL = false,
+          bool CMB = false>
 __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k_gemm(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wq, const uint16_t* __restrict__ S,
     const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
     const int32_t* __restrict__ ntpp, const float* __restrict__ topk_w, int n_pairs, int B,
-    int x_row_div, int E) {
+    int x_row_div, int E, uint16_t* __restrict__ Out, int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ topk_ids, const float* __restrict__ cw, int topk) {
   constexpr int NT = NW * 64;
   constexpr int MS = BM / 32;          // 32-row MFMA tiles along M
   constexpr int NS = WN / 32;          // 32-col MFMA tiles along N per wave
@@ -170,6 +184,7 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
     tile_n = in_group / gm;
   }
   static_assert(!SWI || (MOE && NW == 4), "fused SwiGLU: grouped product, four waves");
+  static_assert(!CMB || (MOE && !SWI), "fused combine: grouped down product");
   const int n_base = SWI ? (wave >> 1) * (N >> 1) + tile_n * (2 * WN) + (wave & 1) * WN
                          : tile_n * (NW * WN) + wave * WN;
   const int G = K >> 5;
@@ -748,7 +763,110 @@ __global__ __launch_bounds__(NW * 64, BM >= 256 ? 1 : (BM <= 32 ? 4 : 2)) void k
               if (n < N) {
                 float y = acc[ms][ns][v];
                 if constexpr (MOE) y *= wgt;
-                Y[(int64_t)yr * N + n] = to_bf16(y);
+                if constexpr (CMB)
+                  __hip_atomic_store(&Y[(int64_t)yr * N + n], to_bf16(y), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+                else
+                  Y[(int64_t)yr * N + n] = to_bf16(y);
+              }
+            }
+          }
+        }
+        if constexpr (CMB) {
+          __shared__ int last_tok[BM];
+          __shared__ int n_last;
+          constexpr int kCols = NW * WN;                  // weight rows (output columns) of the tile
+          const int ntn = (N + kCols - 1) / kCols;
+          // every wave's coherent stores are done before any count goes out
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (tid == 0) n_last = 0;
+          __syncthreads();
+          if (tid < BM) {
+            const int f = orow[tid];
+            if (f >= 0) {
+              const int t = f / topk;
+              int need = 0;
+              for (int j = 0; j < topk; ++j) {
+                const int e = topk_ids[(int64_t)t * topk + j];
+                need += (e >= 0 && e < E) ? 1 : 0;
+              }
+              int32_t* c = cnt + (int64_t)t * ntn + tile_n;
+              const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+              if (prev == need - 1) {
+                __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_tok[atomicAdd(&n_last, 1)] = t;
+              }
+            }
+          }
+          __syncthreads();
+          const int nl = n_last;
+          if (nl > 0) {
+            const int col0 = tile_n * kCols;
+            constexpr int kMaxK = 16;
+            if ((N & 3) == 0 && (((uintptr_t)Out | (uintptr_t)Y) & 7) == 0) {
+              // four columns per item, items of all tokens spread over the
+              // workgroup, a pair's 8 bytes in one coherent load, every load
+              // of an item issued before its sums
+              constexpr int kG = kCols / 4;
+              const int items = nl * kG;
+              for (int it = tid; it < items; it += NT) {
+                const int i = it / kG;
+                const int n = col0 + 4 * (it - i * kG);
+                const int t = last_tok[i];
+                if (n < N) {
+                  uint64_t hv[kMaxK];
+                  float wv[kMaxK];
+                  uint32_t vm = 0;   // bit j: pair j routed to an expert
+#pragma unroll
+                  for (int j = 0; j < kMaxK; ++j) {
+                    hv[j] = 0;
+                    wv[j] = 0.0f;
+                    if (j < topk) {
+                      const int64_t f = (int64_t)t * topk + j;
+                      const int e = topk_ids[f];
+                      if (e >= 0 && e < E) {
+                        vm |= 1u << j;
+                        wv[j] = cw[f];
+                        hv[j] = __hip_atomic_load((const uint64_t*)&Y[f * N + n], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                      }
+                    }
+                  }
+                  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+                  for (int j = 0; j < kMaxK; ++j) {
+                    if ((vm >> j) & 1u) {
+                      const uint32_t lo = (uint32_t)hv[j], hi = (uint32_t)(hv[j] >> 32);
+                      a0 = __builtin_fmaf(wv[j], bf16_lo(lo), a0);
+                      a1 = __builtin_fmaf(wv[j], bf16_hi(lo), a1);
+                      a2 = __builtin_fmaf(wv[j], bf16_lo(hi), a2);
+                      a3 = __builtin_fmaf(wv[j], bf16_hi(hi), a3);
+                    }
+                  }
+                  *(uint64_t*)&Out[(int64_t)t * N + n] =
+                      (uint64_t)pk_bf16(a0, a1) | ((uint64_t)pk_bf16(a2, a3) << 32);
+                }
+              }
+            } else {
+              for (int i = 0; i < nl; ++i) {
+                const int t = last_tok[i];
+                for (int cc = tid; cc < kCols; cc += NT) {
+                  const int n = col0 + cc;
+                  if (n < N) {
+                    float s = 0.0f;
+                    for (int j = 0; j < topk; ++j) {
+                      const int64_t f = (int64_t)t * topk + j;
+                      const int e = topk_ids[f];
+                      if (e >= 0 && e < E) {
+                        const uint16_t h = __hip_atomic_load(&Y[f * N + n], __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                        s = __builtin_fmaf(cw[f], bf16f(h), s);
+                      }
+                    }
+                    Out[(int64_t)t * N + n] = to_bf16(s);
+                  }
+                }
               }
             }
           }
@@ -806,11 +924,13 @@ hipError_t launch_dense_t(const uint16_t* X, const int32_t* Wq, const uint16_t* 
   if (K % 256 == 0)
     hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, true, false, ZP, TL>), grid,
                        dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
-                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0, nullptr, nullptr,
+                       nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((k_gemm<kBMDense, kWN, kNW, false, false, false, ZP, TL>), grid,
                        dim3(kNW * 64), 0, st, X, (const uint32_t*)Wq, S, Z, Y, (int)M, (int)N,
-                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0);
+                       (int)K, nullptr, nullptr, nullptr, nullptr, 0, 1, 1, 0, nullptr, nullptr,
+                       nullptr, nullptr, 0);
   return hipGetLastError();
 }
 }  // namespace
@@ -858,24 +978,34 @@ int64_t moe_gemm_workgroups(int64_t T, int32_t k, int32_t E, int64_t N, int32_t 
 }
 
 namespace {
-template <int BM, int WN, bool SWI, bool ZP, bool TL>
+// the fused combine's operands (all null / 0 without it)
+struct CmbArgs {
+  uint16_t* out = nullptr;
+  int32_t* cnt = nullptr;
+  const int32_t* topk_ids = nullptr;
+  const float* w = nullptr;
+};
+
+template <int BM, int WN, bool SWI, bool ZP, bool TL, bool CMB = false>
 hipError_t launch_grouped_t(const uint16_t* X, const int32_t* Wq, const uint16_t* S,
                           const uint8_t* Z, const int32_t* sorted_ids, const int32_t* expert_ids,
                           const int32_t* ntpp, const float* topk_w, uint16_t* Y, int64_t T,
                           int32_t k, int32_t E, int64_t N, int64_t K, int32_t B,
-                          int32_t x_row_div, hipStream_t st) {
+                          int32_t x_row_div, hipStream_t st, const CmbArgs& c = CmbArgs()) {
   // a fused SwiGLU workgroup covers 2 WN gate rows and the matching up rows
   const int64_t ntn = SWI ? (N / 2 + 2 * WN - 1) / (2 * WN) : (N + kNW * WN - 1) / (kNW * WN);
   const dim3 grid((unsigned)(ntn * moe_gemm_slots(T, k, E, B)));
   const int n_pairs = (int)(T * k);
   if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI, ZP, TL>), grid, dim3(kNW * 64), 0, st, X,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, true, SWI, ZP, TL, CMB>), grid, dim3(kNW * 64), 0, st, X,
                        (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
-                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E, c.out, c.cnt,
+                       c.topk_ids, c.w, (int)k);
   else
-    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI, ZP, TL>), grid, dim3(kNW * 64), 0, st, X,
+    hipLaunchKernelGGL((k_gemm<BM, WN, kNW, true, false, SWI, ZP, TL, CMB>), grid, dim3(kNW * 64), 0, st, X,
                        (const uint32_t*)Wq, S, Z, Y, 0, (int)N, (int)K, sorted_ids,
-                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E);
+                       expert_ids, ntpp, topk_w, n_pairs, (int)B, (int)x_row_div, (int)E, c.out, c.cnt,
+                       c.topk_ids, c.w, (int)k);
   return hipGetLastError();
 }
 
@@ -921,6 +1051,42 @@ hipError_t launch_moe_gemm(const uint16_t* X, const int32_t* Wq, const uint16_t*
                            int32_t x_row_div, bool tiled, hipStream_t st) {
   return launch_grouped<false>(X, Wq, S, Z, sorted_ids, expert_ids, ntpp, topk_w, Y, T, k, E, N,
                                K, B, x_row_div, tiled, st);
+}
+
+// The grouped down product with the top-k combine fused (symmetric codes;
+// tiled: codes and scales in kernel order).  H2 receives the unweighted
+// bf16 rows, Out the combined tokens, cnt the arrival counters (zero before,
+// zero after).
+hipError_t launch_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                                   const int32_t* sorted_ids, const int32_t* expert_ids,
+                                   const int32_t* ntpp, const int32_t* topk_ids,
+                                   const float* topk_w, uint16_t* H2, uint16_t* Out, int32_t* cnt,
+                                   int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
+                                   int32_t B, bool tiled, hipStream_t st) {
+  CmbArgs c;
+  c.out = Out;
+  c.cnt = cnt;
+  c.topk_ids = topk_ids;
+  c.w = topk_w;
+  if (moe_tile_rows(T, k, E, B) == kBMMoeSmall)
+    return tiled ? launch_grouped_t<kBMMoeSmall, kWNMoeSmall, false, false, true, true>(
+                       A, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, nullptr, H2, T, k, E, N, K,
+                       B, 1, st, c)
+                 : launch_grouped_t<kBMMoeSmall, kWNMoeSmall, false, false, false, true>(
+                       A, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, nullptr, H2, T, k, E, N, K,
+                       B, 1, st, c);
+  return tiled ? launch_grouped_t<kBMMoe, kWN, false, false, true, true>(
+                     A, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, nullptr, H2, T, k, E, N, K, B,
+                     1, st, c)
+               : launch_grouped_t<kBMMoe, kWN, false, false, false, true>(
+                     A, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, nullptr, H2, T, k, E, N, K, B,
+                     1, st, c);
+}
+
+// Arrival counters of the fused combine: one per token and weight-row tile.
+int64_t moe_combine_counters(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B) {
+  const int64_t cols = moe_tile_rows(T, k, E, B) == kBMMoeSmall ? kNW * kWNMoeSmall : kNW * kWN;
+  return T * ((N + cols - 1) / cols);
 }
 
 hipError_t launch_moe_gemm_swiglu(const uint16_t* X, const int32_t* Wq, const uint16_t* S,

@@ -24,7 +24,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_route, w4_moe_sum,
+from . import (moe_align_block_size, w4_moe_align_capacity, w4_moe_combine_workspace_words,
+               w4_moe_route, w4_moe_sum, w4a16_moe_gemm_combine,
                w4_pick_block_size, w4_quantize_pack, w4_quantize_pack_asym, w4_repack,
                w4_repack_groups, w4_silu_mul, w4a16_moe_gemm, w4a16_moe_gemm_asym, w4a16_moe_gemm_swiglu,
                w4a16_moe_gemm_swiglu_asym, w4a16_moe_gemm_swiglu_tiled, w4a16_moe_gemm_tiled)
@@ -142,6 +143,7 @@ class MoEBuffers:
     A: torch.Tensor
     H2: torch.Tensor
     out: torch.Tensor
+    ws: torch.Tensor            # arrival counters of the fused combine (zeros)
 
 
 def alloc_buffers(T, k, E, H, I, B, device, fused=True):
@@ -152,16 +154,20 @@ def alloc_buffers(T, k, E, H, I, B, device, fused=True):
     return MoEBuffers(torch.empty(cap, **i32), torch.empty(cap // B, **i32),
                       torch.empty(1, **i32), H1,
                       torch.empty((T * k, I), **bf), torch.empty((T * k, H), **bf),
-                      torch.empty((T, H), **bf))
+                      torch.empty((T, H), **bf),
+                      torch.zeros(w4_moe_combine_workspace_words(T, k, E, H, B), **i32))
 
 
-def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None, fused=True):
+def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None, fused=True,
+                fused_combine=False):
     """Expert part of the layer for routed tokens.
 
     X bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
     gate_up: E experts of [2I, H]; down: E experts of [H, I].  B defaults to
-    ``w4_pick_block_size``.  ``fused``: SwiGLU in the gate_up epilogue (the
-    result is the same bit for bit).  Returns (Out bf16 [T, H], buffers).
+    ``w4_pick_block_size``.  ``fused``: SwiGLU in the gate_up epilogue;
+    ``fused_combine``: the top-k combine in the down product
+    (``w4a16_moe_gemm_combine``, symmetric experts).  Either way the result is
+    the same bit for bit.  Returns (Out bf16 [T, H], buffers).
     """
     T, H = X.shape
     k = topk_ids.shape[1]
@@ -182,13 +188,31 @@ def moe_forward(X, topk_ids, topk_weights, gate_up, down, B=None, buffers=None, 
         grouped_gemm(X, gate_up, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, k,
                      out=b.H1)
         w4_silu_mul(b.H1, out=b.A)
-    grouped_gemm(b.A, down, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, 1, out=b.H2)
-    w4_moe_sum(b.H2, topk_weights, T, k, out=b.out)
+    if fused_combine:
+        down_combine(b.A, down, b.sorted_token_ids, b.expert_ids, b.ntpp, topk_ids, topk_weights,
+                     B, b)
+    else:
+        grouped_gemm(b.A, down, b.sorted_token_ids, b.expert_ids, b.ntpp, T, k, B, 1, out=b.H2)
+        w4_moe_sum(b.H2, topk_weights, T, k, out=b.out)
     return b.out, b
 
 
-def moe_layer(X, logits, k, gate_up, down, B=None, buffers=None, fused=True):
+def down_combine(A, w, sorted_token_ids, expert_ids, ntpp, topk_ids, topk_weights, B, b):
+    """``w4a16_moe_gemm_combine`` on canonical or kernel-order symmetric
+    experts ``w``: H2 and the combined output into buffers ``b``."""
+    if w.Z is not None or w.Zt is not None:
+        raise ValueError("the fused combine takes symmetric experts")
+    if w.Wt is not None:
+        return w4a16_moe_gemm_combine(A, w.Wt, w.St, sorted_token_ids, expert_ids, ntpp,
+                                      topk_ids, topk_weights, B, N=w.N, tiled=True, H2=b.H2,
+                                      out=b.out, workspace=b.ws)
+    return w4a16_moe_gemm_combine(A, w.Wq, w.S, sorted_token_ids, expert_ids, ntpp, topk_ids,
+                                  topk_weights, B, H2=b.H2, out=b.out, workspace=b.ws)
+
+
+def moe_layer(X, logits, k, gate_up, down, B=None, buffers=None, fused=True,
+              fused_combine=False):
     """Routing plus ``moe_forward``: logits fp32 [T, E] -> Out bf16 [T, H]."""
     ids, w = w4_moe_route(logits, k)
-    out, b = moe_forward(X, ids, w, gate_up, down, B, buffers, fused)
+    out, b = moe_forward(X, ids, w, gate_up, down, B, buffers, fused, fused_combine)
     return out, ids, w, b

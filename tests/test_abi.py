@@ -305,6 +305,33 @@ def test_elementwise_validation(lib):
     assert lib.w4_moe_route(None, 0, 64, 8, None, None, None) == OK
 
 
+def test_moe_combine_validation(lib):
+    """The fused down + combine call checks the grouped product's arguments
+    and its own (top-k ids and weights, output, workspace) before anything
+    is enqueued; the workspace size is one counter per token and tile."""
+    f = lib.w4a16_moe_gemm_combine
+    ops = (A16, A16, A2, A4, A4, A4)                 # A, Wq, S, sorted, expert_ids, ntpp
+    tail = (A4, A4, A4, A2)                          # topk_ids, topk_weights, H2, Out
+    assert f(*ops, *tail, -1, 2, 8, 64, 64, 16, 0, A4, None) == SHAPE
+    assert f(*ops, *tail, 4, 2, 8, 64, 48, 16, 0, A4, None) == SHAPE        # K % 32
+    assert f(*ops, *tail, 4, 2, 2000, 64, 64, 16, 0, A4, None) == UNSUPPORTED
+    assert f(*ops, *tail, 4, 17, 64, 64, 64, 16, 0, A4, None) == UNSUPPORTED   # k > 16
+    assert f(*ops, None, A4, A4, A2, 4, 2, 8, 64, 64, 16, 0, A4, None) == NULL
+    assert f(*ops, A4, None, A4, A2, 4, 2, 8, 64, 64, 16, 0, A4, None) == NULL
+    assert f(*ops, A4, A4, A4, None, 4, 2, 8, 64, 64, 16, 0, A4, None) == NULL
+    assert f(*ops, *tail, 4, 2, 8, 64, 64, 16, 0, None, None) == NULL
+    assert f(*ops, A2, A4, A4, A2, 4, 2, 8, 64, 64, 16, 0, A4, None) == MISALIGNED
+    assert f(*ops, *tail, 4, 2, 8, 64, 64, 16, 0, A2, None) == MISALIGNED
+    assert f(A4, *ops[1:], *tail, 4, 2, 8, 64, 64, 16, 0, A4, None) == MISALIGNED
+    assert f(None, None, None, None, None, None, None, None, None, None, 0, 2, 8, 64, 64, 16, 0,
+             None, None) == OK
+    w = lib.w4_moe_combine_workspace_words
+    assert w(256, 8, 128, 4096, 16) == 256 * (4096 // 128)      # 32-row tile: 128 columns
+    assert w(4096, 8, 384, 7168, 64) == 4096 * (7168 // 256)    # 128-row tile: 256 columns
+    assert w(10, 2, 4, 300, 64) == 10 * 2
+    assert w(-1, 2, 4, 300, 64) == -1 and w(1, 0, 4, 300, 64) == -1
+
+
 def test_qat_op_refuses_cpu_tensors():
     """The QAT op has no CPU path: a CPU weight is rejected before any call."""
     import torch
