@@ -482,6 +482,30 @@ int w4a16_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t*
                            int32_t E, int64_t N, int64_t K, int32_t B, int32_t tiled,
                            int32_t* workspace, void* stream);
 
+/*
+ * w4a16_moe_gemm_combine_noalloc -- w4a16_moe_gemm_combine without the
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The arrival counters live in a fixed array of the library:
+ * 2^18 int32 (1 MiB) per GPU, held until the process ends, zero when the
+ * library loads and left zero by every call.  A layer needing more
+ * counters than that (w4_moe_combine_workspace_words(T, k, E, N, B) >
+ * 262144) returns W4_ERR_UNSUPPORTED with nothing enqueued.  The call
+ * allocates nothing and calls no allocating routine; on its first use on a
+ * device it looks up that device's copy of the array.  All calls on one GPU
+ * share the counters: calls that overlap in time on one GPU (unordered
+ * streams, or several host threads) race and give undefined results.
+ * Outputs, other limits and errors as w4a16_moe_gemm_combine.
+ */
+int w4a16_moe_gemm_combine_noalloc(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                                   const int32_t* sorted_token_ids,
+                                   const int32_t* expert_ids,
+                                   const int32_t* num_tokens_post_padded,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   uint16_t* H2, uint16_t* Out, int64_t T, int32_t k,
+                                   int32_t E, int64_t N, int64_t K, int32_t B,
+                                   int32_t tiled, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ __all__ = [
     "w4_moe_align_capacity", "moe_align_block_size", "w4a16_moe_gemm", "w4a16_moe_gemm_swiglu",
     "w4a16_moe_gemm_asym", "w4a16_moe_gemm_swiglu_asym",
     "w4_silu_mul", "w4_moe_sum", "w4_moe_route", "w4_moe_combine_workspace_words",
-    "w4a16_moe_gemm_combine", "library_path",
+    "w4a16_moe_gemm_combine", "w4a16_moe_gemm_combine_noalloc", "library_path",
     "w4_repacked_words", "w4_repack", "w4_restore", "w4_repacked_group_elems",
     "w4_repack_groups", "w4_restore_groups", "w4a16_gemm_tiled",
     "w4a16_moe_gemm_tiled", "w4a16_moe_gemm_swiglu_tiled",
@@ -733,4 +733,34 @@ def w4a16_moe_gemm_combine(A, Wq, S, sorted_token_ids, expert_ids, num_tokens_po
         _ptr(A), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_ids), _ptr(topk_weights), _ptr(H2), _ptr(out),
         T, k, E, N, K, B, 1 if tiled else 0, _ptr(workspace), _stream(A)))
+    return out, H2
+
+
+def w4a16_moe_gemm_combine_noalloc(A, Wq, S, sorted_token_ids, expert_ids,
+                                   num_tokens_post_padded, topk_ids, topk_weights, B, H2, out,
+                                   N=None, tiled=False):
+    """``w4a16_moe_gemm_combine`` with the library's own counters: the call
+    allocates nothing (H2 and out are given).  Returns (out, H2)."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    if tiled:
+        if N is None:
+            raise ValueError("kernel-order experts need N")
+        E, K = _moe_tiled_args(A, Wq, S, None, N, T, k, 1)
+    else:
+        E, N, K = _moe_args(A, Wq, S, None, sorted_token_ids, expert_ids,
+                            num_tokens_post_padded, T, k, B, 1)
+    for t, n, dt in ((sorted_token_ids, "sorted_token_ids", torch.int32),
+                     (expert_ids, "expert_ids", torch.int32),
+                     (num_tokens_post_padded, "num_tokens_post_padded", torch.int32),
+                     (topk_weights, "topk_weights", torch.float32),
+                     (H2, "H2", torch.bfloat16), (out, "out", torch.bfloat16)):
+        _need(t, n, dt)
+    if H2.numel() != T * k * N or out.numel() != T * N or topk_weights.numel() != T * k:
+        raise ValueError("H2 must be [T*k, N], out [T, N], topk_weights [T, k]")
+    lib = _lib.load()
+    _lib.check("w4a16_moe_gemm_combine_noalloc", lib.w4a16_moe_gemm_combine_noalloc(
+        _ptr(A), _ptr(Wq), _ptr(S), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(topk_ids), _ptr(topk_weights), _ptr(H2), _ptr(out),
+        T, k, E, N, K, B, 1 if tiled else 0, _stream(A)))
     return out, H2

@@ -43,6 +43,8 @@ SIGNATURES = {
     "w4_moe_combine_workspace_words": (_i64, [_i64, _i32, _i32, _i64, _i32]),
     "w4a16_moe_gemm_combine": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32,
                                               _i32, _i64, _i64, _i32, _i32, _p, _p]),
+    "w4a16_moe_gemm_combine_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64,
+                                                      _i32, _i32, _i64, _i64, _i32, _i32, _p]),
     "w4_dequant_t": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p, _p]),
     "w4_bf16_gemm_nt": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
     "w4_repacked_words": (_i64, [_i64, _i64]),

@@ -515,24 +515,68 @@ int64_t w4_moe_combine_workspace_words(int64_t T, int32_t k, int32_t E, int64_t 
   return w4::moe_combine_counters(T, k, E, N, B);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of the fused combine's operands other than the counters: W4_OK,
+// -1 for a valid call with nothing to do (T == 0), or an error status.
+int combine_validate(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                     const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_padded, const int32_t* topk_ids,
+                     const float* topk_weights, uint16_t* H2, uint16_t* Out, int64_t T,
+                     int32_t k, int32_t E, int64_t N, int64_t K, int32_t B, int32_t tiled) {
+  const int v = moe_gemm_validate(A, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
+                                  num_tokens_post_padded, topk_weights, H2, T, k, E, N, K, B, 1,
+                                  false, tiled != 0);
+  if (v != W4_OK) return v;
+  if (T * N >= ((int64_t)1 << 40) || k > 16) return W4_ERR_UNSUPPORTED;
+  if (!topk_ids || !topk_weights || !Out) return W4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(Out, 2)) return W4_ERR_MISALIGNED;
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int w4a16_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
                            const int32_t* num_tokens_post_padded, const int32_t* topk_ids,
                            const float* topk_weights, uint16_t* H2, uint16_t* Out, int64_t T,
                            int32_t k, int32_t E, int64_t N, int64_t K, int32_t B, int32_t tiled,
                            int32_t* workspace, void* stream) {
-  const int v = moe_gemm_validate(A, Wq, S, nullptr, false, sorted_token_ids, expert_ids,
-                                  num_tokens_post_padded, topk_weights, H2, T, k, E, N, K, B, 1,
-                                  false, tiled != 0);
+  const int v = combine_validate(A, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                 topk_ids, topk_weights, H2, Out, T, k, E, N, K, B, tiled);
   if (v < 0) return W4_OK;
   if (v != W4_OK) return v;
-  if (T * N >= ((int64_t)1 << 40) || k > 16) return W4_ERR_UNSUPPORTED;
-  if (!topk_ids || !topk_weights || !Out || !workspace) return W4_ERR_NULL;
-  if (!aligned(topk_ids, 4) || !aligned(Out, 2) || !aligned(workspace, 4))
-    return W4_ERR_MISALIGNED;
+  if (!workspace) return W4_ERR_NULL;
+  if (!aligned(workspace, 4)) return W4_ERR_MISALIGNED;
   return hip_status(w4::launch_moe_gemm_combine(A, Wq, S, sorted_token_ids, expert_ids,
                                                 num_tokens_post_padded, topk_ids, topk_weights,
                                                 H2, Out, workspace, T, k, E, N, K, B, tiled != 0,
+                                                as_stream(stream)));
+}
+
+int w4a16_moe_gemm_combine_noalloc(const uint16_t* A, const int32_t* Wq, const uint16_t* S,
+                                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                   const int32_t* num_tokens_post_padded,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   uint16_t* H2, uint16_t* Out, int64_t T, int32_t k, int32_t E,
+                                   int64_t N, int64_t K, int32_t B, int32_t tiled,
+                                   void* stream) {
+  const int v = combine_validate(A, Wq, S, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                 topk_ids, topk_weights, H2, Out, T, k, E, N, K, B, tiled);
+  if (v < 0) return W4_OK;
+  if (v != W4_OK) return v;
+  if (w4::moe_combine_counters(T, k, E, N, B) > w4::kCombineScratchWords)
+    return W4_ERR_UNSUPPORTED;
+  int32_t* words = nullptr;
+  const hipError_t e = w4::combine_scratch(&words);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(w4::launch_moe_gemm_combine(A, Wq, S, sorted_token_ids, expert_ids,
+                                                num_tokens_post_padded, topk_ids, topk_weights,
+                                                H2, Out, words, T, k, E, N, K, B, tiled != 0,
                                                 as_stream(stream)));
 }
 

@@ -168,6 +168,10 @@ hipError_t launch_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const u
                                    int64_t T, int32_t k, int32_t E, int64_t N, int64_t K,
                                    int32_t B, bool tiled, hipStream_t st);
 int64_t moe_combine_counters(int64_t T, int32_t k, int32_t E, int64_t N, int32_t B);
+// The library's own counters for the allocation-free fused combine: the
+// current device's copy (looked up once per device).
+constexpr int64_t kCombineScratchWords = (int64_t)1 << 18;
+hipError_t combine_scratch(int32_t** words);
 hipError_t launch_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t B,
                         int64_t cap, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
                         hipStream_t st);

@@ -45,6 +45,7 @@
 // is a raw buffer load whose out-of-range lanes read zero (rows past the
 // end, K past the end, the padding steps of the unrolled loop), so no
 // load is conditional.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1081,6 +1082,31 @@ hipError_t launch_moe_gemm_combine(const uint16_t* A, const int32_t* Wq, const u
                : launch_grouped_t<kBMMoe, kWN, false, false, false, true>(
                      A, Wq, S, nullptr, sorted_ids, expert_ids, ntpp, nullptr, H2, T, k, E, N, K, B,
                      1, st, c);
+}
+
+// The arrival counters of w4a16_moe_gemm_combine_noalloc: a fixed device
+// array per GPU, held until the process ends, zero when the library loads
+// and left zero by every call.  On the host `scratch` names a stand-in, not
+// a device address: each device's copy is looked up once, with that device
+// current, and only the looked-up address is passed to a kernel.
+static __device__ __align__(256) int32_t scratch[kCombineScratchWords];
+
+hipError_t combine_scratch(int32_t** words) {
+  static std::mutex mu;
+  static int32_t* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = (int32_t*)p;
+  }
+  *words = ptrs[dev];
+  return hipSuccess;
 }
 
 // Arrival counters of the fused combine: one per token and weight-row tile.

@@ -325,6 +325,14 @@ def test_moe_combine_validation(lib):
     assert f(A4, *ops[1:], *tail, 4, 2, 8, 64, 64, 16, 0, A4, None) == MISALIGNED
     assert f(None, None, None, None, None, None, None, None, None, None, 0, 2, 8, 64, 64, 16, 0,
              None, None) == OK
+    g = lib.w4a16_moe_gemm_combine_noalloc
+    assert g(*ops, *tail, -1, 2, 8, 64, 64, 16, 0, None) == SHAPE
+    assert g(*ops, None, A4, A4, A2, 4, 2, 8, 64, 64, 16, 0, None) == NULL
+    assert g(*ops, *tail, 4, 17, 64, 64, 64, 16, 0, None) == UNSUPPORTED
+    # more counters than the library's fixed array holds (70000 x 16 > 2^18)
+    assert g(*ops, *tail, 70000, 1, 8, 4096, 64, 16, 0, None) == UNSUPPORTED
+    assert g(None, None, None, None, None, None, None, None, None, None, 0, 2, 8, 64, 64, 16, 0,
+             None) == OK
     w = lib.w4_moe_combine_workspace_words
     assert w(256, 8, 128, 4096, 16) == 256 * (4096 // 128)      # 32-row tile: 128 columns
     assert w(4096, 8, 384, 7168, 64) == 4096 * (7168 // 256)    # 128-row tile: 256 columns
