@@ -110,3 +110,41 @@ def test_moe_layer_graph_replay(T, E, k, asym):
         torch.cuda.synchronize()
         ref, _, _, _ = wmoe.moe_layer(X, L, k, gate_up, down, B=B)
         np.testing.assert_array_equal(down_bits(bufs.out), down_bits(ref), err_msg=f"replay {r}")
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_fused_combine_graph_replay(noalloc):
+    """The down product with the combine fused, captured once (workspace
+    counters, or the library's own with the allocation-free call) and
+    replayed with new activations and routing weights copied in between:
+    every replay equals the eager down product + combine bit for bit, and
+    the counters are back at zero."""
+    T, E, k, H, I, seed = 64, 8, 4, 512, 128, 13
+    say(f"graph fused combine noalloc={noalloc}")
+    down = wmoe.quantize_experts(
+        E, H, I, lambda e: synth.weights(H, I, seed, stream=700 + e, device=DEV), DEV)
+    ids, tw = w4.w4_moe_route(synth.router_logits(T, E, seed, device=DEV), k)
+    B = w4.w4_pick_block_size(T, k, E)
+    b = wmoe.alloc_buffers(T, k, E, H, I, B, DEV)
+    w4.moe_align_block_size(ids, E, B, b.sorted_token_ids, b.expert_ids, b.ntpp)
+    A = b.A
+    A.copy_(synth.activations(T * k, I, seed, device=DEV))
+    if noalloc:
+        fn = lambda: w4.w4a16_moe_gemm_combine_noalloc(A, down.Wq, down.S, b.sorted_token_ids,
+                                                       b.expert_ids, b.ntpp, ids, tw, B, b.H2,
+                                                       b.out)
+    else:
+        fn = lambda: wmoe.down_combine(A, down, b.sorted_token_ids, b.expert_ids, b.ntpp, ids,
+                                       tw, B, b)
+    g = capture(fn)
+    for r in range(3):
+        A.copy_(synth.activations(T * k, I, 50 + r, device=DEV))
+        tw.copy_(torch.rand((T, k), generator=torch.Generator().manual_seed(r)).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        h2 = w4.w4a16_moe_gemm(A, down.Wq, down.S, b.sorted_token_ids, b.expert_ids, b.ntpp,
+                               T, k, B, 1)
+        ref = w4.w4_moe_sum(h2, tw, T, k)
+        np.testing.assert_array_equal(down_bits(b.out), down_bits(ref), err_msg=f"replay {r}")
+        assert int(torch.count_nonzero(b.ws).item()) == 0
